@@ -1,0 +1,92 @@
+"""Second, independent CPU implementation for tiny inputs (numpy + Python).
+
+TEST INFRASTRUCTURE ONLY. It pins the C oracle: every step is written a
+different way from ``oracle.c`` so that a slip in one (a wrong shift, a
+dropped term, a transposed operand) shows up as a disagreement:
+
+  * codes come from integer division and modulo of the packed word
+    (``word // base**i % base``), not from shifts and masks;
+  * fp16/bf16 values come from numpy's own float16 / float32 decoding;
+  * the contraction is numpy's float64 matrix product of the dequantized
+    matrix (a library routine);
+  * top-k is Python's stable ``sorted`` over (-logit, index);
+  * GELU uses ``math.erf`` / ``math.tanh``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def f16(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16(bits) -> np.ndarray:
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) * np.uint32(65536)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
+
+
+def codes(bits: int, wq: np.ndarray, K: int) -> np.ndarray:
+    """Integer codes [N][K] by division/modulo of each packed word."""
+    base = 1 << bits
+    per = 32 // bits
+    words = np.asarray(wq, dtype=np.uint32).astype(np.int64)
+    N = words.shape[0]
+    out = np.empty((N, K), dtype=np.int64)
+    for k in range(K):
+        out[:, k] = (words[:, k // per] // (base ** (k % per))) % base
+    return out
+
+
+def dense(w) -> np.ndarray:
+    """fp64 matrix [N][K] of a synth.AffineWeights: s*q + b per group of 64."""
+    q = codes(w.bits, w.wq, w.K)
+    s = np.repeat(f16(w.scales), 64, axis=1)
+    b = np.repeat(f16(w.biases), 64, axis=1)
+    return s * q + b
+
+
+def gemv(w, x: np.ndarray) -> np.ndarray:
+    return np.atleast_2d(x) @ dense(w).T
+
+
+def route_topk(logits, k: int):
+    L = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    T, E = L.shape
+    idx = np.zeros((T, k), dtype=np.int32)
+    p = np.zeros((T, k), dtype=np.float64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-L[t, e], e))[:k]
+        ex = [math.exp(L[t, e] - L[t].max()) for e in range(E)]
+        tot = math.fsum(ex)
+        probs = [ex[e] / tot for e in order]
+        kept = math.fsum(probs)
+        idx[t] = order
+        p[t] = [v / kept for v in probs]
+    return idx, p
+
+
+def gelu(u: float, variant: int = 0) -> float:
+    if variant == 1:
+        return 0.5 * u * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+    return 0.5 * u * (1.0 + math.erf(u / math.sqrt(2.0)))
+
+
+def moe_experts(mw, x, idx, p, act: int = 0):
+    x = np.atleast_2d(x)
+    T = x.shape[0]
+    y = np.zeros((T, mw.H))
+    ge = np.vectorize(lambda u: gelu(u, act))
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            z = dense(mw.expert_gu(e)) @ x[t]
+            h = ge(z[:mw.I]) * z[mw.I:]
+            y[t] += p[t, j] * (dense(mw.expert_dn(e)) @ h)
+        z = dense(mw.sgu) @ x[t]
+        hs = ge(z[:mw.Is]) * z[mw.Is:]
+        y[t] += dense(mw.sdn) @ hs
+    return y

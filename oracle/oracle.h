@@ -1,0 +1,86 @@
+/*
+ * CPU oracle for the affine-quantized decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link
+ * or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code with the HIP library.
+ *
+ * Everything is computed in fp64 from the plain definitions, with no
+ * blocking, fusion or reordering:
+ *   - weight format (TurboFieldfare article, "성능과 제약" / performance
+ *     and constraints section): MLX affine quantization, 4-bit codes with
+ *     one scale and one bias per group of 64 inputs, router at 8 bits;
+ *     w = s*q + b;
+ *   - GEMV: y[t][n] = sum over k ascending of w[n][k] * x[t][k];
+ *   - routing (same article, top section and "내부 구조" / internals
+ *     section: only the router's top-8 experts are used): softmax over
+ *     all experts, keep the 8 largest, renormalize over those 8;
+ *   - expert block (internals section: the shared-expert output and the
+ *     routed output are combined): y = sum_j p_j * down_j(GELU(gate_j x)
+ *     * up_j x) + down_s(GELU(gate_s x) * up_s x);
+ *   - prefill chunk (internals section: prompts run in chunks of at most
+ *     128 tokens): Y[m][n] = sum_k w[n][k] * X[m][k].
+ *
+ * Readings where the pages are silent (nibble order LSB-first; separate
+ * fp16 scale and bias arrays [N][K/64]; gate rows before up rows; exact
+ * erf GELU by default; ties in the top-k broken towards the lower expert
+ * index) are listed with the design notes.
+ */
+#ifndef QD_ORACLE_H
+#define QD_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+double qo_f16_to_f64(uint16_t h);
+double qo_bf16_to_f64(uint16_t h);
+void qo_f16_array(const uint16_t* in, int64_t n, double* out);
+void qo_bf16_array(const uint16_t* in, int64_t n, double* out);
+
+/* Code k of one packed row: bits = 4 or 8; LSB-first inside each uint32. */
+int qo_code(int bits, const uint32_t* row, int64_t k);
+
+/* Dequantized matrix w[N][K] in fp64. */
+void qo_dequant(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                int64_t N, int64_t K, double* w);
+
+/* y[T][N] = W x for T activation rows x[T][K]; a[T][N] = sum_k |w*x| (may be NULL). */
+void qo_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+             const double* x, int64_t T, int64_t N, int64_t K, double* y, double* a);
+
+/* Same, for the listed output rows only: y[T][nrows], a[T][nrows]. */
+void qo_gemv_rows(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                  const double* x, int64_t T, int64_t N, int64_t K,
+                  const int64_t* rows, int64_t nrows, double* y, double* a);
+
+/* Top-k routing of logits[T][E] -> idx[T][k], p[T][k]. Returns 0, or -1 on bad sizes. */
+int qo_route_topk(const double* logits, int64_t T, int64_t E, int64_t k, int32_t* idx, double* p);
+
+/* variant 0: exact erf form; 1: tanh approximation. */
+double qo_gelu(double u, int variant);
+
+typedef struct {
+    int64_t E, H, I, Is;
+    const uint32_t *gu_q, *dn_q, *sgu_q, *sdn_q;
+    const uint16_t *gu_s, *gu_b, *dn_s, *dn_b, *sgu_s, *sgu_b, *sdn_s, *sdn_b;
+} qo_moe;
+
+/*
+ * Expert block for T tokens: x[T][H] (fp64), idx/p [T][k].
+ * Writes y[T][H] and a[T][H] = sum_j p_j sum_k |Wdn_j h_j| + sum_k |Wdn_s h_s|.
+ * h[T][k][I] and hs[T][Is] receive the gated activations when non-NULL.
+ */
+void qo_moe_experts(const qo_moe* w, const double* x, int64_t T, int64_t k,
+                    const int32_t* idx, const double* p, int act,
+                    double* y, double* a, double* h, double* hs);
+
+/* Number of OpenMP threads the oracle uses (0 = runtime default). */
+void qo_set_threads(int n);
+int qo_get_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,308 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+Each check compares the oracle with an independent route to the same
+number: exhaustive format decoding by numpy, a brute force that unpacks
+with integer division, exact rational arithmetic, the grouped closed form
+of the affine contraction, special inputs with known answers, Python's
+stable sort, and textbook values of the normal CDF.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import brute
+
+
+# ---------------------------------------------------------------- formats
+
+def test_f16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.f16_to_f64(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    # signed zero
+    assert math.copysign(1.0, oracle.f16_to_f64(np.array([0x8000], np.uint16))[0]) == -1.0
+
+
+def test_bf16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = brute.bf16(bits)
+    got = oracle.bf16_to_f64(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_code_unpack_matches_divmod(bits):
+    w = synth.affine_weights(bits, 3, 256, cfg=90, set_id=bits)
+    q = brute.codes(bits, w.wq, 256)
+    for n in range(3):
+        got = [oracle.code(bits, w.wq[n], k) for k in range(256)]
+        assert got == list(q[n])
+    assert q.min() == 0 and q.max() == (1 << bits) - 1
+
+
+def test_code_order_lsb_first():
+    # word 0x76543210: code k of the row is k (LSB-first nibble order)
+    row = np.array([0x76543210, 0xFEDCBA98], dtype=np.uint32)
+    assert [oracle.code(4, row, k) for k in range(16)] == list(range(16))
+    row8 = np.array([0x03020100], dtype=np.uint32)
+    assert [oracle.code(8, row8, k) for k in range(4)] == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------- GEMV
+
+SHAPES = [(1, 64, 1), (3, 128, 2), (17, 256, 3), (5, 192, 8), (2, 64, 5)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("N,K,T", SHAPES)
+def test_gemv_matches_bruteforce(bits, N, K, T):
+    w = synth.affine_weights(bits, N, K, cfg=91, set_id=N * 1000 + K + T)
+    xb = synth.x_f16(T, K, cfg=91, set_id=N * 1000 + K + T)
+    y, a = oracle.gemv_f16(w, xb)
+    yb = brute.gemv(w, brute.f16(xb))
+    assert y.shape == (T, N)
+    assert np.all(np.abs(y - yb) <= 1e-12 * a + 1e-300)
+    # A really is sum |w x|
+    ab = np.abs(brute.f16(xb)) @ np.abs(brute.dense(w)).T
+    assert np.allclose(a, ab, rtol=1e-13, atol=0)
+
+
+def test_dequant_matches_bruteforce():
+    w = synth.affine_weights(4, 5, 192, cfg=92, set_id=0)
+    assert np.array_equal(oracle.dequant(w), brute.dense(w))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_against_exact_rationals(bits):
+    N, K, T = 3, 128, 2
+    w = synth.affine_weights(bits, N, K, cfg=93, set_id=bits)
+    xb = synth.x_f16(T, K, cfg=93, set_id=bits)
+    y, a = oracle.gemv_f16(w, xb)
+    q = brute.codes(bits, w.wq, K)
+    s = [[Fraction(float(v)) for v in row] for row in w.scales.view(np.float16)]
+    b = [[Fraction(float(v)) for v in row] for row in w.biases.view(np.float16)]
+    x = [[Fraction(float(v)) for v in row] for row in xb.view(np.float16)]
+    for t in range(T):
+        for n in range(N):
+            exact = sum((s[n][k // 64] * int(q[n, k]) + b[n][k // 64]) * x[t][k] for k in range(K))
+            assert abs(float(exact) - y[t, n]) <= 4 * K * 2.0 ** -53 * a[t, n]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_grouped_closed_form(bits):
+    # y_n = sum_g s_g * (q . x)_g + b_g * (sum x)_g
+    N, K, T = 7, 320, 2
+    w = synth.affine_weights(bits, N, K, cfg=94, set_id=bits)
+    xb = synth.x_f16(T, K, cfg=94, set_id=bits)
+    x = brute.f16(xb)
+    q = brute.codes(bits, w.wq, K).astype(np.float64)
+    s, b = brute.f16(w.scales), brute.f16(w.biases)
+    G = K // 64
+    qx = np.einsum("nk,tk->tnk", q, x).reshape(T, N, G, 64).sum(-1)      # (q.x)_g
+    xs = x.reshape(T, G, 64).sum(-1)                                      # (sum x)_g
+    yc = (s[None] * qx).sum(-1) + (b[None] * xs[:, None, :]).sum(-1)
+    y, a = oracle.gemv_f16(w, xb)
+    assert np.all(np.abs(y - yc) <= 1e-12 * a)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_codes_give_bias_term(bits):
+    N, K = 4, 256
+    w = synth.affine_weights(bits, N, K, cfg=95, set_id=0, codes="zero")
+    xb = synth.x_f16(1, K, cfg=95, set_id=0)
+    x = brute.f16(xb)[0]
+    y, a = oracle.gemv_f16(w, xb)
+    xs = x.reshape(-1, 64).sum(-1)
+    exp = (brute.f16(w.biases) * xs[None]).sum(-1)
+    assert np.allclose(y[0], exp, rtol=0, atol=1e-13 * a.max())
+
+
+@pytest.mark.parametrize("bits,c", [(4, 0), (4, 7), (4, 15), (8, 200)])
+def test_constant_codes(bits, c):
+    N, K = 3, 192
+    w = synth.affine_weights(bits, N, K, cfg=96, set_id=c, codes="const", const_code=c)
+    xb = synth.x_f16(1, K, cfg=96, set_id=c)
+    x = brute.f16(xb)[0]
+    y, a = oracle.gemv_f16(w, xb)
+    xs = x.reshape(-1, 64).sum(-1)
+    exp = ((c * brute.f16(w.scales) + brute.f16(w.biases)) * xs[None]).sum(-1)
+    assert np.allclose(y[0], exp, rtol=0, atol=1e-13 * a.max())
+
+
+def test_zero_activation_gives_exact_zero():
+    w = synth.affine_weights(4, 5, 128, cfg=97, set_id=0)
+    y, a = oracle.gemv_f16(w, np.zeros((2, 128), np.uint16))
+    assert np.all(y == 0.0) and np.all(a == 0.0)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_one_hot_activation_is_exact_weight(bits):
+    N, K = 4, 256
+    w = synth.affine_weights(bits, N, K, cfg=98, set_id=bits)
+    q = brute.codes(bits, w.wq, K)
+    one = np.float16(1.0).view(np.uint16)
+    for k in (0, 5, 63, 64, 200, 255):
+        xb = np.zeros((1, K), np.uint16)
+        xb[0, k] = one
+        y, _ = oracle.gemv_f16(w, xb)
+        sv = w.scales.view(np.float16)[:, k // 64].astype(np.float64)
+        bv = w.biases.view(np.float16)[:, k // 64].astype(np.float64)
+        assert np.array_equal(y[0], sv * q[:, k] + bv)
+
+
+def test_rows_variant_matches_full():
+    w = synth.affine_weights(4, 33, 256, cfg=99, set_id=0)
+    xb = synth.x_f16(2, 256, cfg=99, set_id=0)
+    y, a = oracle.gemv_f16(w, xb)
+    rows = np.array([0, 7, 32, 13])
+    yr, ar = oracle.gemv_f16(w, xb, rows=rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(ar, a[:, rows])
+
+
+def test_chunk_is_rowwise_gemv_on_bf16():
+    w = synth.affine_weights(4, 9, 192, cfg=100, set_id=0)
+    X = synth.x_bf16(5, 192, cfg=100, set_id=0)
+    Y, A = oracle.gemm_chunk(w, X)
+    Yb = brute.gemv(w, brute.bf16(X))
+    assert np.all(np.abs(Y - Yb) <= 1e-12 * A)
+    for m in range(5):
+        ym, _ = oracle.gemv(w, brute.bf16(X[m:m + 1]))
+        assert np.array_equal(ym[0], Y[m])
+
+
+# ---------------------------------------------------------------- routing
+
+def test_topk_matches_stable_sort():
+    r = np.random.default_rng(5)
+    L = r.standard_normal((20, 128)) * 3
+    L[3, 10] = L[3, 20] = L[3, 5] = L[3].max() + 1.0      # three-way tie at the top
+    L[4, :] = 0.5                                           # all tied
+    idx, p = oracle.route_topk(L, 8)
+    ib, pb = brute.route_topk(L, 8)
+    assert np.array_equal(idx, ib)
+    assert np.allclose(p, pb, rtol=1e-14, atol=1e-15)
+    assert list(idx[3, :3]) == [5, 10, 20]
+    assert list(idx[4]) == list(range(8))
+    assert np.allclose(p[4], 1.0 / 8, rtol=0, atol=1e-15)
+    assert np.allclose(p.sum(1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(p, axis=1) <= 0)
+
+
+def test_topk_renormalized_softmax_identity():
+    # softmax over all experts then renormalizing over the kept ones equals a
+    # softmax over the kept logits alone
+    r = np.random.default_rng(6)
+    L = r.standard_normal((10, 64)) * 2
+    idx, p = oracle.route_topk(L, 8)
+    for t in range(10):
+        kl = L[t, idx[t]]
+        direct = np.exp(kl - kl.max()) / np.exp(kl - kl.max()).sum()
+        assert np.allclose(p[t], direct, rtol=1e-13, atol=0)
+
+
+def test_topk_k_equals_e_and_bad_sizes():
+    L = np.array([[1.0, 3.0, 2.0]])
+    idx, p = oracle.route_topk(L, 3)
+    assert list(idx[0]) == [1, 2, 0]
+    with pytest.raises(ValueError):
+        oracle.route_topk(L, 4)
+
+
+# ---------------------------------------------------------------- GELU
+
+def test_gelu_textbook_values_and_identities():
+    # GELU(u) = u * Phi(u); Phi(1) = 0.8413447460685429, Phi(2) = 0.9772498680518208
+    assert abs(oracle.gelu(1.0) - 0.8413447460685429) < 1e-15
+    assert abs(oracle.gelu(2.0) - 2 * 0.9772498680518208) < 2e-15
+    assert abs(oracle.gelu(-1.0) + (1 - 0.8413447460685429)) < 1e-15
+    for v in (0, 1):
+        assert oracle.gelu(0.0, v) == 0.0
+        for u in (0.1, 0.7, 1.3, 3.0, 6.5):
+            assert abs(oracle.gelu(u, v) - oracle.gelu(-u, v) - u) < 1e-14
+        assert abs(oracle.gelu(40.0, v) - 40.0) < 1e-12
+        assert abs(oracle.gelu(-40.0, v)) < 1e-12
+
+
+def test_gelu_against_torch():
+    import torch
+    u = torch.linspace(-6, 6, 241, dtype=torch.float64)
+    ex = torch.nn.functional.gelu(u)
+    th = torch.nn.functional.gelu(u, approximate="tanh")
+    for i in range(u.numel()):
+        assert abs(oracle.gelu(float(u[i]), 0) - float(ex[i])) < 1e-14
+        assert abs(oracle.gelu(float(u[i]), 1) - float(th[i])) < 1e-14
+
+
+# ---------------------------------------------------------------- MoE block
+
+def _tiny_moe(**kw):
+    return synth.moe_weights(E=6, H=128, I=64, Is=128, cfg=101, layer=0, **kw)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_moe_block_matches_bruteforce(act):
+    mw = _tiny_moe()
+    xb = synth.x_f16(3, 128, cfg=101, set_id=1)
+    x = brute.f16(xb)
+    logits, _ = oracle.gemv(mw.router, x)
+    idx, p = oracle.route_topk(logits, 3)
+    y, a = oracle.moe_experts(mw, x, idx, p, act)
+    yb = brute.moe_experts(mw, x, idx, p, act)
+    assert np.all(np.abs(y - yb) <= 1e-12 * a + 1e-300)
+
+
+def test_moe_identical_experts_do_not_depend_on_routing():
+    mw = _tiny_moe(identical_experts=True)
+    xb = synth.x_f16(1, 128, cfg=101, set_id=2)
+    x = brute.f16(xb)
+    ya, aa = oracle.moe_experts(mw, x, np.array([[0, 1, 2]]), np.array([[0.5, 0.3, 0.2]]))
+    yb, _ = oracle.moe_experts(mw, x, np.array([[5, 3, 4]]), np.array([[0.6, 0.25, 0.15]]))
+    assert np.all(np.abs(ya - yb) <= 1e-12 * aa)
+    # equals one expert with weight one plus the shared expert
+    y1, _ = oracle.moe_experts(mw, x, np.array([[2]]), np.array([[1.0]]))
+    assert np.all(np.abs(ya - y1) <= 1e-12 * aa)
+
+
+def test_flat_router_routes_first_k_evenly():
+    mw = _tiny_moe(flat_router=True)
+    xb = synth.x_f16(2, 128, cfg=101, set_id=3)
+    out = oracle.moe_layer(mw, xb, k=4)
+    assert np.all(out["idx"] == np.arange(4))
+    assert np.allclose(out["p"], 0.25, rtol=0, atol=1e-15)
+
+
+def test_moe_layer_composes_steps():
+    mw = _tiny_moe()
+    xb = synth.x_f16(2, 128, cfg=101, set_id=4)
+    out = oracle.moe_layer(mw, xb, k=2)
+    x = brute.f16(xb)
+    assert np.allclose(out["logits"], brute.gemv(mw.router, x), rtol=0, atol=1e-12 * out["logits_abs"].max())
+    ib, _ = brute.route_topk(out["logits"], 2)
+    assert np.array_equal(out["idx"], ib)
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_generator_is_deterministic_and_in_range():
+    a = synth.affine_weights(4, 16, 256, cfg=1, set_id=3)
+    b = synth.affine_weights(4, 16, 256, cfg=1, set_id=3)
+    c = synth.affine_weights(4, 16, 256, cfg=1, set_id=4)
+    assert a.wq.tobytes() == b.wq.tobytes() and a.scales.tobytes() == b.scales.tobytes()
+    assert a.wq.tobytes() != c.wq.tobytes()
+    s = a.scales.view(np.float16).astype(np.float64)
+    assert s.min() >= np.float16(0.002) and s.max() <= np.float16(0.02)
+    bias = a.biases.view(np.float16).astype(np.float64)
+    assert np.all(np.abs(bias + 8 * s) < 0.01)
+    x = synth.x_bf16(4, 256, cfg=1, set_id=0)
+    xd = brute.bf16(x)
+    assert abs(xd.mean()) < 0.2 and 0.8 < xd.std() < 1.2

@@ -1,0 +1,96 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins catch each.
+
+A pin set that still passes on a broken oracle would not be a pin. Each
+mutation below edits one line of a private copy of ``oracle/oracle.c``
+(the committed file is never touched), builds it with gcc, swaps it in
+for the real library, and runs the pins; at least one must fail.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "bias dropped": ("return sc * (double)qo_code(bits, wq + n * words, k) + bi;",
+                     "return sc * (double)qo_code(bits, wq + n * words, k) + 0.0 * bi;"),
+    "nibble order reversed": ("int shift = bits * (int)(k % per_word);",
+                              "int shift = bits * (int)(per_word - 1 - k % per_word);"),
+    "scale and bias swapped": ("double sc = qo_f16_to_f64(s[n * groups + g]);",
+                               "double sc = qo_f16_to_f64(b[n * groups + g]) + 0.0 * qo_f16_to_f64(s[0]);"),
+    "wrong group": ("int64_t g = k / 64;", "int64_t g = (k / 64 + 1) % groups;"),
+    "fp16 exponent bias": ("v = ldexp((double)(1024 + m), e - 25);",
+                           "v = ldexp((double)(1024 + m), e - 24);"),
+    "bf16 exponent bias": ("v = ldexp((double)(128 + m), e - 134);",
+                           "v = ldexp((double)(128 + m), e - 133);"),
+    "activation reversed": ("double prod = weight(bits, wq, s, b, K, n, k) * x[k];",
+                            "double prod = weight(bits, wq, s, b, K, n, k) * x[K - 1 - k];"),
+    "ties to higher index": ("if (best < 0 || l[e] > l[best]) best = e;",
+                             "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "no renormalization": ("p[t * k + j] = prob[idx[t * k + j]] / kept;",
+                           "p[t * k + j] = prob[idx[t * k + j]] / (0.0 * kept + 1.0);"),
+    "gelu sign": ("return 0.5 * u * (1.0 + erf(u / sqrt(2.0)));",
+                  "return 0.5 * u * (1.0 - erf(u / sqrt(2.0)));"),
+    "gate and up swapped": ("h[i] = qo_gelu(z[i], act) * z[I + i];",
+                            "h[i] = qo_gelu(z[I + i], act) * z[i];"),
+    "routing weight ignored": ("yt[n] += pj * o[n];", "yt[n] += o[n] + 0.0 * pj;"),
+    "shared expert halved": ("yt[n] += o[n];\n            if (at) at[n] += oa[n];\n        }\n    }",
+                             "yt[n] += 0.5 * o[n];\n            if (at) at[n] += oa[n];\n        }\n    }"),
+}
+
+PIN_CALLS = [
+    (pins.test_f16_decode_exhaustive, {}),
+    (pins.test_bf16_decode_exhaustive, {}),
+    (pins.test_code_unpack_matches_divmod, {"bits": 4}),
+    (pins.test_code_unpack_matches_divmod, {"bits": 8}),
+    (pins.test_code_order_lsb_first, {}),
+    (pins.test_gemv_matches_bruteforce, {"bits": 4, "N": 17, "K": 256, "T": 3}),
+    (pins.test_gemv_matches_bruteforce, {"bits": 8, "N": 5, "K": 192, "T": 8}),
+    (pins.test_gemv_grouped_closed_form, {"bits": 4}),
+    (pins.test_zero_codes_give_bias_term, {"bits": 4}),
+    (pins.test_one_hot_activation_is_exact_weight, {"bits": 4}),
+    (pins.test_chunk_is_rowwise_gemv_on_bf16, {}),
+    (pins.test_topk_matches_stable_sort, {}),
+    (pins.test_topk_renormalized_softmax_identity, {}),
+    (pins.test_gelu_textbook_values_and_identities, {}),
+    (pins.test_moe_block_matches_bruteforce, {"act": 0}),
+    (pins.test_moe_identical_experts_do_not_depend_on_routing, {}),
+]
+
+
+def _build_mutant(tmp_path, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
+    mdir = tmp_path / "m"
+    mdir.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), mdir / "oracle.h")
+    (mdir / "oracle.c").write_text(src.replace(old, new))
+    lib = str(mdir / "liboracle_mut.so")
+    subprocess.run(["gcc", "-std=gnu11", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", lib,
+                    str(mdir / "oracle.c"), "-lm"], check=True)
+    return lib
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    lib = _build_mutant(tmp_path, old, new)
+    saved_lib, saved_path = oracle._lib, oracle._LIB_PATH
+    failed = []
+    try:
+        oracle._lib = None
+        oracle._LIB_PATH = lib
+        oracle._load()
+        for fn, kw in PIN_CALLS:
+            try:
+                fn(**kw)
+            except AssertionError:
+                failed.append(fn.__name__)
+    finally:
+        oracle._lib, oracle._LIB_PATH = saved_lib, saved_path
+    assert failed, f"no pin caught the planted mistake '{name}'"
