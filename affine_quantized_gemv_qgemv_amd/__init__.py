@@ -1,0 +1,265 @@
+"""Python binding of libqdecode (affine-quantized decode kernels for MI355X).
+
+Argument marshalling only: every step of every call runs in the HIP kernels
+of ``libqdecode.so``; PyTorch supplies device memory and the current
+stream. There is no fallback path: if the library is missing or the call
+fails, a ``QDecodeError`` is raised.
+
+Tensor conventions (see include/qdecode.h for the full contract):
+  * packed codes: int32 (or uint32) tensor [N][K*bits/32], LSB-first codes;
+  * scales / biases: float16 tensors [N][K/64];
+  * activations: float16 (decode) or bfloat16 (prefill) [batch][K];
+  * outputs: float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqdecode.so")
+
+QD_OK, QD_ERR_INVALID_ARGUMENT, QD_ERR_MISALIGNED, QD_ERR_UNSUPPORTED, QD_ERR_WORKSPACE, QD_ERR_HIP = range(6)
+QD_F16, QD_BF16 = 0, 1
+QD_GELU_ERF, QD_GELU_TANH = 0, 1
+
+EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qmoe_route_topk", "qmoe_expert_workspace_bytes",
+           "qmoe_expert_gemv", "qgemm_affine4_chunk", "qd_status_string", "qd_last_error")
+
+
+class QDecodeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+class MoeWeightsC(ctypes.Structure):
+    """Mirror of qd_moe_weights."""
+    _fields_ = [("E", _I32), ("H", _I32), ("I", _I32), ("I_shared", _I32), ("group_size", _I32),
+                ("act", ctypes.c_int)] + \
+        [(n, _P) for n in ("gu_q", "dn_q", "sgu_q", "sdn_q", "gu_s", "gu_b", "dn_s", "dn_b",
+                           "sgu_s", "sgu_b", "sdn_s", "sdn_b")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types declared. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python affine_quantized_gemv_qgemv_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    gemv_args = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemv_affine4.argtypes = gemv_args
+    L.qgemv_affine8.argtypes = gemv_args
+    L.qmoe_route_topk.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P]
+    L.qmoe_expert_workspace_bytes.argtypes = [ctypes.POINTER(MoeWeightsC), _I32, _I32]
+    L.qmoe_expert_workspace_bytes.restype = ctypes.c_size_t
+    L.qmoe_expert_gemv.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _I32, _I32, _P, ctypes.c_int,
+                                   _P, _P, ctypes.c_size_t, _P]
+    L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
+    L.qd_status_string.argtypes = [ctypes.c_int]
+    L.qd_status_string.restype = ctypes.c_char_p
+    L.qd_last_error.argtypes = []
+    L.qd_last_error.restype = ctypes.c_char_p
+    for fn in ("qgemv_affine4", "qgemv_affine8", "qmoe_route_topk", "qmoe_expert_gemv",
+               "qgemm_affine4_chunk"):
+        getattr(L, fn).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_name(status: int) -> str:
+    return lib().qd_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().qd_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != QD_OK:
+        raise QDecodeError(status, last_error())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float16:
+        return QD_F16
+    if x.dtype == torch.bfloat16:
+        return QD_BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {x.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got shape {tuple(t.shape)}")
+
+
+_CODES = (torch.int32, torch.uint32)
+_HALF = (torch.float16,)
+
+
+def _qgemv(bits: int, wq, scales, biases, x, out):
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _need(wq, "wq", _CODES, 2)
+    _need(scales, "scales", _HALF, 2)
+    _need(biases, "biases", _HALF, 2)
+    _need(x2, "x", (torch.float16, torch.bfloat16), 2)
+    N = wq.shape[0]
+    K = wq.shape[1] * (32 // bits)
+    batch = x2.shape[0]
+    if x2.shape[1] != K:
+        raise ValueError(f"x has {x2.shape[1]} columns, the codes imply K = {K}")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales/biases must be [N][K/64]")
+    if out is None:
+        out = torch.empty((batch, N), dtype=torch.float32, device=x2.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (batch, N):
+        raise ValueError("out must be [batch][N]")
+    fn = lib().qgemv_affine4 if bits == 4 else lib().qgemv_affine8
+    _check(fn(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x2), _x_dtype(x2), _ptr(out), N, K, batch,
+              64, _stream()))
+    return out[0] if squeeze else out
+
+
+def qgemv_affine4(wq, scales, biases, x, out=None):
+    """y[b][n] = sum_k (s*q + b)[n][k] x[b][k] with 4-bit codes; batch <= 8."""
+    return _qgemv(4, wq, scales, biases, x, out)
+
+
+def qgemv_affine8(wq, scales, biases, x, out=None):
+    """Same with 8-bit codes (router); batch <= 128."""
+    return _qgemv(8, wq, scales, biases, x, out)
+
+
+def qmoe_route_topk(logits, k: int, idx=None, weights=None):
+    """Top-k experts of each row of logits [T][E] and their renormalized softmax weights."""
+    _need(logits, "logits", (torch.float32,), 2)
+    T, E = logits.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need(idx, "idx", (torch.int32,), 2)
+    _need(weights, "weights", (torch.float32,), 2)
+    if tuple(idx.shape) != (T, k) or tuple(weights.shape) != (T, k):
+        raise ValueError("idx/weights must be [T][k]")
+    _check(lib().qmoe_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(weights), _stream()))
+    return idx, weights
+
+
+@dataclass
+class MoeWeights:
+    """Device tensors of one MoE layer (see qd_moe_weights in include/qdecode.h)."""
+    E: int
+    H: int
+    I: int
+    Is: int
+    router_q: torch.Tensor
+    router_s: torch.Tensor
+    router_b: torch.Tensor
+    gu_q: torch.Tensor
+    gu_s: torch.Tensor
+    gu_b: torch.Tensor
+    dn_q: torch.Tensor
+    dn_s: torch.Tensor
+    dn_b: torch.Tensor
+    sgu_q: torch.Tensor
+    sgu_s: torch.Tensor
+    sgu_b: torch.Tensor
+    sdn_q: torch.Tensor
+    sdn_s: torch.Tensor
+    sdn_b: torch.Tensor
+    act: int = QD_GELU_ERF
+
+    def cstruct(self) -> MoeWeightsC:
+        return MoeWeightsC(self.E, self.H, self.I, self.Is, 64, self.act,
+                           *(t.data_ptr() for t in (self.gu_q, self.dn_q, self.sgu_q, self.sdn_q,
+                                                    self.gu_s, self.gu_b, self.dn_s, self.dn_b,
+                                                    self.sgu_s, self.sgu_b, self.sdn_s, self.sdn_b)))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (
+            self.router_q, self.router_s, self.router_b, self.gu_q, self.gu_s, self.gu_b,
+            self.dn_q, self.dn_s, self.dn_b, self.sgu_q, self.sgu_s, self.sgu_b,
+            self.sdn_q, self.sdn_s, self.sdn_b))
+
+
+def qmoe_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
+    st = w.cstruct()
+    return int(lib().qmoe_expert_workspace_bytes(ctypes.byref(st), T, k))
+
+
+def qmoe_expert_gemv(w: MoeWeights, idx, weights, x, out=None, workspace=None):
+    """Routed + shared experts of one MoE layer for tokens x [T][H] (fp16 or bf16)."""
+    _need(x, "x", (torch.float16, torch.bfloat16), 2)
+    _need(idx, "idx", (torch.int32,), 2)
+    _need(weights, "weights", (torch.float32,), 2)
+    T, k = idx.shape
+    if x.shape[0] != T or x.shape[1] != w.H:
+        raise ValueError("x must be [T][H]")
+    if out is None:
+        out = torch.empty((T, w.H), dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float32,), 2)
+    st = w.cstruct()
+    need = int(lib().qmoe_expert_workspace_bytes(ctypes.byref(st), T, k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().qmoe_expert_gemv(ctypes.byref(st), _ptr(idx), _ptr(weights), T, k, _ptr(x),
+                                  _x_dtype(x), _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def qmoe_layer(w: MoeWeights, x, k: int = 8, workspace=None, logits=None, idx=None, weights=None,
+               out=None):
+    """One MoE FFN layer: int8 router GEMV -> top-k routing -> expert block."""
+    T = x.shape[0]
+    if logits is None:
+        logits = torch.empty((T, w.E), dtype=torch.float32, device=x.device)
+    qgemv_affine8(w.router_q, w.router_s, w.router_b, x, out=logits)
+    idx, weights = qmoe_route_topk(logits, k, idx, weights)
+    return qmoe_expert_gemv(w, idx, weights, x, out=out, workspace=workspace)
+
+
+def qgemm_affine4_chunk(wq, scales, biases, x, out=None):
+    """Prefill chunk Y[m][n] = sum_k w[n][k] X[m][k] for bf16 X [M][K], M <= 128."""
+    _need(wq, "wq", _CODES, 2)
+    _need(scales, "scales", _HALF, 2)
+    _need(biases, "biases", _HALF, 2)
+    _need(x, "x", (torch.bfloat16,), 2)
+    N, K = wq.shape[0], wq.shape[1] * 8
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float32,), 2)
+    _check(lib().qgemm_affine4_chunk(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), M, N,
+                                     K, 64, _stream()))
+    return out

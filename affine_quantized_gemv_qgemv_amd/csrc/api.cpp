@@ -1,0 +1,293 @@
+// C ABI of libqdecode: argument checks, then kernel launches.
+//
+// Conventions follow the uzu engine as described in
+// fiv.co.kr/repos/uzu-deep-dive.html: tensors are checked by shape and dtype
+// before use (section 4-3), failures come back as values rather than
+// panics (sections 4-2 and 4-4), and an unsupported layout is rejected with
+// an error (section 7-1). Every check here runs before any HIP call, so a
+// bad argument is reported identically on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "../../include/qdecode.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qd_status fail(qd_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+qd_status ok() {
+    g_last_error.clear();
+    return QD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+qd_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(QD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define CHECK_PTR(p)                                                               \
+    do {                                                                           \
+        if (!(p)) return fail(QD_ERR_INVALID_ARGUMENT, "%s is NULL", #p);          \
+        if (!aligned16(p)) return fail(QD_ERR_MISALIGNED, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+qd_status check_matrix(const char* fn, int32_t N, int32_t K, int32_t group_size) {
+    if (group_size != 64)
+        return fail(QD_ERR_UNSUPPORTED, "%s: group_size %d (only 64 is supported)", fn, group_size);
+    if (N < 1) return fail(QD_ERR_INVALID_ARGUMENT, "%s: N = %d must be >= 1", fn, N);
+    if (K < 64 || K % 64)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: K = %d must be a positive multiple of 64", fn, K);
+    return QD_OK;
+}
+
+qd_status gemv_common(const char* fn, int bits, int max_batch, const uint32_t* wq,
+                      const uint16_t* scales, const uint16_t* biases, const uint16_t* x,
+                      qd_dtype x_dtype, float* y, int32_t N, int32_t K, int32_t batch,
+                      int32_t group_size, qd_stream stream) {
+    qd_status st = check_matrix(fn, N, K, group_size);
+    if (st != QD_OK) return st;
+    if (batch < 1 || batch > max_batch)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: batch = %d must be in [1, %d]", fn, batch,
+                    max_batch);
+    if (x_dtype != QD_F16 && x_dtype != QD_BF16)
+        return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
+    CHECK_PTR(wq);
+    CHECK_PTR(scales);
+    CHECK_PTR(biases);
+    CHECK_PTR(x);
+    CHECK_PTR(y);
+    const int xkind = x_dtype == QD_F16 ? 0 : 1;
+    return from_hip(qd::launch_gemv(bits, wq, scales, biases, x, xkind, y, N, K, batch,
+                                    (hipStream_t)stream),
+                    fn);
+}
+
+qd_status check_moe(const char* fn, const qd_moe_weights* w) {
+    if (!w) return fail(QD_ERR_INVALID_ARGUMENT, "%s: weights is NULL", fn);
+    if (w->group_size != 64)
+        return fail(QD_ERR_UNSUPPORTED, "%s: group_size %d (only 64 is supported)", fn,
+                    w->group_size);
+    if (w->E < 1) return fail(QD_ERR_INVALID_ARGUMENT, "%s: E = %d must be >= 1", fn, w->E);
+    if (w->H < 64 || w->H % 64 || w->I < 64 || w->I % 64 || w->I_shared < 64 ||
+        w->I_shared % 64)
+        return fail(QD_ERR_INVALID_ARGUMENT,
+                    "%s: H = %d, I = %d, I_shared = %d must be positive multiples of 64", fn, w->H,
+                    w->I, w->I_shared);
+    if (w->H > (1 << 20) || w->I > (1 << 20) || w->I_shared > (1 << 20))
+        return fail(QD_ERR_UNSUPPORTED, "%s: H, I and I_shared are limited to 2^20", fn);
+    if (w->act != QD_GELU_ERF && w->act != QD_GELU_TANH)
+        return fail(QD_ERR_UNSUPPORTED, "%s: act %d", fn, (int)w->act);
+    CHECK_PTR(w->gu_q);
+    CHECK_PTR(w->gu_s);
+    CHECK_PTR(w->gu_b);
+    CHECK_PTR(w->dn_q);
+    CHECK_PTR(w->dn_s);
+    CHECK_PTR(w->dn_b);
+    CHECK_PTR(w->sgu_q);
+    CHECK_PTR(w->sgu_s);
+    CHECK_PTR(w->sgu_b);
+    CHECK_PTR(w->sdn_q);
+    CHECK_PTR(w->sdn_s);
+    CHECK_PTR(w->sdn_b);
+    return QD_OK;
+}
+
+qd::MoeArgs moe_args(const qd_moe_weights* w) {
+    qd::MoeArgs m{};
+    m.E = w->E;
+    m.H = w->H;
+    m.I = w->I;
+    m.Is = w->I_shared;
+    m.act = (int)w->act;
+    m.gu_q = w->gu_q;
+    m.dn_q = w->dn_q;
+    m.sgu_q = w->sgu_q;
+    m.sdn_q = w->sdn_q;
+    m.gu_s = w->gu_s;
+    m.gu_b = w->gu_b;
+    m.dn_s = w->dn_s;
+    m.dn_b = w->dn_b;
+    m.sgu_s = w->sgu_s;
+    m.sgu_b = w->sgu_b;
+    m.sdn_s = w->sdn_s;
+    m.sdn_b = w->sdn_b;
+    return m;
+}
+
+}  // namespace
+
+namespace qd {
+
+const DeviceInfo& device_info() {
+    static DeviceInfo infos[64];
+    static std::once_flag flags[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    std::call_once(flags[dev], [dev] {
+        DeviceInfo d;
+        d.id = dev;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            d.cus = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+                hipSuccess &&
+            v > 0)
+            d.max_lds_per_block = (size_t)v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) ==
+                hipSuccess &&
+            v > 0)
+            d.lds_per_cu = (size_t)v;
+        else
+            d.lds_per_cu = d.max_lds_per_block;
+        infos[dev] = d;
+    });
+    return infos[dev];
+}
+
+int occupancy(const void* func, int threads, size_t lds_bytes) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_tuple(dev, func, threads, lds_bytes);
+    {
+        std::lock_guard<std::mutex> g(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    if (lds_bytes > 65536)
+        (void)hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds_bytes);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, func, threads, lds_bytes) != hipSuccess ||
+        n < 1)
+        n = 1;
+    std::lock_guard<std::mutex> g(mu);
+    cache[key] = n;
+    return n;
+}
+
+}  // namespace qd
+
+extern "C" {
+
+qd_status qgemv_affine4(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
+                        int32_t batch, int32_t group_size, qd_stream stream) {
+    return gemv_common("qgemv_affine4", 4, 8, wq, scales, biases, x, x_dtype, y, N, K, batch,
+                       group_size, stream);
+}
+
+qd_status qgemv_affine8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
+                        int32_t batch, int32_t group_size, qd_stream stream) {
+    return gemv_common("qgemv_affine8", 8, 128, wq, scales, biases, x, x_dtype, y, N, K, batch,
+                       group_size, stream);
+}
+
+qd_status qmoe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* idx,
+                          float* weights, qd_stream stream) {
+    if (T < 1) return fail(QD_ERR_INVALID_ARGUMENT, "qmoe_route_topk: T = %d must be >= 1", T);
+    if (E < 1 || E > 1024)
+        return fail(QD_ERR_INVALID_ARGUMENT, "qmoe_route_topk: E = %d must be in [1, 1024]", E);
+    if (k < 1 || k > E || k > 32)
+        return fail(QD_ERR_INVALID_ARGUMENT, "qmoe_route_topk: k = %d must be in [1, min(E, 32)]",
+                    k);
+    CHECK_PTR(logits);
+    CHECK_PTR(idx);
+    CHECK_PTR(weights);
+    return from_hip(qd::launch_route_topk(logits, T, E, k, idx, weights, (hipStream_t)stream),
+                    "qmoe_route_topk");
+}
+
+size_t qmoe_expert_workspace_bytes(const qd_moe_weights* w, int32_t T, int32_t k) {
+    if (!w || T < 1 || k < 1 || w->I < 1 || w->I_shared < 1 || w->E < 1) return 0;
+    return qd::moe_workspace_bytes(moe_args(w), T, k);
+}
+
+qd_status qmoe_expert_gemv(const qd_moe_weights* w, const int32_t* idx, const float* weights,
+                           int32_t T, int32_t k, const void* x, qd_dtype x_dtype, float* y,
+                           void* workspace, size_t ws_bytes, qd_stream stream) {
+    const char* fn = "qmoe_expert_gemv";
+    qd_status st = check_moe(fn, w);
+    if (st != QD_OK) return st;
+    if (T < 1 || T > 128)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: T = %d must be in [1, 128]", fn, T);
+    if (k < 1 || k > w->E || k > 32)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: k = %d must be in [1, min(E, 32)]", fn, k);
+    if (x_dtype != QD_F16 && x_dtype != QD_BF16)
+        return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
+    CHECK_PTR(idx);
+    CHECK_PTR(weights);
+    CHECK_PTR(x);
+    CHECK_PTR(y);
+    const qd::MoeArgs m = moe_args(w);
+    const size_t need = qd::moe_workspace_bytes(m, T, k);
+    if (need > 0) {
+        if (!workspace)
+            return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+        if (!aligned16(workspace))
+            return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+        if (ws_bytes < need)
+            return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes,
+                        need);
+    }
+    return from_hip(qd::launch_moe_experts(m, idx, weights, T, k, x, x_dtype == QD_F16 ? 0 : 1, y,
+                                           workspace, ws_bytes, (hipStream_t)stream),
+                    fn);
+}
+
+qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* x, float* y, int32_t M, int32_t N, int32_t K,
+                              int32_t group_size, qd_stream stream) {
+    const char* fn = "qgemm_affine4_chunk";
+    qd_status st = check_matrix(fn, N, K, group_size);
+    if (st != QD_OK) return st;
+    if (M < 1 || M > 128)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: M = %d must be in [1, 128]", fn, M);
+    CHECK_PTR(wq);
+    CHECK_PTR(scales);
+    CHECK_PTR(biases);
+    CHECK_PTR(x);
+    CHECK_PTR(y);
+    return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, y, M, N, K,
+                                          (hipStream_t)stream),
+                    fn);
+}
+
+const char* qd_status_string(qd_status s) {
+    switch (s) {
+        case QD_OK: return "QD_OK";
+        case QD_ERR_INVALID_ARGUMENT: return "QD_ERR_INVALID_ARGUMENT";
+        case QD_ERR_MISALIGNED: return "QD_ERR_MISALIGNED";
+        case QD_ERR_UNSUPPORTED: return "QD_ERR_UNSUPPORTED";
+        case QD_ERR_WORKSPACE: return "QD_ERR_WORKSPACE";
+        case QD_ERR_HIP: return "QD_ERR_HIP";
+    }
+    return "QD_UNKNOWN_STATUS";
+}
+
+const char* qd_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,336 @@
+// Device helpers shared by the libqdecode kernels (gfx950 / CDNA4, wave64).
+//
+// Weight format ([TF] = jeff.news/article/5193, section "성능과 제약",
+// performance and constraints): MLX affine quantization, codes of 4 bits
+// (8 for the router), one fp16 scale and one fp16 bias per group of 64
+// inputs, w = s*q + b. Codes are packed LSB-first, eight (or four) per
+// uint32 along the input dimension.
+//
+// Arithmetic used on the fp16-activation path
+// -------------------------------------------
+// OR-ing a 4-bit code into the low mantissa bits of fp16 1024.0 (0x6400)
+// gives exactly 1024 + q; OR-ing it one nibble higher gives 1024 + 16q.
+// One v_and_or_b32 therefore turns two codes of a word (the nibbles at
+// bits 0 and 16, or 4 and 20) into a packed half2, and v_dot2_f32_f16
+// multiplies such a pair with two activations and adds both products into
+// an fp32 accumulator. Each product is exact in fp32 (11-bit times 11-bit
+// significands). The 1024 offsets and the factor 16 are removed once per
+// 16-byte chunk with per-chunk activation sums computed while staging x:
+//     sum_k q_k x_k = acc_1 + acc_16 / 16 - (1024 * sum_1 x + 64 * sum_16 x)
+// where class "1" holds the codes at nibbles 0, 2, 4, 6 and class "16"
+// those at nibbles 1, 3, 5, 7. The affine epilogue then adds
+// s_g * (that sum) + b_g * (sum of the chunk's activations).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <climits>
+
+namespace qd {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kMagic16 = 0x64006400u;  // fp16 pair (1024, 1024)
+
+// A value the compiler must keep in a VGPR. Used for the fp16 magic so that
+// (w & mask) | magic is selected as one v_and_or_b32 (a VOP3 on gfx9 reads at
+// most one SGPR or constant; the mask takes that slot).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
+                                  false);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(uint16_t lo, uint16_t hi) {
+    return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Activation element kinds accepted by the staging code.
+enum XKind : int { X_F16 = 0, X_BF16 = 1, X_F32 = 2 };
+
+__device__ __forceinline__ float load_x(const void* x, int kind, int64_t i) {
+    if (kind == X_F16) return h2f(((const uint16_t*)x)[i]);
+    if (kind == X_BF16) return bf2f(((const uint16_t*)x)[i]);
+    return ((const float*)x)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk partial dot products. A chunk is 16 bytes of codes (32 int4 or
+// 16 int8 codes = 4 words); the activations for it sit in LDS in the order
+// the unpacking produces the codes.
+// ---------------------------------------------------------------------------
+
+// int4 codes, fp32 activations: lo bytes are q0,q2,q4,q6 and hi bytes
+// q1,q3,q5,q7; xa = (x0,x2,x4,x6), xb = (x1,x3,x5,x7).
+__device__ __forceinline__ float word_i4_f32(uint32_t w, const float4& xa, const float4& xb,
+                                             float acc) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+    acc = fmaf((float)(lo & 0xFFu), xa.x, acc);
+    acc = fmaf((float)((lo >> 8) & 0xFFu), xa.y, acc);
+    acc = fmaf((float)((lo >> 16) & 0xFFu), xa.z, acc);
+    acc = fmaf((float)(lo >> 24), xa.w, acc);
+    acc = fmaf((float)(hi & 0xFFu), xb.x, acc);
+    acc = fmaf((float)((hi >> 8) & 0xFFu), xb.y, acc);
+    acc = fmaf((float)((hi >> 16) & 0xFFu), xb.z, acc);
+    acc = fmaf((float)(hi >> 24), xb.w, acc);
+    return acc;
+}
+
+// int8 codes, fp32 activations in natural order.
+__device__ __forceinline__ float word_i8_f32(uint32_t w, const float4& xa, float acc) {
+    acc = fmaf((float)(w & 0xFFu), xa.x, acc);
+    acc = fmaf((float)((w >> 8) & 0xFFu), xa.y, acc);
+    acc = fmaf((float)((w >> 16) & 0xFFu), xa.z, acc);
+    acc = fmaf((float)(w >> 24), xa.w, acc);
+    return acc;
+}
+
+// Sum over the `width` lanes of an aligned lane segment (width a power of two).
+template <int WIDTH>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Activation staging into LDS.
+//
+// Layout for nc chunks and nb activation vectors:
+//   xs[b][q][c]  (uint4; q < QPC words-of-x per chunk), consecutive chunks
+//                at consecutive 16-byte slots so the lanes of a row segment
+//                read disjoint banks;
+//   cs[b][c]     float2 (1024*sum_1 + 64*sum_16 (or 1024*sum), sum) on the
+//                fp16 path, float sum on the fp32 path.
+// ---------------------------------------------------------------------------
+template <int BITS, int XF>
+struct Stage {
+    static constexpr int CC = 128 / BITS;                               // codes per chunk
+    static constexpr int QPC = XF ? CC / 4 : (BITS == 4 ? 4 : 2);       // uint4 per chunk
+    static constexpr int CSZ = XF ? 4 : 8;                              // const bytes per chunk
+    static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
+};
+
+// Stage chunks [c0, c0 + nc) of activation vector(s) x[b][K] for b < nb into
+// lds. xstride = elements between consecutive vectors.
+template <int BITS, int XF>
+__device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0, int nc,
+                        uint4* lds) {
+    using St = Stage<BITS, XF>;
+    constexpr int CC = St::CC;
+    constexpr int QPC = St::QPC;
+    uint4* xs = lds;
+    for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
+        const int b = item / nc, c = item - b * nc;
+        const int64_t base = (int64_t)b * xstride + (int64_t)(c0 + c) * CC;
+        if constexpr (XF == 0) {
+            // fp16 activations, kept as raw bits
+            const uint16_t* xp = (const uint16_t*)x + base;
+            float s1 = 0.f, s16 = 0.f;
+            if constexpr (BITS == 4) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 raw = *(const uint4*)(xp + 8 * q);
+                    uint16_t h[8];
+                    h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
+                    h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
+                    h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
+                    h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                    uint4 o;
+                    o.x = pack_h2(h[0], h[4]);
+                    o.y = pack_h2(h[1], h[5]);
+                    o.z = pack_h2(h[2], h[6]);
+                    o.w = pack_h2(h[3], h[7]);
+                    xs[(b * QPC + q) * nc + c] = o;
+                    s1 += (h2f(h[0]) + h2f(h[4])) + (h2f(h[2]) + h2f(h[6]));
+                    s16 += (h2f(h[1]) + h2f(h[5])) + (h2f(h[3]) + h2f(h[7]));
+                }
+                float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
+                cs[b * nc + c] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint4 raw = *(const uint4*)(xp + 8 * q);   // two words' x (8 values)
+                    uint16_t h[8];
+                    h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
+                    h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
+                    h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
+                    h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                    uint4 o;
+                    o.x = pack_h2(h[0], h[2]);
+                    o.y = pack_h2(h[1], h[3]);
+                    o.z = pack_h2(h[4], h[6]);
+                    o.w = pack_h2(h[5], h[7]);
+                    xs[(b * QPC + q) * nc + c] = o;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s1 += h2f(h[i]);
+                }
+                float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
+                cs[b * nc + c] = make_float2(1024.f * s1, s1);
+            }
+        } else {
+            float v[CC];
+#pragma unroll
+            for (int i = 0; i < CC; ++i) v[i] = load_x(x, kind, base + i);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < CC; ++i) sum += v[i];
+            if constexpr (BITS == 4) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* u = v + 8 * w;
+                    xs[(b * QPC + 2 * w) * nc + c] =
+                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
+                                   __float_as_uint(u[4]), __float_as_uint(u[6]));
+                    xs[(b * QPC + 2 * w + 1) * nc + c] =
+                        make_uint4(__float_as_uint(u[1]), __float_as_uint(u[3]),
+                                   __float_as_uint(u[5]), __float_as_uint(u[7]));
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* u = v + 4 * w;
+                    xs[(b * QPC + w) * nc + c] =
+                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[1]),
+                                   __float_as_uint(u[2]), __float_as_uint(u[3]));
+                }
+            }
+            float* cs = (float*)(xs + (size_t)nb * QPC * nc);
+            cs[b * nc + c] = sum;
+        }
+    }
+}
+
+// Partial dot products of one 16-byte code chunk of each of R rows with every
+// activation vector b < B, followed by the affine epilogue into y[r][b]:
+//   y[r][b] += s_r * (sum_k q_k x_k) + bias_r * (sum_k x_k).
+// The chunk's activations are read from LDS once and shared by the R rows.
+template <int BITS, int XF, int B, int R>
+__device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&sc)[R],
+                                           const float (&bi)[R], const uint4* lds, int nb_staged,
+                                           int nc, int c, uint32_t magic, float (&y)[R][B]) {
+    using St = Stage<BITS, XF>;
+    constexpr int QPC = St::QPC;
+    const uint4* xs = lds;
+    if constexpr (XF == 0) {
+        const float2* cs = (const float2*)(xs + (size_t)nb_staged * QPC * nc);
+        float a1[R][B], a16[R][B];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) a1[r][b] = a16[r][b] = 0.f;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint4 xq[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
+                    const uint32_t p04 = (w & 0x000F000Fu) | magic;   // 1024+q0, 1024+q4
+                    const uint32_t p15 = (w & 0x00F000F0u) | magic;   // 1024+16q1, 1024+16q5
+                    const uint32_t w8 = w >> 8;
+                    const uint32_t p26 = (w8 & 0x000F000Fu) | magic;  // 1024+q2, 1024+q6
+                    const uint32_t p37 = (w8 & 0x00F000F0u) | magic;  // 1024+16q3, 1024+16q7
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        a1[r][b] = dot2(p04, xq[b].x, a1[r][b]);
+                        a16[r][b] = dot2(p15, xq[b].y, a16[r][b]);
+                        a1[r][b] = dot2(p26, xq[b].z, a1[r][b]);
+                        a16[r][b] = dot2(p37, xq[b].w, a16[r][b]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                uint4 xq[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t w0 = q == 0 ? cw[r].x : cw[r].z;
+                    const uint32_t w1 = q == 0 ? cw[r].y : cw[r].w;
+                    const uint32_t p02 = (w0 & 0x00FF00FFu) | magic;          // 1024+q0, 1024+q2
+                    const uint32_t p13 = ((w0 >> 8) & 0x00FF00FFu) | magic;   // 1024+q1, 1024+q3
+                    const uint32_t r02 = (w1 & 0x00FF00FFu) | magic;
+                    const uint32_t r13 = ((w1 >> 8) & 0x00FF00FFu) | magic;
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        a1[r][b] = dot2(p02, xq[b].x, a1[r][b]);
+                        a16[r][b] = dot2(p13, xq[b].y, a16[r][b]);
+                        a1[r][b] = dot2(r02, xq[b].z, a1[r][b]);
+                        a16[r][b] = dot2(r13, xq[b].w, a16[r][b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float2 k = cs[b * nc + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float p =
+                    (BITS == 4 ? fmaf(a16[r][b], 0.0625f, a1[r][b]) : a1[r][b] + a16[r][b]) - k.x;
+                y[r][b] = fmaf(sc[r], p, y[r][b]);
+                y[r][b] = fmaf(bi[r], k.y, y[r][b]);
+            }
+        }
+    } else {
+        const float* cs = (const float*)(xs + (size_t)nb_staged * QPC * nc);
+        float acc[R][B];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if constexpr (BITS == 4) {
+                    const uint4 xa = xs[(b * QPC + 2 * q) * nc + c];
+                    const uint4 xb = xs[(b * QPC + 2 * q + 1) * nc + c];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
+                        acc[r][b] = word_i4_f32(w, *(const float4*)&xa, *(const float4*)&xb, acc[r][b]);
+                    }
+                } else {
+                    const uint4 xa = xs[(b * QPC + q) * nc + c];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
+                        acc[r][b] = word_i8_f32(w, *(const float4*)&xa, acc[r][b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float xsum = cs[b * nc + c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                y[r][b] = fmaf(sc[r], acc[r][b], y[r][b]);
+                y[r][b] = fmaf(bi[r], xsum, y[r][b]);
+            }
+        }
+    }
+}
+
+}  // namespace qd

@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace qd {
+
+struct DeviceInfo {
+    int id = -1;
+    int cus = 256;                  // compute units
+    size_t max_lds_per_block = 65536;
+    size_t lds_per_cu = 65536;
+};
+
+// Properties of the calling thread's current device (queried once per device).
+const DeviceInfo& device_info();
+
+// Resident workgroups per CU for a kernel at this block size and LDS use.
+int occupancy(const void* func, int threads, size_t lds_bytes);
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// x kinds: 0 = fp16 bits, 1 = bf16 bits, 2 = fp32.
+hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                       const void* x, int xkind, float* y, int N, int K, int batch,
+                       hipStream_t st);
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             hipStream_t st);
+
+struct MoeArgs {
+    int E, H, I, Is, act;
+    const uint32_t *gu_q, *dn_q, *sgu_q, *sdn_q;
+    const uint16_t *gu_s, *gu_b, *dn_s, *dn_b, *sgu_s, *sgu_b, *sdn_s, *sdn_b;
+};
+
+size_t moe_workspace_bytes(const MoeArgs& m, int T, int k);
+
+hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
+                              const void* x, int xkind, float* y, void* ws, size_t ws_bytes,
+                              hipStream_t st);
+
+hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                             const uint16_t* x_bf16, float* y, int M, int N, int K,
+                             hipStream_t st);
+
+}  // namespace qd

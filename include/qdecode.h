@@ -1,0 +1,159 @@
+/*
+ * libqdecode: affine-quantized decode contractions for AMD Instinct MI355X
+ * (gfx950), as hand-written HIP kernels behind a plain C ABI.
+ *
+ * Sources for what each call computes:
+ *   [TF]  jeff.news/article/5193, on TurboFieldfare (Gemma 4 26B-A4B on Apple
+ *         Silicon): section "성능과 제약" (performance and constraints) fixes
+ *         the weight format -- MLX affine quantization with 4-bit codes and
+ *         a scale and a bias per group of 64 inputs, the router at 8 bits;
+ *         section "내부 구조가 진짜 흥미로운 부분" (internals) describes the
+ *         per-layer flow -- router on the GPU, top-8 expert IDs, a resident
+ *         shared expert whose output is combined with the routed output, and
+ *         prefill in chunks of at most 128 tokens.
+ *   [uzu] fiv.co.kr/repos/uzu-deep-dive.html, sections 4-3 and 4-4 (tensors
+ *         checked by shape and dtype; errors returned as values) and 7-1
+ *         (a CPU reference matmul that rejects unsupported layouts).
+ *
+ * Data layout (all row-major, rows along the output dimension N):
+ *   codes   uint32_t wq[N][K*bits/32]; code k of a row sits in word
+ *           k/(32/bits) at bit offset bits*(k mod (32/bits)) (LSB first);
+ *   scales  fp16 s[N][K/64], biases fp16 b[N][K/64] (raw uint16_t bits);
+ *   weight  w[n][k] = s[n][k/64] * q[n][k] + b[n][k/64].
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is a DEVICE pointer (hipMalloc / torch CUDA tensor) that
+ *     the caller owns. The library allocates, frees and copies nothing and
+ *     never synchronizes; work is enqueued on `stream` (a hipStream_t; NULL
+ *     selects the null stream) and is complete once that stream is.
+ *   - Inputs must stay unmodified until the stream reaches the call;
+ *     outputs must not overlap inputs or each other.
+ *   - All arguments are checked before anything is launched. On an error
+ *     nothing is written and the status says why; qd_last_error() gives a
+ *     thread-local message. A launch failure returns QD_ERR_HIP.
+ *   - Pointers must be 16-byte aligned; group_size must be 64; K must be a
+ *     multiple of 64.
+ *   - The calls are stateless and may be issued from several threads.
+ */
+#ifndef QDECODE_H
+#define QDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QD_OK = 0,
+    QD_ERR_INVALID_ARGUMENT = 1, /* null pointer, size out of range, K % 64 != 0 */
+    QD_ERR_MISALIGNED = 2,       /* a pointer is not 16-byte aligned */
+    QD_ERR_UNSUPPORTED = 3,      /* group_size != 64, dtype or shape not built */
+    QD_ERR_WORKSPACE = 4,        /* workspace missing or too small */
+    QD_ERR_HIP = 5               /* the HIP runtime reported an error */
+} qd_status;
+
+typedef enum { QD_F16 = 0, QD_BF16 = 1 } qd_dtype;
+
+typedef enum { QD_GELU_ERF = 0, QD_GELU_TANH = 1 } qd_act;
+
+typedef void* qd_stream; /* hipStream_t */
+
+/*
+ * y[t][n] = sum_k w[n][k] * x[t][k] for t < batch, with 4-bit codes.
+ * [TF] performance section (4-bit affine weights, group 64).
+ *   wq [N][K/8] uint32, scales/biases [N][K/64] fp16 bits,
+ *   x  [batch][K] fp16 (QD_F16) or bf16 (QD_BF16) bits, y [batch][N] fp32.
+ *   1 <= batch <= 8, N >= 1, K >= 64, K % 64 == 0, group_size == 64.
+ */
+qd_status qgemv_affine4(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, qd_dtype x_dtype, float* y,
+                        int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                        qd_stream stream);
+
+/*
+ * The same contraction with 8-bit codes (the router of a MoE layer:
+ * [TF] performance section, router at 8 bits; internals section, router
+ * computed on the GPU from resident weights).
+ *   wq [N][K/4] uint32; 1 <= batch <= 128 (prefill routers run a whole
+ *   chunk of tokens); otherwise as qgemv_affine4.
+ */
+qd_status qgemv_affine8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, qd_dtype x_dtype, float* y,
+                        int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                        qd_stream stream);
+
+/*
+ * Top-k routing ([TF] top and internals sections: each token uses only the
+ * router's top-8 experts). For each token t: idx[t][0..k) are the experts
+ * with the k largest logits in descending order, equal logits going to the
+ * lower expert index; weights[t][j] = softmax over all E logits, kept for
+ * the k selected experts and renormalized to sum to one (equivalently
+ * exp(l_j - l_max) / sum over the k kept of exp(l - l_max)).
+ *   logits [T][E] fp32, idx [T][k] int32, weights [T][k] fp32.
+ *   1 <= T, 1 <= E <= 1024, 1 <= k <= min(E, 32).
+ */
+qd_status qmoe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                          int32_t* idx, float* weights, qd_stream stream);
+
+/*
+ * One MoE FFN layer's experts ([TF] internals section): for each token t
+ * and slot j with e = idx[t][j],
+ *   z = W_gu[e] x_t (2I outputs: rows [0,I) gate, rows [I,2I) up),
+ *   h = act(z[0:I]) * z[I:2I],  o_j = W_dn[e] h;
+ * the shared expert gives o_s the same way, and
+ *   y[t] = sum_j weights[t][j] * o_j + o_s.
+ * All intermediates stay in fp32. Expert ids outside [0, E) contribute
+ * nothing.
+ *   gu_q [E][2I][H/8], gu_s/gu_b [E][2I][H/64];
+ *   dn_q [E][H][I/8],  dn_s/dn_b [E][H][I/64];
+ *   sgu_q [2Is][H/8], sgu_s/sgu_b [2Is][H/64];
+ *   sdn_q [H][Is/8],  sdn_s/sdn_b [H][Is/64];
+ *   H, I, Is multiples of 64; act selects exact-erf or tanh GELU.
+ */
+typedef struct {
+    int32_t E, H, I, I_shared, group_size;
+    qd_act act;
+    const uint32_t *gu_q, *dn_q, *sgu_q, *sdn_q;
+    const uint16_t *gu_s, *gu_b, *dn_s, *dn_b, *sgu_s, *sgu_b, *sdn_s, *sdn_b;
+} qd_moe_weights;
+
+/* Bytes of device workspace qmoe_expert_gemv needs for T tokens and k slots. */
+size_t qmoe_expert_workspace_bytes(const qd_moe_weights* w, int32_t T, int32_t k);
+
+/*
+ *   idx/weights [T][k] (device, as produced by qmoe_route_topk),
+ *   x [T][H] fp16 (QD_F16) or bf16 (QD_BF16) bits, y [T][H] fp32,
+ *   workspace: device scratch of at least qmoe_expert_workspace_bytes();
+ *   1 <= T <= 128 (a prefill chunk, [TF] internals), 1 <= k <= min(E, 32).
+ * T == 1 runs the decode GEMV kernels; T > 1 groups the (token, slot)
+ * pairs by expert so each selected expert's weights are read once.
+ */
+qd_status qmoe_expert_gemv(const qd_moe_weights* w, const int32_t* idx, const float* weights,
+                           int32_t T, int32_t k, const void* x, qd_dtype x_dtype, float* y,
+                           void* workspace, size_t ws_bytes, qd_stream stream);
+
+/*
+ * Prefill chunk ([TF] internals: prompts run in chunks of at most 128 tokens
+ * so one fetch of a weight serves many rows):
+ *   Y[m][n] = sum_k w[n][k] * X[m][k],  X [M][K] bf16 bits, Y [M][N] fp32.
+ *   1 <= M <= 128; 4-bit codes as qgemv_affine4. Runs on bf16 MFMA with the
+ *   exact integer codes as the matrix operand and the scales and biases
+ *   applied per group in fp32.
+ */
+qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                              const uint16_t* x, float* y,
+                              int32_t M, int32_t N, int32_t K, int32_t group_size,
+                              qd_stream stream);
+
+/* Human-readable name of a status. */
+const char* qd_status_string(qd_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* qd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QDECODE_H */

@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments with the documented status before
+touching the HIP runtime (errors as values, as the uzu walk-through at
+fiv.co.kr/repos/uzu-deep-dive.html sections 4-4 and 7-1 describes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import affine_quantized_gemv_qgemv_amd as qd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qdecode.h")
+
+A = 1 << 20      # a fake, 16-byte aligned "device" address (never dereferenced)
+MIS = A + 4      # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for fn in ("qgemv_affine4", "qgemv_affine8", "qmoe_route_topk", "qmoe_expert_gemv",
+               "qgemm_affine4_chunk"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = qd.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing
+    assert set(qd.EXPORTS) <= set(declared_functions())
+
+
+def test_status_strings():
+    assert qd.status_name(qd.QD_OK) == "QD_OK"
+    assert qd.status_name(qd.QD_ERR_MISALIGNED) == "QD_ERR_MISALIGNED"
+    assert qd.status_name(99) == "QD_UNKNOWN_STATUS"
+
+
+def gemv(fn="qgemv_affine4", wq=A, s=A, b=A, x=A, dt=0, y=A, N=16, K=128, batch=1, g=64):
+    return getattr(qd.lib(), fn)(wq, s, b, x, dt, y, N, K, batch, g, None)
+
+
+@pytest.mark.parametrize("fn", ["qgemv_affine4", "qgemv_affine8"])
+def test_gemv_argument_errors(fn):
+    E = qd
+    assert gemv(fn, g=32) == E.QD_ERR_UNSUPPORTED
+    assert "group_size" in qd.last_error()
+    assert gemv(fn, K=100) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, K=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, N=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, batch=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, batch=129) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, wq=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert "wq" in qd.last_error()
+    assert gemv(fn, y=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv(fn, x=MIS) == E.QD_ERR_MISALIGNED
+    assert gemv(fn, s=MIS) == E.QD_ERR_MISALIGNED
+    assert gemv(fn, dt=7) == E.QD_ERR_UNSUPPORTED
+
+
+def test_affine4_batch_limit_is_eight():
+    assert gemv("qgemv_affine4", batch=9) == qd.QD_ERR_INVALID_ARGUMENT
+
+
+def test_route_argument_errors():
+    L = qd.lib()
+    assert L.qmoe_route_topk(A, 0, 128, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(A, 1, 0, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(A, 1, 4, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(A, 1, 2048, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(A, 1, 128, 33, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(None, 1, 128, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert L.qmoe_route_topk(A, 1, 128, 8, MIS, A, None) == qd.QD_ERR_MISALIGNED
+
+
+def moe_struct(**kw):
+    f = dict(E=128, H=2816, I=704, I_shared=2112, group_size=64, act=0)
+    f.update({n: A for n in ("gu_q", "dn_q", "sgu_q", "sdn_q", "gu_s", "gu_b", "dn_s", "dn_b",
+                            "sgu_s", "sgu_b", "sdn_s", "sdn_b")})
+    f.update(kw)
+    return qd.MoeWeightsC(**f)
+
+
+def moe_call(st, T=1, k=8, ws=A, ws_bytes=1 << 30, x=A, dt=0):
+    return qd.lib().qmoe_expert_gemv(ctypes.byref(st), A, A, T, k, x, dt, A, ws, ws_bytes, None)
+
+
+def test_moe_argument_errors():
+    L = qd.lib()
+    assert L.qmoe_expert_gemv(None, A, A, 1, 8, A, 0, A, A, 1 << 30, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(group_size=128)) == qd.QD_ERR_UNSUPPORTED
+    assert moe_call(moe_struct(H=100)) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(act=5)) == qd.QD_ERR_UNSUPPORTED
+    assert moe_call(moe_struct(dn_s=None)) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(sgu_q=MIS)) == qd.QD_ERR_MISALIGNED
+    assert moe_call(moe_struct(), T=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(), T=129) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(), k=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(E=4), k=8) == qd.QD_ERR_INVALID_ARGUMENT
+    assert moe_call(moe_struct(), ws=None) == qd.QD_ERR_WORKSPACE
+    assert moe_call(moe_struct(), ws_bytes=16) == qd.QD_ERR_WORKSPACE
+    assert moe_call(moe_struct(), ws=MIS) == qd.QD_ERR_MISALIGNED
+    assert moe_call(moe_struct(), dt=3) == qd.QD_ERR_UNSUPPORTED
+
+
+def test_moe_workspace_size_grows_with_tokens():
+    st = moe_struct()
+    L = qd.lib()
+    w1 = L.qmoe_expert_workspace_bytes(ctypes.byref(st), 1, 8)
+    w128 = L.qmoe_expert_workspace_bytes(ctypes.byref(st), 128, 8)
+    assert 0 < w1 < w128
+    assert L.qmoe_expert_workspace_bytes(None, 1, 8) == 0
+
+
+def test_chunk_argument_errors():
+    L = qd.lib()
+    f = lambda **kw: L.qgemm_affine4_chunk(kw.get("wq", A), A, A, kw.get("x", A), A, kw.get("M", 128),
+                                           kw.get("N", 256), kw.get("K", 256), kw.get("g", 64), None)
+    assert f(M=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(M=129) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(K=96) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(g=128) == qd.QD_ERR_UNSUPPORTED
+    assert f(wq=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(x=MIS) == qd.QD_ERR_MISALIGNED

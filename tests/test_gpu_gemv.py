@@ -1,0 +1,156 @@
+"""GPU parity of qgemv_affine4 / qgemv_affine8 against the fp64 oracle.
+
+Bar: |y_gpu - y_ref| <= 1e-4 * sum_k |w_k x_k| + 1e-6 per output, and
+bit-exact results for the special inputs whose exact answer is
+representable in fp32 (one-hot activations, zero activations,
+power-of-two scaling).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_within, dev_bf16, dev_half, dev_weights
+
+qd = pytest.importorskip("affine_quantized_gemv_qgemv_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemv(bits, w, xb, xdt="f16", out=None):
+    wq, s, b = dev_weights(w)
+    x = dev_half(xb) if xdt == "f16" else dev_bf16(xb)
+    fn = qd.qgemv_affine4 if bits == 4 else qd.qgemv_affine8
+    y = fn(wq, s, b, x, out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def ref_gemv(w, xb, xdt="f16", rows=None):
+    return oracle.gemv_f16(w, xb, rows) if xdt == "f16" else oracle.gemm_chunk(w, xb, rows)
+
+
+def draw_x(T, K, xdt, seed):
+    return synth.x_f16(T, K, cfg=200, set_id=seed) if xdt == "f16" else synth.x_bf16(T, K, cfg=200, set_id=seed)
+
+
+SMALL = [(1, 64), (3, 128), (17, 704), (5, 2112), (129, 2816), (33, 4096), (70, 8192), (9, 14336)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("N,K", SMALL)
+def test_small_shapes(bits, xdt, N, K):
+    for batch in (1, 3, 8):
+        seed = N * 7 + K + batch
+        w = synth.affine_weights(bits, N, K, cfg=200, set_id=seed)
+        xb = draw_x(batch, K, xdt, seed)
+        y = run_gemv(bits, w, xb, xdt).cpu().numpy()
+        yr, a = ref_gemv(w, xb, xdt)
+        print(f"bits={bits} xdt={xdt} N={N} K={K} batch={batch}", flush=True)
+        assert_within(y, yr, a, f"bits={bits} {xdt} N={N} K={K} batch={batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 5, 6, 7, 8])
+def test_every_batch_size(batch):
+    w = synth.affine_weights(4, 100, 1024, cfg=201, set_id=batch)
+    xb = draw_x(batch, 1024, "f16", batch)
+    y = run_gemv(4, w, xb).cpu().numpy()
+    yr, a = ref_gemv(w, xb)
+    assert_within(y, yr, a, f"batch={batch}")
+
+
+def test_router_prefill_batch_128():
+    w = synth.affine_weights(8, 128, 2816, cfg=202, set_id=0)
+    for xdt in ("f16", "bf16"):
+        xb = draw_x(128, 2816, xdt, 1)
+        y = run_gemv(8, w, xb, xdt).cpu().numpy()
+        yr, a = ref_gemv(w, xb, xdt)
+        assert_within(y, yr, a, f"router T=128 {xdt}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_one_hot_is_bit_exact(bits):
+    N, K = 64, 2048
+    w = synth.affine_weights(bits, N, K, cfg=203, set_id=bits)
+    one = np.float16(1.0).view(np.uint16)
+    for k in (0, 1, 7, 31, 32, 63, 64, 100, 1000, 2047):
+        xb = np.zeros((1, K), np.uint16)
+        xb[0, k] = one
+        y = run_gemv(bits, w, xb).cpu().numpy().astype(np.float64)
+        yr, _ = ref_gemv(w, xb)
+        assert np.array_equal(y, yr), f"k={k}"
+
+
+def test_zero_activation_gives_zero():
+    w = synth.affine_weights(4, 40, 1024, cfg=204, set_id=0)
+    y = run_gemv(4, w, np.zeros((3, 1024), np.uint16)).cpu().numpy()
+    assert np.all(y == 0.0)
+
+
+def test_power_of_two_scaling_is_exact():
+    N, K = 300, 4096
+    w = synth.affine_weights(4, N, K, cfg=205, set_id=0)
+    xb = synth.x_f16(2, K, cfg=205, set_id=0)
+    x = xb.view(np.float16)
+    y1 = run_gemv(4, w, xb).cpu().numpy()
+    for j in (1, 3):
+        xs = (x.astype(np.float32) * 2.0 ** j).astype(np.float16).view(np.uint16)
+        yj = run_gemv(4, w, xs).cpu().numpy()
+        assert np.array_equal(yj, y1 * np.float32(2.0 ** j)), f"2^{j}"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_constant_and_zero_codes(bits):
+    K = 1024
+    for kind, c in (("zero", 0), ("const", 5), ("const", (1 << bits) - 1)):
+        w = synth.affine_weights(bits, 50, K, cfg=206, set_id=c, codes=kind, const_code=c)
+        xb = synth.x_f16(2, K, cfg=206, set_id=c)
+        y = run_gemv(bits, w, xb).cpu().numpy()
+        yr, a = ref_gemv(w, xb)
+        assert_within(y, yr, a, f"{kind} {c}")
+
+
+def test_deterministic_and_no_out_of_bounds_writes():
+    N, K, batch = 1000, 4096, 3
+    w = synth.affine_weights(4, N, K, cfg=207, set_id=0)
+    xb = synth.x_f16(batch, K, cfg=207, set_id=0)
+    guard = 4096
+    buf = torch.full((guard + batch * N + guard,), float("nan"), device="cuda")
+    out = buf[guard:guard + batch * N].view(batch, N)
+    y1 = run_gemv(4, w, xb, out=out).clone()
+    y2 = run_gemv(4, w, xb).clone()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + batch * N:]).all()
+    assert torch.equal(y1, y2)
+
+
+# --------------------------------------------------------------- full sizes
+
+FULL = [
+    ("c1 4096->4096", 4096, 4096, 1, None),
+    ("c2 gate+up 4096->28672", 4096, 28672, 1, None),
+    ("c2 down 14336->4096", 14336, 4096, 1, None),
+    ("c5 8192->28672 b1", 8192, 28672, 1, 512),
+    ("c5 28672->8192 b1", 28672, 8192, 1, 512),
+    ("c5 8192->28672 b8", 8192, 28672, 8, 384),
+    ("c5 28672->8192 b2", 28672, 8192, 2, 384),
+    ("c5 28672->8192 b4", 28672, 8192, 4, 384),
+    ("c5 28672->8192 b8", 28672, 8192, 8, 384),
+]
+
+
+@pytest.mark.parametrize("name,K,N,batch,nsample", FULL, ids=[f[0] for f in FULL])
+def test_full_size(name, K, N, batch, nsample):
+    print(name, flush=True)
+    w = synth.affine_weights(4, N, K, cfg=5, set_id=0)
+    xb = synth.x_f16(batch, K, cfg=5, set_id=0)
+    y = run_gemv(4, w, xb).cpu().numpy()
+    if nsample is None:
+        yr, a = ref_gemv(w, xb)
+        assert_within(y, yr, a, name)
+    else:
+        r = np.random.default_rng(N + K + batch)
+        rows = np.unique(np.concatenate([r.choice(N, nsample, replace=False), [0, N - 1]]))
+        yr, a = ref_gemv(w, xb, rows=rows)
+        assert_within(y[:, rows], yr, a, name)
