@@ -123,7 +123,7 @@ struct Stage {
     static constexpr int CC = 128 / BITS;                               // codes per chunk
     static constexpr int QPC = XF ? CC / 4 : (BITS == 4 ? 4 : 2);       // uint4 per chunk
     static constexpr int CSZ = XF ? 4 : 8;                              // const bytes per chunk
-    static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
+    __host__ __device__ static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
 };
 
 // Stage chunks [c0, c0 + nc) of activation vector(s) x[b][K] for b < nb into

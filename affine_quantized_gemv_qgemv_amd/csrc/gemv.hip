@@ -38,8 +38,16 @@ struct GemvArgs {
     int atomic_out;
 };
 
-template <int BITS, int XF, int B, int LPR, int R, int U>
-__global__ __launch_bounds__(256) void qgemv_kernel(GemvArgs a) {
+// One round of loads: U steps (16-byte chunks per lane) of R rows.
+template <int R, int U>
+struct Round {
+    uint4 cw[U][R];
+    uint16_t sc[U][R], bi[U][R];   // raw fp16 bits; masked when consumed
+};
+
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
+    GemvArgs a) {
     extern __shared__ uint4 lds[];
     constexpr int CC = 128 / BITS;     // codes per 16-byte chunk
     constexpr int CPG = 64 / CC;       // chunks per group of 64
@@ -51,76 +59,118 @@ __global__ __launch_bounds__(256) void qgemv_kernel(GemvArgs a) {
     const int G = a.K / 64;
     const int64_t wpr = (int64_t)a.K * BITS / 32;  // words per row
 
-    stage_x<BITS, XF>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
     const int seg = lane / LPR, sl = lane % LPR;
     const int nwaves = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6;
-    const int S = (nc + LPR - 1) / LPR;
+    // wave-uniform: keeps the tile bounds and loop control in scalar registers
+    const int gw = blockIdx.x * nwaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = gridDim.x * nwaves;
+    const int S = (nc + LPR - 1) / LPR;            // steps per row
+    const int RPT = (S + U - 1) / U;               // rounds per tile
     const int ntiles = (a.N + ROWS - 1) / ROWS;
-    const uint32_t magic = in_vgpr(kMagic16);
+    // contiguous, balanced share of tiles for this wave
+    const int t0 = (int)((int64_t)ntiles * gw / W);
+    const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
+    const int nrounds = (t1 - t0) * RPT;
 
-    for (int tile = blockIdx.x * nwaves + wave; tile < ntiles; tile += gridDim.x * nwaves) {
-        int row[R];
-        bool rv[R];
+    // Loads are unconditional inside a wave-uniform step test: rows past N and
+    // chunks past the staged range read a clamped, valid address and get a
+    // zero scale and bias, so they add nothing. (Branches around individual
+    // loads would make the compiler wait for every load in flight.)
+    auto issue = [&](Round<R, U>& buf, int rd) {
+        if (rd >= nrounds) return;
+        const int tile = t0 + rd / RPT;
+        const int sg = rd - (rd / RPT) * RPT;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            row[r] = tile * ROWS + r * RPI + seg;
-            rv[r] = row[r] < a.N;
+        for (int u = 0; u < U; ++u) {
+            if (sg * U + u >= S) break;  // uniform
+            const int c = (sg * U + u) * LPR + sl;
+            const int gc = c0 + min(c, nc - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = tile * ROWS + r * RPI + seg;
+                const int rc = min(row, a.N - 1);
+                buf.cw[u][r] = *(const uint4*)(a.wq + (int64_t)rc * wpr + (int64_t)gc * 4);
+                const int64_t gi = (int64_t)rc * G + gc / CPG;
+                buf.sc[u][r] = a.s[gi];
+                buf.bi[u][r] = a.b[gi];
+            }
         }
-        float y[R][B];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int bb = 0; bb < B; ++bb) y[r][bb] = 0.f;
+    };
 
-        for (int s0 = 0; s0 < S; s0 += U) {
-            uint4 cw[U][R];
-            float sc[U][R], bi[U][R];
-            // issue every load of this batch of steps before using any
+    float y[R][B];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = (s0 + u) * LPR + sl;
-                const bool cv = (s0 + u < S) && (c < nc);
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if (cv && rv[r]) {
-                        const int gc = c0 + c;
-                        cw[u][r] = *(const uint4*)(a.wq + (int64_t)row[r] * wpr + (int64_t)gc * 4);
-                        const int64_t gi = (int64_t)row[r] * G + gc / CPG;
-                        sc[u][r] = h2f(a.s[gi]);
-                        bi[u][r] = h2f(a.b[gi]);
-                    } else {
-                        cw[u][r] = make_uint4(0, 0, 0, 0);
-                        sc[u][r] = 0.f;
-                        bi[u][r] = 0.f;
+        for (int bb = 0; bb < B; ++bb) y[r][bb] = 0.f;
+
+    const uint32_t magic = in_vgpr(kMagic16);
+    auto consume = [&](const Round<R, U>& buf, int rd) {
+        if (rd >= nrounds) return;
+        const int tile = t0 + rd / RPT;
+        const int sg = rd - (rd / RPT) * RPT;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sg * U + u >= S) break;  // uniform
+            const int cu = (sg * U + u) * LPR + sl;
+            const int c = min(cu, nc - 1);
+            float sc[R], bi[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const bool ok = (cu < nc) && (tile * ROWS + r * RPI + seg < a.N);
+                sc[r] = ok ? h2f(buf.sc[u][r]) : 0.f;
+                bi[r] = ok ? h2f(buf.bi[u][r]) : 0.f;
+            }
+            chunk_rows<BITS, XF, B, R>(buf.cw[u], sc, bi, lds, a.nb, nc, c, magic, y);
+        }
+        if (sg == RPT - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = tile * ROWS + r * RPI + seg;
+#pragma unroll
+                for (int bb = 0; bb < B; ++bb) {
+                    const float v = seg_sum<LPR>(y[r][bb]);
+                    y[r][bb] = 0.f;
+                    if (sl == 0 && row < a.N && bb < a.nb) {
+                        float* dst = a.y + (int64_t)bb * a.N + row;
+                        if (a.atomic_out)
+                            atomicAdd(dst, v);
+                        else
+                            *dst = v;
                     }
                 }
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = (s0 + u) * LPR + sl;
-                if ((s0 + u < S) && (c < nc))
-                    chunk_rows<BITS, XF, B, R>(cw[u], sc[u], bi[u], lds, a.nb, nc, c, magic, y);
-            }
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int bb = 0; bb < B; ++bb) {
-                const float v = seg_sum<LPR>(y[r][bb]);
-                if (sl == 0 && rv[r] && bb < a.nb) {
-                    float* dst = a.y + (int64_t)bb * a.N + row[r];
-                    if (a.atomic_out)
-                        atomicAdd(dst, v);
-                    else
-                        *dst = v;
-                }
-            }
-        }
+    };
+
+#ifdef QD_GEMV_DOUBLE_BUFFER
+    Round<R, U> A, Bf;
+    issue(A, 0);  // the first weights are in flight while the activations are staged
+    stage_x<BITS, XF>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    __syncthreads();
+    for (int rd = 0; rd < nrounds; rd += 2) {
+        issue(Bf, rd + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(A, rd);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(A, rd + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(Bf, rd + 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+#else
+    // One buffer per wave: a round's loads are all issued before any is used;
+    // other waves on the SIMD keep the memory system busy while this one
+    // computes.
+    Round<R, U> A;
+    issue(A, 0);  // the first weights are in flight while the activations are staged
+    stage_x<BITS, XF>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    __syncthreads();
+    for (int rd = 0; rd < nrounds; ++rd) {
+        if (rd > 0) issue(A, rd);
+        consume(A, rd);
+    }
+#endif
 }
 
 __global__ void fill_zero_kernel(float* p, int64_t n) {
@@ -142,18 +192,19 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int BITS, int XF, int B, int LPR, int R, int U>
-hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE>
+hipError_t run_cfg(const GemvArgs& base, hipStream_t st) {
     using St = Stage<BITS, XF>;
+    constexpr int nwaves = 4;
     const DeviceInfo& dev = device_info();
-    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U>;
+    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE>;
     const int C16 = base.K / St::CC;
     // Split the chunk range when the staged activations exceed the LDS budget
     // per workgroup (half the CU's LDS, so two workgroups stay resident).
     const size_t budget = std::min<size_t>(dev.max_lds_per_block, dev.lds_per_cu / 2);
     int splits = 1;
     while (St::bytes(base.nb, (C16 + splits - 1) / splits) > budget && splits < C16) ++splits;
-    int per = (C16 + splits - 1) / splits;
+    const int per = (C16 + splits - 1) / splits;
     splits = (C16 + per - 1) / per;
     const size_t lds = St::bytes(base.nb, per);
     if (lds > dev.max_lds_per_block) return hipErrorInvalidValue;
@@ -170,11 +221,14 @@ hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     const int ntiles = (a.N + rows_per_tile - 1) / rows_per_tile;
     const int want = (ntiles + nwaves - 1) / nwaves;
     const int occ = occupancy((const void*)kern, threads, lds);
-    int grid = std::min(want, std::max(1, occ) * dev.cus);
-    grid = std::max(grid, 1);
+    const int grid = std::max(1, std::min(want, std::max(1, occ) * dev.cus));
     hipLaunchKernelGGL(kern, dim3(grid, splits), dim3(threads), lds, st, a);
     return hipGetLastError();
 }
+
+struct Cfg {
+    int lpr, r, u, wpe;
+};
 
 // Lanes per row: the largest segment width that wastes the fewest lane
 // slots on the row's chunk count.
@@ -193,33 +247,82 @@ int pick_lpr(int chunks) {
     return best;
 }
 
-template <int BITS, int XF, int B, int R, int U>
-hipError_t run_lpr(const GemvArgs& a, int lpr, hipStream_t st) {
-    switch (lpr) {
-        case 64: return run_cfg<BITS, XF, B, 64, R, U>(a, 4, st);
-        case 32: return run_cfg<BITS, XF, B, 32, R, U>(a, 4, st);
-        case 16: return run_cfg<BITS, XF, B, 16, R, U>(a, 4, st);
-        default: return run_cfg<BITS, XF, B, 8, R, U>(a, 4, st);
+// Measured on MI355X (graph-replayed, weights cycled through HBM): batch 1
+// wants few loads per wave and many waves; R rows per tile is raised only
+// when N leaves enough tiles for every resident wave.
+Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
+    Cfg c;
+    const int chunks = K * bits / 128;
+    c.lpr = pick_lpr(chunks);
+    const int S = (chunks + c.lpr - 1) / c.lpr;
+    c.wpe = 1;
+    (void)xf;
+    if (nb <= 1) {
+        if (S <= 2) {
+            c.r = N >= 16384 ? 4 : 1;
+            c.u = N >= 16384 ? 2 : 4;
+        } else if (S <= 8) {
+            c.r = 2;
+            c.u = 2;
+        } else {
+            c.r = 4;
+            c.u = 1;
+        }
+    } else if (nb <= 4) {
+        c.r = 2;
+        c.u = 2;
+    } else {
+        c.r = 1;
+        c.u = 2;
     }
+    return c;
 }
 
+#define QD_TRY(LPR_, R_, U_, WPE_)                                                        \
+    if (c.lpr == LPR_ && c.r == R_ && c.u == U_ && c.wpe == WPE_)                          \
+        return run_cfg<BITS, XF, B, LPR_, R_, U_, WPE_>(a, st);
+#define QD_LPRS(R_, U_, WPE_) \
+    QD_TRY(64, R_, U_, WPE_) QD_TRY(32, R_, U_, WPE_) QD_TRY(16, R_, U_, WPE_) QD_TRY(8, R_, U_, WPE_)
+
+template <int BITS, int XF, int B>
+hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
+    if constexpr (B == 1) {
+        QD_LPRS(4, 2, 1) QD_LPRS(1, 4, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1)
+#ifdef QD_TUNING
+        if constexpr (BITS == 4 && XF == 0) {
+            QD_LPRS(2, 4, 1) QD_LPRS(8, 1, 1) QD_LPRS(1, 8, 1) QD_LPRS(2, 8, 1) QD_LPRS(8, 2, 1)
+            QD_LPRS(1, 4, 4) QD_LPRS(2, 2, 4) QD_LPRS(2, 4, 4) QD_LPRS(4, 1, 4) QD_LPRS(4, 2, 4)
+            QD_LPRS(8, 1, 4) QD_LPRS(1, 8, 4)
+        }
+#endif
+    } else if constexpr (B == 2 || B == 4) {
+        QD_LPRS(2, 2, 1)
+    } else {
+        QD_LPRS(1, 2, 1)
+    }
+    return hipErrorInvalidConfiguration;
+}
+#undef QD_LPRS
+#undef QD_TRY
+
 template <int BITS, int XF>
-hipError_t run_batch(const GemvArgs& a, int lpr, hipStream_t st) {
-    if (a.nb <= 1) return run_lpr<BITS, XF, 1, 4, 2>(a, lpr, st);
-    if (a.nb <= 2) return run_lpr<BITS, XF, 2, 2, 2>(a, lpr, st);
-    if (a.nb <= 4) return run_lpr<BITS, XF, 4, 2, 2>(a, lpr, st);
-    return run_lpr<BITS, XF, 8, 1, 2>(a, lpr, st);
+hipError_t run_batch(const GemvArgs& a, const Cfg& c, hipStream_t st) {
+    if (a.nb <= 1) return run_b<BITS, XF, 1>(a, c, st);
+    if (a.nb <= 2) return run_b<BITS, XF, 2>(a, c, st);
+    if (a.nb <= 4) return run_b<BITS, XF, 4>(a, c, st);
+    return run_b<BITS, XF, 8>(a, c, st);
 }
 
 }  // namespace
 
+#ifdef QD_TUNING
+// Tuning builds only: force a configuration (all zero = the default policy).
+extern "C" int qd_tune_gemv[4] = {0, 0, 0, 0};
+#endif
+
 hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                        const void* x, int xkind, float* y, int N, int K, int batch,
                        hipStream_t st) {
-    const int chunks = K * bits / 128;
-    const int lpr = pick_lpr(chunks);
-    const int per_word = 32 / bits;
-    (void)per_word;
     for (int b0 = 0; b0 < batch; b0 += 8) {
         GemvArgs a{};
         a.wq = wq;
@@ -232,11 +335,16 @@ hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const ui
         a.N = N;
         a.K = K;
         a.nb = std::min(8, batch - b0);
+        const int xf = xkind == X_F16 ? 0 : 1;
+        Cfg c = default_cfg(bits, xf, a.nb, N, K);
+#ifdef QD_TUNING
+        if (qd_tune_gemv[0]) c = Cfg{qd_tune_gemv[0], qd_tune_gemv[1], qd_tune_gemv[2], qd_tune_gemv[3]};
+#endif
         hipError_t e;
         if (bits == 4)
-            e = xkind == X_F16 ? run_batch<4, 0>(a, lpr, st) : run_batch<4, 1>(a, lpr, st);
+            e = xf == 0 ? run_batch<4, 0>(a, c, st) : run_batch<4, 1>(a, c, st);
         else
-            e = xkind == X_F16 ? run_batch<8, 0>(a, lpr, st) : run_batch<8, 1>(a, lpr, st);
+            e = xf == 0 ? run_batch<8, 0>(a, c, st) : run_batch<8, 1>(a, c, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -39,6 +39,15 @@ struct MoeArgs {
 };
 
 size_t moe_workspace_bytes(const MoeArgs& m, int T, int k);
+size_t moe_decode_workspace_bytes(const MoeArgs& m, int k);
+size_t moe_prefill_workspace_bytes(const MoeArgs& m, int T, int k);
+
+// One token at a time through the GEMV kernels (workspace: decode bytes).
+hipError_t launch_moe_decode(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
+                             const void* x, int xkind, float* y, void* ws, hipStream_t st);
+// Expert-grouped MFMA path for prefill chunks.
+hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
+                              const void* x, int xkind, float* y, void* ws, hipStream_t st);
 
 hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
                               const void* x, int xkind, float* y, void* ws, size_t ws_bytes,

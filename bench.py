@@ -1,0 +1,332 @@
+"""Benchmark of the affine-quantized decode path on one MI355X.
+
+Default workload (the 7B-shaped decode FFN, batch 1): one step is the
+gate+up projection (K=4096 -> N=2*14336) followed by the down projection
+(K=14336 -> N=4096), both int4 codes with fp16 scale and bias per group of
+64, fp16 activations, fp32 outputs. Sixteen distinct weight sets (1.59 GB,
+far above the 256 MB Infinity Cache) are cycled so every step streams its
+weights from HBM. Inputs are seeded synthetic data (``synth``) resident in
+HBM before timing starts. Steps are replayed from a HIP graph; the timed
+region is bracketed by device synchronizations and measured with HIP
+events on the launch stream.
+
+Printed: one JSON line with the achieved HBM bandwidth (algorithmic bytes
+over time), the roofline of the dominant kernel, and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+
+Other workloads (``--config``): c1 (4096x4096 GEMV), c3 (MoE decode layer),
+c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "achieved HBM GB/s (% of peak) for int4 g64 GEMV at batch 1; µs/MoE layer"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--config", default="c2",
+                   choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "stream"])
+    p.add_argument("--sets", type=int, default=0, help="weight sets cycled (0 = workload default)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def matrix_bytes(N: int, K: int, bits: int = 4) -> int:
+    """Algorithmic bytes of one packed matrix: codes + fp16 scale + fp16 bias per group."""
+    return N * K * bits // 8 + 2 * 2 * N * (K // 64)
+
+
+def gemv_bytes(N: int, K: int, batch: int, bits: int = 4) -> int:
+    return matrix_bytes(N, K, bits) + batch * K * 2 + batch * N * 4
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMV_SOURCES = ["affine_quantized_gemv_qgemv_amd/csrc/gemv.hip",
+                "affine_quantized_gemv_qgemv_amd/csrc/common.h"]
+
+
+def stored_traffic(name: str, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash(sources):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Times a list of step callables replayed from HIP graphs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, step_fns, steps: int, warmup: int):
+        torch = self.torch
+        n = len(step_fns)
+        for i in range(warmup):
+            step_fns[i % n]()
+        torch.cuda.synchronize()
+        cyc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cyc):
+            for f in step_fns:
+                f()
+        rem = steps % n
+        remg = None
+        if rem:
+            remg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(remg):
+                for f in step_fns[:rem]:
+                    f()
+        cyc.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(steps // n):
+            cyc.replay()
+        if remg is not None:
+            remg.replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / 1e3, wall
+
+
+def cpu_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_gemv(mats, seconds: float):
+    """The fp64 oracle on the same matrices (one step = every matrix once), repeated
+    until `seconds` of CPU time have passed; returns GB/s on the algorithmic bytes."""
+    import oracle
+    oracle.set_threads(cpu_threads())
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for w, xb in mats:
+            oracle.gemv_f16(w, xb)
+            nbytes += gemv_bytes(w.N, w.K, xb.shape[0], w.bits)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return nbytes / el / 1e9, done, el, oracle.get_threads()
+
+
+# ---------------------------------------------------------------------------
+def to_dev_codes(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
+
+
+def to_dev_half(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.float16)
+
+
+def make_sets(torch, shapes, nsets, cfg_id):
+    import synth
+    sets = []
+    for s in range(nsets):
+        mats = []
+        for j, (K, N) in enumerate(shapes):
+            w = synth.affine_weights(4, N, K, cfg=cfg_id, set_id=s, tensor_base=8 * j)
+            mats.append((to_dev_codes(torch, w.wq), to_dev_half(torch, w.scales),
+                         to_dev_half(torch, w.biases)))
+            if s == 0:
+                mats[-1] = mats[-1] + (w,)
+        sets.append(mats)
+    return sets
+
+
+def run_dense(args, torch, qd, shapes, batch, nsets, cfg_id):
+    import synth
+    sets = make_sets(torch, shapes, nsets, cfg_id)
+    xs, ys, xbits = [], [], []
+    for j, (K, N) in enumerate(shapes):
+        xb = synth.x_f16(batch, K, cfg=cfg_id, set_id=1000 + j)
+        xbits.append(xb)
+        xs.append(to_dev_half(torch, xb))
+        ys.append(torch.empty((batch, N), dtype=torch.float32, device="cuda"))
+
+    def step_fn(s, only=None):
+        def f():
+            for j in range(len(shapes)):
+                if only is not None and j != only:
+                    continue
+                wq, sc, bi = sets[s][j][:3]
+                qd.qgemv_affine4(wq, sc, bi, xs[j], out=ys[j])
+        return f
+
+    timer = Timer(torch)
+    steps = args.steps
+    secs, wall = timer.run([step_fn(s) for s in range(nsets)], steps, args.warmup)
+    step_bytes = sum(gemv_bytes(N, K, batch) for K, N in shapes)
+    per_shape = []
+    for j, (K, N) in enumerate(shapes):
+        sj, _ = timer.run([step_fn(s, j) for s in range(nsets)], max(nsets, steps // 2),
+                          min(args.warmup, nsets))
+        n = max(nsets, steps // 2)
+        per_shape.append(dict(K=K, N=N, us=sj / n * 1e6,
+                              gbs=gemv_bytes(N, K, batch) * n / sj / 1e9))
+    return dict(secs=secs, wall=wall, step_bytes=step_bytes, per_shape=per_shape,
+                launches_per_step=len(shapes), cpu_mats=[(sets[0][j][3], xbits[j]) for j in range(len(shapes))])
+
+
+def bench_stream(args, torch):
+    """Plain device copy (torch's copy kernel) and a read-mostly reduction over
+    2 GiB buffers: the practical HBM ceiling, and the known-size reference used
+    to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 29  # fp32 elements = 2 GiB
+    src = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    reps = max(4, min(args.steps, 50))
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    for _ in range(3):
+        torch.sum(src, 0, out=acc)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.sum(src, 0, out=acc)
+    e1.record()
+    torch.cuda.synchronize()
+    red_s = e0.elapsed_time(e1) / 1e3 / reps
+    nbytes = n * 4
+    return {"config": "stream", "bytes_per_buffer": nbytes, "reps": reps,
+            "copy_GBps_read_plus_write": round(2 * nbytes / copy_s / 1e9, 1),
+            "copy_us": round(copy_s * 1e6, 2),
+            "reduce_GBps_read": round(nbytes / red_s / 1e9, 1),
+            "reduce_us": round(red_s * 1e6, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    import affine_quantized_gemv_qgemv_amd as qd
+    qd.lib()  # fail loudly if the HIP library is missing
+
+    if args.config == "stream":
+        print(json.dumps(bench_stream(args, torch)), flush=True)
+        return
+    if args.config in ("c1", "c2", "c5"):
+        if args.config == "c1":
+            shapes, batches, nsets, cfg_id = [(4096, 4096)], [1], 64, 1
+            wl = "c1: dense int4 g64 GEMV, batch 1, K=4096 -> N=4096; 64 weight sets cycled (604 MB)"
+        elif args.config == "c2":
+            shapes, batches, nsets, cfg_id = [(4096, 28672), (14336, 4096)], [1], 16, 2
+            wl = ("c2: 7B-shaped decode FFN, batch 1: gate+up K=4096 -> N=2x14336 then down "
+                  "K=14336 -> N=4096, int4 g64; 16 weight sets cycled (1.59 GB)")
+        else:
+            shapes, batches, nsets, cfg_id = [(8192, 28672), (28672, 8192)], [1, 2, 4, 8], 80, 5
+            wl = ("c5: 70B-shaped decode, K=8192 -> N=28672 and K=28672 -> N=8192, int4 g64, "
+                  "80 weight-set pairs cycled (21.1 GB)")
+        if args.sets:
+            nsets = args.sets
+        results = []
+        for batch in batches:
+            r = run_dense(args, torch, qd, shapes, batch, nsets, cfg_id)
+            results.append((batch, r))
+        batch, r = results[0]
+        secs = r["secs"]
+        gbs = r["step_bytes"] * args.steps / secs / 1e9
+        launch_s = secs / (args.steps * r["launches_per_step"])
+        bytes_per_launch = r["step_bytes"] / r["launches_per_step"]
+        achieved = bytes_per_launch / launch_s / 1e9
+        traffic = stored_traffic(f"qgemv_affine4_{args.config}_traffic.json", GEMV_SOURCES)
+        out = {
+            "metric": METRIC,
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(secs / args.steps * 1e3, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": wl, "batch": batch, "weight_sets": nsets,
+                       "step_bytes": r["step_bytes"],
+                       "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                       "per_shape": [{k: (round(v, 3) if isinstance(v, float) else v)
+                                      for k, v in d.items()} for d in r["per_shape"]]},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "kernel": "qd::qgemv_kernel<4,0,1,64,4,2>",
+                         "bytes_per_launch": bytes_per_launch,
+                         "avg_launch_us": round(launch_s * 1e6, 3)},
+        }
+        if len(results) > 1:
+            out["config"]["batch_sweep"] = [
+                {"batch": b, "GBps": round(rr["step_bytes"] * args.steps / rr["secs"] / 1e9, 1),
+                 "us_per_step": round(rr["secs"] / args.steps * 1e6, 2)} for b, rr in results]
+        if not args.no_cpu:
+            v, done, el, thr = cpu_baseline_gemv(r["cpu_mats"], args.cpu_seconds)
+            out["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": thr,
+                                   "kind": "oracle",
+                                   "sample": f"{done} full step(s) of weight set 0 "
+                                             f"({', '.join(f'{K}->{N}' for K, N in shapes)}, batch {batch}) "
+                                             f"in {el:.1f} s, fp64 C oracle"}
+        else:
+            out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return
+    raise SystemExit(f"config {args.config} is not wired into bench.py yet")
+
+
+if __name__ == "__main__":
+    main()
