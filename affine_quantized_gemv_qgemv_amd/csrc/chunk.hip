@@ -23,36 +23,13 @@
 // identically on both operands (step st, half h takes word 4h + st).
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace qd {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
 constexpr int CH_NT = 64;    // output columns per workgroup
 constexpr int CH_MT = 128;   // rows per workgroup (the whole chunk)
-constexpr int XS_STRIDE = 9; // uint4 per staged X row: 8 of data + 1 of padding, so the
-                             // 32 rows an MFMA operand read touches fall in distinct banks
 
-// 8 codes of one word -> bf16 (128 + q) in natural k order.
-__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t w) {
-    const uint32_t t = w & 0x0F0F0F0Fu;         // q0 q2 q4 q6 in bytes 0..3
-    const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;  // q1 q3 q5 q7
-    // v_perm_b32(u, t, sel): selector bytes 0..3 pick t's bytes, 4..7 u's, 0x0C gives 0
-    const uint32_t p01 = __builtin_amdgcn_perm(u, t, 0x0C040C00u) | 0x43004300u;
-    const uint32_t p23 = __builtin_amdgcn_perm(u, t, 0x0C050C01u) | 0x43004300u;
-    const uint32_t p45 = __builtin_amdgcn_perm(u, t, 0x0C060C02u) | 0x43004300u;
-    const uint32_t p67 = __builtin_amdgcn_perm(u, t, 0x0C070C03u) | 0x43004300u;
-    uint4 v = make_uint4(p01, p23, p45, p67);
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
-__device__ __forceinline__ float bf16_pair_sum(uint32_t v, float acc) {
-    // v_dot2_f32_bf16 with (1, 1): adds both bf16 halves into an fp32 sum
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), ones, acc, false);
-}
 
 struct ChunkArgs {
     const uint32_t* wq;
@@ -200,19 +177,6 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
     const int grid = (N + CH_NT - 1) / CH_NT;
     hipLaunchKernelGGL(chunk_gemm_kernel, dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// MoE prefill (placeholder: one token at a time through the decode kernels).
-// ---------------------------------------------------------------------------
-size_t moe_prefill_workspace_bytes(const MoeArgs& m, int T, int k) {
-    (void)T;
-    return moe_decode_workspace_bytes(m, k);
-}
-
-hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
-                              const void* x, int xkind, float* y, void* ws, hipStream_t st) {
-    return launch_moe_decode(m, idx, w, T, k, x, xkind, y, ws, st);
 }
 
 }  // namespace qd
