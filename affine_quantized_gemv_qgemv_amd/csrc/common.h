@@ -126,9 +126,19 @@ struct Stage {
     __host__ __device__ static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
 };
 
+// Slot of chunk c when each lane reads CPL consecutive chunks: chunk c goes
+// to (c mod CPL) * (nc / CPL) + c / CPL, so the lanes of a segment read
+// consecutive 16-byte slots for each of their CPL chunks (nc is a multiple
+// of CPL).
+template <int CPL>
+__device__ __forceinline__ int xslot(int c, int nc) {
+    if constexpr (CPL == 1) return c;
+    return (c % CPL) * (nc / CPL) + c / CPL;
+}
+
 // Stage chunks [c0, c0 + nc) of activation vector(s) x[b][K] for b < nb into
 // lds. xstride = elements between consecutive vectors.
-template <int BITS, int XF>
+template <int BITS, int XF, int CPL = 1>
 __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0, int nc,
                         uint4* lds) {
     using St = Stage<BITS, XF>;
@@ -136,8 +146,9 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
     constexpr int QPC = St::QPC;
     uint4* xs = lds;
     for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
-        const int b = item / nc, c = item - b * nc;
-        const int64_t base = (int64_t)b * xstride + (int64_t)(c0 + c) * CC;
+        const int b = item / nc, cc = item - b * nc;
+        const int c = xslot<CPL>(cc, nc);   // destination slot of chunk cc
+        const int64_t base = (int64_t)b * xstride + (int64_t)(c0 + cc) * CC;
         if constexpr (XF == 0) {
             // fp16 activations, kept as raw bits
             const uint16_t* xp = (const uint16_t*)x + base;
@@ -216,14 +227,17 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
     }
 }
 
-// Partial dot products of one 16-byte code chunk of each of R rows with every
-// activation vector b < B, followed by the affine epilogue into y[r][b]:
+// Partial dot products of NCH consecutive 16-byte code chunks (one lane's
+// share of a group) of each of R rows with every activation vector b < B,
+// followed by one affine epilogue into y[r][b]:
 //   y[r][b] += s_r * (sum_k q_k x_k) + bias_r * (sum_k x_k).
-// The chunk's activations are read from LDS once and shared by the R rows.
-template <int BITS, int XF, int B, int R>
-__device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&sc)[R],
+// The chunks' activations are read from LDS once and shared by the R rows;
+// slot[i] is the staged slot of chunk i.
+template <int BITS, int XF, int B, int R, int NCH>
+__device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const float (&sc)[R],
                                            const float (&bi)[R], const uint4* lds, int nb_staged,
-                                           int nc, int c, uint32_t magic, float (&y)[R][B]) {
+                                           int nc, const int (&slot)[NCH], uint32_t magic,
+                                           float (&y)[R][B]) {
     using St = Stage<BITS, XF>;
     constexpr int QPC = St::QPC;
     const uint4* xs = lds;
@@ -234,62 +248,74 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&s
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) a1[r][b] = a16[r][b] = 0.f;
-        if constexpr (BITS == 4) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint4 xq[B];
+        for (int ch = 0; ch < NCH; ++ch) {
+            const int c = slot[ch];
+            if constexpr (BITS == 4) {
 #pragma unroll
-                for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+                for (int q = 0; q < 4; ++q) {
+                    uint4 xq[B];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
-                    const uint32_t p04 = (w & 0x000F000Fu) | magic;   // 1024+q0, 1024+q4
-                    const uint32_t p15 = (w & 0x00F000F0u) | magic;   // 1024+16q1, 1024+16q5
-                    const uint32_t w8 = w >> 8;
-                    const uint32_t p26 = (w8 & 0x000F000Fu) | magic;  // 1024+q2, 1024+q6
-                    const uint32_t p37 = (w8 & 0x00F000F0u) | magic;  // 1024+16q3, 1024+16q7
+                    for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
 #pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        a1[r][b] = dot2(p04, xq[b].x, a1[r][b]);
-                        a16[r][b] = dot2(p15, xq[b].y, a16[r][b]);
-                        a1[r][b] = dot2(p26, xq[b].z, a1[r][b]);
-                        a16[r][b] = dot2(p37, xq[b].w, a16[r][b]);
+                    for (int r = 0; r < R; ++r) {
+                        const uint4& w4 = cw[ch][r];
+                        const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
+                        const uint32_t p04 = (w & 0x000F000Fu) | magic;   // 1024+q0, 1024+q4
+                        const uint32_t p15 = (w & 0x00F000F0u) | magic;   // 1024+16q1, 1024+16q5
+                        const uint32_t w8 = w >> 8;
+                        const uint32_t p26 = (w8 & 0x000F000Fu) | magic;  // 1024+q2, 1024+q6
+                        const uint32_t p37 = (w8 & 0x00F000F0u) | magic;  // 1024+16q3, 1024+16q7
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            a1[r][b] = dot2(p04, xq[b].x, a1[r][b]);
+                            a16[r][b] = dot2(p15, xq[b].y, a16[r][b]);
+                            a1[r][b] = dot2(p26, xq[b].z, a1[r][b]);
+                            a16[r][b] = dot2(p37, xq[b].w, a16[r][b]);
+                        }
                     }
                 }
-            }
-        } else {
+            } else {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                uint4 xq[B];
+                for (int q = 0; q < 2; ++q) {
+                    uint4 xq[B];
 #pragma unroll
-                for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+                    for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t w0 = q == 0 ? cw[r].x : cw[r].z;
-                    const uint32_t w1 = q == 0 ? cw[r].y : cw[r].w;
-                    const uint32_t p02 = (w0 & 0x00FF00FFu) | magic;          // 1024+q0, 1024+q2
-                    const uint32_t p13 = ((w0 >> 8) & 0x00FF00FFu) | magic;   // 1024+q1, 1024+q3
-                    const uint32_t r02 = (w1 & 0x00FF00FFu) | magic;
-                    const uint32_t r13 = ((w1 >> 8) & 0x00FF00FFu) | magic;
+                    for (int r = 0; r < R; ++r) {
+                        const uint4& w4 = cw[ch][r];
+                        const uint32_t w0 = q == 0 ? w4.x : w4.z;
+                        const uint32_t w1 = q == 0 ? w4.y : w4.w;
+                        const uint32_t p02 = (w0 & 0x00FF00FFu) | magic;          // 1024+q0, 1024+q2
+                        const uint32_t p13 = ((w0 >> 8) & 0x00FF00FFu) | magic;   // 1024+q1, 1024+q3
+                        const uint32_t r02 = (w1 & 0x00FF00FFu) | magic;
+                        const uint32_t r13 = ((w1 >> 8) & 0x00FF00FFu) | magic;
 #pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        a1[r][b] = dot2(p02, xq[b].x, a1[r][b]);
-                        a16[r][b] = dot2(p13, xq[b].y, a16[r][b]);
-                        a1[r][b] = dot2(r02, xq[b].z, a1[r][b]);
-                        a16[r][b] = dot2(r13, xq[b].w, a16[r][b]);
+                        for (int b = 0; b < B; ++b) {
+                            a1[r][b] = dot2(p02, xq[b].x, a1[r][b]);
+                            a16[r][b] = dot2(p13, xq[b].y, a16[r][b]);
+                            a1[r][b] = dot2(r02, xq[b].z, a1[r][b]);
+                            a16[r][b] = dot2(r13, xq[b].w, a16[r][b]);
+                        }
                     }
                 }
             }
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const float2 k = cs[b * nc + c];
+            float kx = 0.f, ky = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                const float2 k = cs[b * nc + slot[ch]];
+                kx += k.x;
+                ky += k.y;
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float p =
-                    (BITS == 4 ? fmaf(a16[r][b], 0.0625f, a1[r][b]) : a1[r][b] + a16[r][b]) - k.x;
+                    (BITS == 4 ? fmaf(a16[r][b], 0.0625f, a1[r][b]) : a1[r][b] + a16[r][b]) - kx;
                 y[r][b] = fmaf(sc[r], p, y[r][b]);
-                y[r][b] = fmaf(bi[r], k.y, y[r][b]);
+                y[r][b] = fmaf(bi[r], ky, y[r][b]);
             }
         }
     } else {
@@ -300,30 +326,38 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&s
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int ch = 0; ch < NCH; ++ch) {
+            const int c = slot[ch];
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if constexpr (BITS == 4) {
-                    const uint4 xa = xs[(b * QPC + 2 * q) * nc + c];
-                    const uint4 xb = xs[(b * QPC + 2 * q + 1) * nc + c];
+            for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
-                        acc[r][b] = word_i4_f32(w, *(const float4*)&xa, *(const float4*)&xb, acc[r][b]);
-                    }
-                } else {
-                    const uint4 xa = xs[(b * QPC + q) * nc + c];
+                for (int b = 0; b < B; ++b) {
+                    if constexpr (BITS == 4) {
+                        const uint4 xa = xs[(b * QPC + 2 * q) * nc + c];
+                        const uint4 xb = xs[(b * QPC + 2 * q + 1) * nc + c];
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint32_t w = q == 0 ? cw[r].x : q == 1 ? cw[r].y : q == 2 ? cw[r].z : cw[r].w;
-                        acc[r][b] = word_i8_f32(w, *(const float4*)&xa, acc[r][b]);
+                        for (int r = 0; r < R; ++r) {
+                            const uint4& w4 = cw[ch][r];
+                            const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
+                            acc[r][b] = word_i4_f32(w, *(const float4*)&xa, *(const float4*)&xb, acc[r][b]);
+                        }
+                    } else {
+                        const uint4 xa = xs[(b * QPC + q) * nc + c];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            const uint4& w4 = cw[ch][r];
+                            const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
+                            acc[r][b] = word_i8_f32(w, *(const float4*)&xa, acc[r][b]);
+                        }
                     }
                 }
             }
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const float xsum = cs[b * nc + c];
+            float xsum = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) xsum += cs[b * nc + slot[ch]];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 y[r][b] = fmaf(sc[r], acc[r][b], y[r][b]);
@@ -331,6 +365,18 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&s
             }
         }
     }
+}
+
+// One chunk per row (the gathered MoE kernels).
+template <int BITS, int XF, int B, int R>
+__device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&sc)[R],
+                                           const float (&bi)[R], const uint4* lds, int nb_staged,
+                                           int nc, int c, uint32_t magic, float (&y)[R][B]) {
+    uint4 cw1[1][R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) cw1[0][r] = cw[r];
+    const int slot[1] = {c};
+    group_rows<BITS, XF, B, R, 1>(cw1, sc, bi, lds, nb_staged, nc, slot, magic, y);
 }
 
 }  // namespace qd

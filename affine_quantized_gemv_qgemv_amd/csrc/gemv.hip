@@ -38,15 +38,16 @@ struct GemvArgs {
     int atomic_out;
 };
 
-// One round of loads: U steps (16-byte chunks per lane) of R rows.
-template <int R, int U>
+// One round of loads: U steps of R rows; a step gives each lane CPL
+// consecutive 16-byte chunks of one group.
+template <int R, int U, int CPL>
 struct Round {
-    uint4 cw[U][R];
+    uint4 cw[U][CPL][R];
     uint16_t sc[U][R], bi[U][R];   // raw fp16 bits; masked when consumed
 };
 
-template <int BITS, int XF, int B, int LPR, int R, int U, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
     GemvArgs a) {
     extern __shared__ uint4 lds[];
     constexpr int CC = 128 / BITS;     // codes per 16-byte chunk
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // wave-uniform: keeps the tile bounds and loop control in scalar registers
     const int gw = blockIdx.x * nwaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = gridDim.x * nwaves;
-    const int S = (nc + LPR - 1) / LPR;            // steps per row
+    const int S = (nc + LPR * CPL - 1) / (LPR * CPL);  // steps per row
     const int RPT = (S + U - 1) / U;               // rounds per tile
     const int ntiles = (a.N + ROWS - 1) / ROWS;
     // contiguous, balanced share of tiles for this wave
@@ -77,20 +78,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // chunks past the staged range read a clamped, valid address and get a
     // zero scale and bias, so they add nothing. (Branches around individual
     // loads would make the compiler wait for every load in flight.)
-    auto issue = [&](Round<R, U>& buf, int rd) {
+    auto issue = [&](Round<R, U, CPL>& buf, int rd) {
         if (rd >= nrounds) return;
         const int tile = t0 + rd / RPT;
         const int sg = rd - (rd / RPT) * RPT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
-            const int c = (sg * U + u) * LPR + sl;
-            const int gc = c0 + min(c, nc - 1);
+            const int c = ((sg * U + u) * LPR + sl) * CPL;
+            const int gc = c0 + min(c, nc - CPL);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int row = tile * ROWS + r * RPI + seg;
                 const int rc = min(row, a.N - 1);
-                buf.cw[u][r] = *(const uint4*)(a.wq + (int64_t)rc * wpr + (int64_t)gc * 4);
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch)
+                    buf.cw[u][ch][r] =
+                        *(const uint4*)(a.wq + (int64_t)rc * wpr + (int64_t)(gc + ch) * 4);
                 const int64_t gi = (int64_t)rc * G + gc / CPG;
                 buf.sc[u][r] = a.s[gi];
                 buf.bi[u][r] = a.b[gi];
@@ -105,15 +109,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         for (int bb = 0; bb < B; ++bb) y[r][bb] = 0.f;
 
     const uint32_t magic = in_vgpr(kMagic16);
-    auto consume = [&](const Round<R, U>& buf, int rd) {
+    auto consume = [&](const Round<R, U, CPL>& buf, int rd) {
         if (rd >= nrounds) return;
         const int tile = t0 + rd / RPT;
         const int sg = rd - (rd / RPT) * RPT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
-            const int cu = (sg * U + u) * LPR + sl;
-            const int c = min(cu, nc - 1);
+            const int cu = ((sg * U + u) * LPR + sl) * CPL;
+            const int c = min(cu, nc - CPL);
             float sc[R], bi[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -121,7 +125,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                 sc[r] = ok ? h2f(buf.sc[u][r]) : 0.f;
                 bi[r] = ok ? h2f(buf.bi[u][r]) : 0.f;
             }
-            chunk_rows<BITS, XF, B, R>(buf.cw[u], sc, bi, lds, a.nb, nc, c, magic, y);
+            int slot[CPL];
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, nc);
+            group_rows<BITS, XF, B, R, CPL>(buf.cw[u], sc, bi, lds, a.nb, nc, slot, magic, y);
         }
         if (sg == RPT - 1) {
 #pragma unroll
@@ -144,9 +151,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     };
 
 #ifdef QD_GEMV_DOUBLE_BUFFER
-    Round<R, U> A, Bf;
+    Round<R, U, CPL> A, Bf;
     issue(A, 0);  // the first weights are in flight while the activations are staged
-    stage_x<BITS, XF>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; rd += 2) {
         issue(Bf, rd + 1);
@@ -162,9 +169,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // One buffer per wave: a round's loads are all issued before any is used;
     // other waves on the SIMD keep the memory system busy while this one
     // computes.
-    Round<R, U> A;
+    Round<R, U, CPL> A;
     issue(A, 0);  // the first weights are in flight while the activations are staged
-    stage_x<BITS, XF>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; ++rd) {
         if (rd > 0) issue(A, rd);
@@ -192,19 +199,21 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int BITS, int XF, int B, int LPR, int R, int U, int WPE>
-hipError_t run_cfg(const GemvArgs& base, hipStream_t st) {
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL>
+hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     using St = Stage<BITS, XF>;
-    constexpr int nwaves = 4;
     const DeviceInfo& dev = device_info();
-    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE>;
+    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL>;
     const int C16 = base.K / St::CC;
     // Split the chunk range when the staged activations exceed the LDS budget
     // per workgroup (half the CU's LDS, so two workgroups stay resident).
     const size_t budget = std::min<size_t>(dev.max_lds_per_block, dev.lds_per_cu / 2);
     int splits = 1;
-    while (St::bytes(base.nb, (C16 + splits - 1) / splits) > budget && splits < C16) ++splits;
-    const int per = (C16 + splits - 1) / splits;
+    // chunks per split: a multiple of 4 so a lane's CPL chunks never straddle
+    // a split
+    auto per_of = [&](int sp) { return (((C16 + sp - 1) / sp) + 3) & ~3; };
+    while (St::bytes(base.nb, per_of(splits)) > budget && splits < C16) ++splits;
+    const int per = std::min(per_of(splits), C16);
     splits = (C16 + per - 1) / per;
     const size_t lds = St::bytes(base.nb, per);
     if (lds > dev.max_lds_per_block) return hipErrorInvalidValue;
@@ -227,7 +236,7 @@ hipError_t run_cfg(const GemvArgs& base, hipStream_t st) {
 }
 
 struct Cfg {
-    int lpr, r, u, wpe;
+    int lpr, r, u, wpe, cpl, nw;
 };
 
 // Lanes per row: the largest segment width that wastes the fewest lane
@@ -247,50 +256,88 @@ int pick_lpr(int chunks) {
     return best;
 }
 
-// Measured on MI355X (graph-replayed, weights cycled through HBM): batch 1
-// wants few loads per wave and many waves; R rows per tile is raised only
-// when N leaves enough tiles for every resident wave.
+// Launch policy, from on-device sweeps (graph-replayed, weights cycled through
+// HBM). Batch 1 wants every resident wave busy with one or two rounds of
+// loads; a lane takes a whole group (two 16-byte chunks, CPL = 2) when the row
+// splits evenly, which halves the scale/bias loads and epilogues; larger
+// workgroups stage x fewer times but must still cover every CU.
+int pow2_floor(int v) {
+    int p = 1;
+    while (p * 2 <= v) p *= 2;
+    return p;
+}
+
 Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
     Cfg c;
     const int chunks = K * bits / 128;
     c.lpr = pick_lpr(chunks);
-    const int S = (chunks + c.lpr - 1) / c.lpr;
     c.wpe = 1;
+    c.cpl = 1;
+    c.nw = 4;
     (void)xf;
-    if (nb <= 1) {
-        if (S <= 2) {
-            c.r = N >= 16384 ? 4 : 1;
-            c.u = N >= 16384 ? 2 : 4;
-        } else if (S <= 8) {
-            c.r = 2;
-            c.u = 2;
-        } else {
-            c.r = 4;
-            c.u = 1;
-        }
-    } else if (nb <= 4) {
-        c.r = 2;
+    if (nb > 1) {
+        c.r = nb <= 4 ? 2 : 1;
         c.u = 2;
-    } else {
-        c.r = 1;
-        c.u = 2;
+        return c;
     }
+    const bool even = chunks % 128 == 0;   // LPR 64 x CPL 2 covers whole steps
+    const int S1 = (chunks + c.lpr - 1) / c.lpr;
+    if ((int64_t)N * S1 / (64 / c.lpr) < 4096) {
+        // latency regime: one row segment per wave, all steps in one round
+        const int s64 = (chunks + 63) / 64;
+        if (c.lpr != 64 && (double)chunks / (s64 * 64) > 0.85) c.lpr = 64;
+        c.cpl = (c.lpr == 64 && even) ? 2 : 1;
+        const int S = (chunks + c.lpr * c.cpl - 1) / (c.lpr * c.cpl);
+        c.r = 1;
+        c.u = S <= 4 ? 4 : 8;
+        const int tiles = N / (64 / c.lpr);
+        c.nw = std::max(1, std::min(16, pow2_floor(std::max(1, tiles / 256))));
+        return c;
+    }
+    if (N >= 16384 && even) {
+        // many rows: two rows per tile, whole groups per lane
+        c.lpr = 64;
+        c.cpl = 2;
+        const int S = chunks / 128;
+        c.r = 2;
+        c.u = S >= 2 ? 2 : 1;
+        c.nw = 8;
+        return c;
+    }
+    if (S1 <= 8 || !even) {
+        // few rows: one row per tile, up to four steps per round
+        if (even && c.lpr == 64) c.cpl = 2;
+        c.r = 1;
+        c.u = 4;
+        c.nw = 16;
+        return c;
+    }
+    c.lpr = 64;
+    c.cpl = 2;
+    c.r = 2;
+    c.u = 1;
+    c.nw = 8;
     return c;
 }
 
-#define QD_TRY(LPR_, R_, U_, WPE_)                                                        \
-    if (c.lpr == LPR_ && c.r == R_ && c.u == U_ && c.wpe == WPE_)                          \
-        return run_cfg<BITS, XF, B, LPR_, R_, U_, WPE_>(a, st);
-#define QD_LPRS(R_, U_, WPE_) \
-    QD_TRY(64, R_, U_, WPE_) QD_TRY(32, R_, U_, WPE_) QD_TRY(16, R_, U_, WPE_) QD_TRY(8, R_, U_, WPE_)
+#define QD_TRY(LPR_, R_, U_, WPE_, CPL_)                                                  \
+    if (c.lpr == LPR_ && c.r == R_ && c.u == U_ && c.wpe == WPE_ && c.cpl == CPL_)         \
+        return run_cfg<BITS, XF, B, LPR_, R_, U_, WPE_, CPL_>(a, c.nw, st);
+#define QD_LPRS(R_, U_, WPE_)                                                    \
+    QD_TRY(64, R_, U_, WPE_, 1) QD_TRY(32, R_, U_, WPE_, 1) QD_TRY(16, R_, U_, WPE_, 1) \
+    QD_TRY(8, R_, U_, WPE_, 1)
+#define QD_LPRS2(R_, U_, WPE_) QD_TRY(64, R_, U_, WPE_, 2) QD_TRY(32, R_, U_, WPE_, 2)
 
 template <int BITS, int XF, int B>
 hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     if constexpr (B == 1) {
-        QD_LPRS(4, 2, 1) QD_LPRS(1, 4, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1)
+        QD_LPRS(1, 4, 1) QD_LPRS(1, 8, 1)
+        QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(1, 4, 1) QD_LPRS2(1, 8, 1)
 #ifdef QD_TUNING
         if constexpr (BITS == 4 && XF == 0) {
-            QD_LPRS(2, 4, 1) QD_LPRS(8, 1, 1) QD_LPRS(1, 8, 1) QD_LPRS(2, 8, 1) QD_LPRS(8, 2, 1)
+            QD_LPRS(4, 2, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1)
+            QD_LPRS2(4, 1, 1) QD_LPRS2(1, 2, 1) QD_LPRS2(4, 2, 1) QD_LPRS2(2, 4, 1) QD_LPRS2(8, 1, 1)
+            QD_LPRS(2, 4, 1) QD_LPRS(8, 1, 1) QD_LPRS(2, 8, 1) QD_LPRS(8, 2, 1)
             QD_LPRS(1, 4, 4) QD_LPRS(2, 2, 4) QD_LPRS(2, 4, 4) QD_LPRS(4, 1, 4) QD_LPRS(4, 2, 4)
             QD_LPRS(8, 1, 4) QD_LPRS(1, 8, 4)
         }
@@ -302,6 +349,7 @@ hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     }
     return hipErrorInvalidConfiguration;
 }
+#undef QD_LPRS2
 #undef QD_LPRS
 #undef QD_TRY
 
@@ -317,7 +365,7 @@ hipError_t run_batch(const GemvArgs& a, const Cfg& c, hipStream_t st) {
 
 #ifdef QD_TUNING
 // Tuning builds only: force a configuration (all zero = the default policy).
-extern "C" int qd_tune_gemv[4] = {0, 0, 0, 0};
+extern "C" int qd_tune_gemv[6] = {0, 0, 0, 0, 1, 4};
 #endif
 
 hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
@@ -338,7 +386,9 @@ hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const ui
         const int xf = xkind == X_F16 ? 0 : 1;
         Cfg c = default_cfg(bits, xf, a.nb, N, K);
 #ifdef QD_TUNING
-        if (qd_tune_gemv[0]) c = Cfg{qd_tune_gemv[0], qd_tune_gemv[1], qd_tune_gemv[2], qd_tune_gemv[3]};
+        if (qd_tune_gemv[0])
+            c = Cfg{qd_tune_gemv[0], qd_tune_gemv[1], qd_tune_gemv[2], qd_tune_gemv[3],
+                    qd_tune_gemv[4], qd_tune_gemv[5]};
 #endif
         hipError_t e;
         if (bits == 4)

@@ -312,13 +312,15 @@ hipError_t launch_gateup(const MoeAArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_down(const MoeBArgs& a, hipStream_t st) {
-    constexpr int LPR = 64, R = 1, U = 4;
+    constexpr int LPR = 64, R = 4, U = 4;
     const int C = a.k * (a.I / 32) + a.Is / 32;
     const size_t lds = ((Stage<4, 1>::bytes(1, C) + 15) & ~(size_t)15) + (size_t)C * sizeof(SegInfo);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     const int ntiles = (a.H + (64 / LPR) * R - 1) / ((64 / LPR) * R);
     auto kern = moe_down_kernel<LPR, R, U>;
-    const int grid = grid_for(kern, 256, lds, ntiles);
+    // every workgroup stages all k*I + Is activations, so keep one per CU; a
+    // wave's four rows x four steps are one round of 16 loads
+    const int grid = std::min(grid_for(kern, 256, lds, ntiles), device_info().cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }

@@ -8,7 +8,7 @@
 // weight one, GELU gate, fp32 intermediates.
 //
 // Four launches:
-//   1. prep: a stable counting sort of the T*k (token, slot) pairs by expert
+//   1. prep: a counting sort of the T*k (token, slot) pairs by expert
 //      (offsets, sorted pair list, each pair's position; pairs with an expert
 //      id outside [0, E) are dropped), and the per-group row sums of x;
 //   2. gate+up: one workgroup per (expert, 64 columns of I) computes gate and
@@ -33,7 +33,7 @@ namespace qd {
 typedef _Float16 halfx8_t __attribute__((ext_vector_type(8)));
 
 struct PrefillWs {
-    int* sorted_pair;   // [T*k] pair ids (t*k + j) ordered by expert, then pair id
+    int* sorted_pair;   // [T*k] pair ids (t*k + j) grouped by expert
     int* pos;           // [T*k] sorted position of each pair, -1 if dropped
     int* offs;          // [E+1] first sorted position of each expert
     float* xsum;        // [T][H/64] row sums of x per group
@@ -113,23 +113,38 @@ __global__ __launch_bounds__(1024) void moe_prep_kernel(const int32_t* __restric
     }
     __syncthreads();
     for (int e = tid; e <= E; e += bs) w.offs[e] = cnt[e];
+    __syncthreads();  // offsets are read before the counters advance
+    // placement: a slot inside the expert's range from an LDS counter. The
+    // order inside an expert's rows does not change any result (every output
+    // row is its own dot-product chain), only which row a pair occupies.
     for (int p = tid; p < P; p += bs) {
         const int e = sidx[p];
         if (e >= 0 && e < E) {
-            int rank = 0;
-            for (int q = 0; q < p; ++q) rank += sidx[q] == e;
-            const int ps = cnt[e] + rank;
+            const int ps = atomicAdd(&cnt[e], 1);
             w.pos[p] = ps;
             w.sorted_pair[ps] = p;
         } else {
             w.pos[p] = -1;
         }
     }
+    // per-group row sums of x: one (token, group) per thread, 8 x 16-byte loads
     const int G = H / 64;
     for (int item = tid; item < T * G; item += bs) {
         const int t = item / G, g = item - t * G;
+        const uint4* src = (const uint4*)((const uint16_t*)x + (int64_t)t * H + g * 64);
         float s = 0.f;
-        for (int i = 0; i < 64; ++i) s += load_x(x, xkind, (int64_t)t * H + g * 64 + i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 v = src[i];
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (xkind == X_F16)
+                    s += h2f(wv[j] & 0xFFFF) + h2f(wv[j] >> 16);
+                else
+                    s += bf2f(wv[j] & 0xFFFF) + bf2f(wv[j] >> 16);
+            }
+        }
         w.xsum[item] = s;
     }
 }

@@ -7,84 +7,92 @@
 // reproducible bit for bit; the weights are exp(l_j - l_max) over the sum of
 // the k kept terms, which equals softmax-then-renormalize.
 //
-// One wave per token: each lane holds E/64 logits; k rounds of a wave-wide
-// arg-max (value, then lowest index) pick the experts in order.
+// One wave per token. The logits go to LDS as order-preserving integer keys
+// (-0.0 folded into +0.0, so they tie as in the real numbers); every lane
+// then ranks its candidates against all E keys, ties going to the lower
+// index. (key, index) is a strict total order, so the ranks are a
+// permutation and the k lanes holding ranks 0..k-1 write the k slots.
 #include "common.h"
 #include "launch.h"
 
 namespace qd {
 
-struct Cand {
-    float v;
-    int i;   // expert index, or INT_MAX when the lane has no live candidate
-};
-
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-    // a ranks before b: larger logit, then smaller index; a lane without a
-    // candidate (i == INT_MAX) never wins
-    if (a.i == INT_MAX) return false;
-    if (b.i == INT_MAX) return true;
-    return a.v > b.v || (a.v == b.v && a.i < b.i);
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+constexpr int ROUTE_MAX_E = 1024;
 
 template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int32_t* __restrict__ idx,
                                                          float* __restrict__ wout) {
+    __shared__ __align__(16) uint32_t keys[4][ROUTE_MAX_E];
+    __shared__ float sel[4][32];
     const int lane = threadIdx.x & 63;
-    const int t = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6);
-    if (t >= T) return;  // uniform per wave
-    const float* l = logits + (int64_t)t * E;
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    const bool live = t < T;
+    const float* l = logits + (int64_t)(live ? t : 0) * E;
     float v[PER];
-    bool live[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        live[i] = e < E;
-        v[i] = live[i] ? l[e] : 0.f;
+        v[i] = (live && e < E) ? l[e] : 0.f;
+        if (e < E) keys[wv][e] = order_key(v[i]);
     }
-    int my_idx = 0;
-    float my_val = 0.f;
-    for (int j = 0; j < k; ++j) {
-        Cand c{0.f, INT_MAX};
+    __syncthreads();
+    int rank[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const Cand o{v[i], live[i] ? lane + 64 * i : INT_MAX};
-            if (better(o, c)) c = o;
-        }
+    for (int i = 0; i < PER; ++i) rank[i] = 0;
+    uint32_t mine[PER];
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            Cand o;
-            o.v = __shfl_xor(c.v, m, 64);
-            o.i = __shfl_xor(c.i, m, 64);
-            if (better(o, c)) c = o;
-        }
-        // c is now the same winner in every lane
-        if (c.i != INT_MAX) {
+    for (int i = 0; i < PER; ++i) mine[i] = order_key(v[i]);
+    // 16 keys per iteration, read as four 16-byte broadcasts issued together
+    const int E16 = (E + 15) & ~15;
+    for (int e2 = E; e2 < E16; ++e2)
+        if (lane == 0) keys[wv][e2] = 0u;  // below every real key: never outranks
+    __syncthreads();
+    for (int e0 = 0; e0 < E16; e0 += 16) {
+        uint4 kv[4];
 #pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (lane + 64 * i == c.i) live[i] = false;
-        }
-        if (lane == j) {
-            my_idx = c.i;
-            my_val = c.v;
+        for (int q = 0; q < 4; ++q) kv[q] = *(const uint4*)&keys[wv][e0 + 4 * q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t kk[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e2 = e0 + 4 * q + c;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = lane + 64 * i;
+                    rank[i] += (kk[c] > mine[i]) || (kk[c] == mine[i] && e2 < e);
+                }
+            }
         }
     }
-    const float lmax = __shfl(my_val, 0, 64);
-    const float e = lane < k ? expf(my_val - lmax) : 0.f;
-    float tot = e;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) tot += __shfl_xor(tot, m, 64);
-    if (lane < k) {
-        idx[(int64_t)t * k + lane] = my_idx;
-        wout[(int64_t)t * k + lane] = e / tot;
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && rank[i] < k) {
+            sel[wv][rank[i]] = v[i];
+            if (live) idx[(int64_t)t * k + rank[i]] = e;
+        }
+    }
+    __syncthreads();
+    if (live && lane < k) {
+        const float lmax = sel[wv][0];
+        float tot = 0.f;
+        for (int j = 0; j < k; ++j) tot += expf(sel[wv][j] - lmax);
+        wout[(int64_t)t * k + lane] = expf(sel[wv][lane] - lmax) / tot;
     }
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              hipStream_t st) {
     const int threads = 256;
-    const int blocks = (int)(((int64_t)T * 64 + threads - 1) / threads);
+    const int blocks = (T + 3) / 4;
     if (E <= 64)
         hipLaunchKernelGGL(route_topk_kernel<1>, dim3(blocks), dim3(threads), 0, st, logits, T, E, k,
                            idx, w);

@@ -244,6 +244,88 @@ def bench_chunk(args, torch, qd):
             "cpu_baseline": None}
 
 
+def device_affine(torch, gen, bits, shape_nk, extra=()):
+    """Weights with the synth distributions, drawn on the device (fast enough to
+    fill 30 MoE layers): uniform code words, scales U[0.002, 0.02] (x 15/255 for
+    8-bit), biases -mid*s + N(0, 1e-3) rounded to fp16."""
+    N, K = shape_nk
+    lead = tuple(extra)
+    wq = torch.randint(-2**31, 2**31 - 1, lead + (N, K * bits // 32), dtype=torch.int32,
+                       device="cuda", generator=gen)
+    su = torch.rand(lead + (N, K // 64), device="cuda", generator=gen) * 0.018 + 0.002
+    if bits == 8:
+        su = su * (15.0 / 255.0)
+    s16 = su.half()
+    mid = 8.0 if bits == 4 else 128.0
+    b16 = (-mid * s16.float() + torch.randn(lead + (N, K // 64), device="cuda", generator=gen) * 1e-3).half()
+    return wq, s16, b16
+
+
+def bench_moe(args, torch, qd, prefill: bool):
+    """MoE layer (router int8 -> top-8 -> 8 routed + shared expert), 30 layers
+    cycled. Decode: batch 1, fp16 activations (16 distinct tokens per layer).
+    Prefill: one 128-token chunk of bf16 activations per step."""
+    E, H, I, Is, k, L = 128, 2816, 704, 2112, 8, 30
+    T = 128 if prefill else 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3 if not prefill else 4)
+    layers = []
+    for _ in range(args.sets or L):
+        rq, rs, rb = device_affine(torch, gen, 8, (E, H))
+        guq, gus, gub = device_affine(torch, gen, 4, (2 * I, H), (E,))
+        dnq, dns, dnb = device_affine(torch, gen, 4, (H, I), (E,))
+        sgq, sgs, sgb = device_affine(torch, gen, 4, (2 * Is, H))
+        sdq, sds, sdb = device_affine(torch, gen, 4, (H, Is))
+        layers.append(qd.MoeWeights(E, H, I, Is, rq, rs, rb, guq, gus, gub, dnq, dns, dnb,
+                                    sgq, sgs, sgb, sdq, sds, sdb))
+    ntok = 16 if not prefill else 1
+    xdt = torch.bfloat16 if prefill else torch.float16
+    xs = [torch.randn((T, H), device="cuda", generator=gen).to(xdt) for _ in range(ntok)]
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, qd.qmoe_workspace_bytes(layers[0], T, k)), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        lw, x = layers[i % len(layers)], xs[i % ntok]
+        def f():
+            qd.qmoe_layer(lw, x, k=k, workspace=ws, logits=logits, idx=idx, weights=wts, out=y)
+        return f
+
+    nsteps_cycle = len(layers) * ntok if not prefill else len(layers)
+    nsteps_cycle = min(nsteps_cycle, 240)
+    secs, _ = Timer(torch).run([step(i) for i in range(nsteps_cycle)], args.steps, args.warmup)
+    t = secs / args.steps
+    # algorithmic bytes: router + each distinct selected expert once + shared expert
+    expert_bytes = matrix_bytes(2 * I, H) + matrix_bytes(H, I)
+    shared_bytes = matrix_bytes(2 * Is, H) + matrix_bytes(H, Is)
+    router_bytes = matrix_bytes(E, H, 8)
+    uniq = []
+    for i in range(min(nsteps_cycle, 32)):
+        step(i)()
+        torch.cuda.synchronize()
+        uniq.append(len(set(idx.cpu().numpy().ravel().tolist())))
+    mean_uniq = float(np.mean(uniq))
+    step_bytes = router_bytes + mean_uniq * expert_bytes + shared_bytes + T * H * (2 + 4)
+    gbs = step_bytes / t / 1e9
+    name = "c4 MoE prefill chunk" if prefill else "c3 MoE decode layer"
+    return {"metric": "µs per MoE layer" + (" (128-token prefill chunk)" if prefill else " (decode, batch 1)"),
+            "value": round(t * 1e6, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if prefill else "f16",
+            "data": "synthetic",
+            "config": {"workload": f"{name}: hidden {H}, {E} experts (int4 g64 gate+up {H}->2x{I}, "
+                                   f"down {I}->{H}), router int8, top-{k}, shared expert "
+                                   f"{H}->2x{Is}->{H}, {len(layers)} layers cycled, T={T}",
+                       "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                       "mean_distinct_experts": mean_uniq, "step_bytes": int(step_bytes),
+                       "launches_per_layer": 4 if not prefill else 6},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "cpu_baseline": None}
+
+
 def bench_stream(args, torch):
     """Plain device copy (torch's copy kernel) and a read-mostly reduction over
     2 GiB buffers: the practical HBM ceiling, and the known-size reference used
@@ -367,6 +449,9 @@ def main():
         return
     if args.config == "c4":
         print(json.dumps(bench_chunk(args, torch, qd)), flush=True)
+        return
+    if args.config in ("c3", "c4moe"):
+        print(json.dumps(bench_moe(args, torch, qd, prefill=args.config == "c4moe")), flush=True)
         return
     raise SystemExit(f"config {args.config} is not wired into bench.py yet")
 
