@@ -51,8 +51,8 @@ struct MoeAArgs {
 // ---------------------------------------------------------------------------
 // A. gathered gate+up rows with the GELU gate.
 // ---------------------------------------------------------------------------
-template <int XF, int LPR, int U>
-__global__ __launch_bounds__(256) void moe_gateup_kernel(MoeAArgs a) {
+template <int XF, int LPR, int U, int CPL>
+__global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
     extern __shared__ uint4 lds[];
     constexpr int RPI = 64 / LPR;  // pairs per wave instruction
     const int C16 = a.H / 32;
@@ -63,13 +63,13 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(MoeAArgs a) {
     const int nwaves = blockDim.x >> 6;
     const int gw = blockIdx.x * nwaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = gridDim.x * nwaves;
-    const int S = (C16 + LPR - 1) / LPR;
+    const int S = (C16 + LPR * CPL - 1) / (LPR * CPL);
     const int npairs = a.k * a.I + a.Is;
     const int ntiles = (npairs + RPI - 1) / RPI;
     const int t0 = (int)((int64_t)ntiles * gw / W);
     const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
 
-    stage_x<4, XF>(a.x, a.xkind, a.H, 1, 0, C16, lds);
+    stage_x<4, XF, CPL>(a.x, a.xkind, a.H, 1, 0, C16, lds);
     __syncthreads();
     const uint32_t magic = in_vgpr(kMagic16);
 
@@ -105,14 +105,17 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(MoeAArgs a) {
         }
         float y[2][1] = {{0.f}, {0.f}};
         for (int s0 = 0; s0 < S; s0 += U) {
-            uint4 cw[U][2];
+            uint4 cw[U][CPL][2];
             uint16_t sr[U][2], br[U][2];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (s0 + u >= S) break;  // uniform
-                const int c = min((s0 + u) * LPR + sl, C16 - 1);
-                cw[u][0] = *(const uint4*)(q + (int64_t)g0 * wpr + (int64_t)c * 4);
-                cw[u][1] = *(const uint4*)(q + (int64_t)g1 * wpr + (int64_t)c * 4);
+                const int c = min(((s0 + u) * LPR + sl) * CPL, C16 - CPL);
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) {
+                    cw[u][ch][0] = *(const uint4*)(q + (int64_t)g0 * wpr + (int64_t)(c + ch) * 4);
+                    cw[u][ch][1] = *(const uint4*)(q + (int64_t)g1 * wpr + (int64_t)(c + ch) * 4);
+                }
                 sr[u][0] = sp[(int64_t)g0 * G + c / 2];
                 br[u][0] = bp[(int64_t)g0 * G + c / 2];
                 sr[u][1] = sp[(int64_t)g1 * G + c / 2];
@@ -121,16 +124,19 @@ __global__ __launch_bounds__(256) void moe_gateup_kernel(MoeAArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (s0 + u >= S) break;
-                const int cu = (s0 + u) * LPR + sl;
+                const int cu = ((s0 + u) * LPR + sl) * CPL;
                 const bool live = ok && cu < C16;
-                const int c = min(cu, C16 - 1);
+                const int c = min(cu, C16 - CPL);
                 float sc[2], bi[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     sc[r] = live ? h2f(sr[u][r]) : 0.f;
                     bi[r] = live ? h2f(br[u][r]) : 0.f;
                 }
-                chunk_rows<4, XF, 1, 2>(cw[u], sc, bi, lds, 1, C16, c, magic, y);
+                int slot[CPL];
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, C16);
+                group_rows<4, XF, 1, 2, CPL>(cw[u], sc, bi, lds, 1, C16, slot, magic, y);
             }
         }
         const float zg = seg_sum<LPR>(y[0][0]);
@@ -160,8 +166,8 @@ struct MoeBArgs {
     int E, H, I, Is, k;
 };
 
-template <int LPR, int R, int U>
-__global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
+template <int LPR, int R, int U, int CPL>
+__global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
     extern __shared__ uint4 lds[];
     constexpr int RPI = 64 / LPR;
     constexpr int ROWS = RPI * R;
@@ -212,15 +218,16 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) sum += v[i];
         constexpr int QPC = St::QPC;
+        const int sl = xslot<CPL>(c, C);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const float* u = v + 8 * w;
-            lds[(2 * w) * C + c] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
-                                              __float_as_uint(u[4]), __float_as_uint(u[6]));
-            lds[(2 * w + 1) * C + c] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[3]),
-                                                  __float_as_uint(u[5]), __float_as_uint(u[7]));
+            lds[(2 * w) * C + sl] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
+                                               __float_as_uint(u[4]), __float_as_uint(u[6]));
+            lds[(2 * w + 1) * C + sl] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[3]),
+                                                   __float_as_uint(u[5]), __float_as_uint(u[7]));
         }
-        ((float*)(lds + (size_t)QPC * C))[c] = sum;
+        ((float*)(lds + (size_t)QPC * C))[sl] = sum;
     }
     __syncthreads();
 
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
     const int nwaves = blockDim.x >> 6;
     const int gw = blockIdx.x * nwaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = gridDim.x * nwaves;
-    const int S = (C + LPR - 1) / LPR;
+    const int S = (C + LPR * CPL - 1) / (LPR * CPL);
     const int ntiles = (a.H + ROWS - 1) / ROWS;
     const int t0 = (int)((int64_t)ntiles * gw / W);
     const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
@@ -240,18 +247,20 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) y[r][0] = 0.f;
         for (int s0 = 0; s0 < S; s0 += U) {
-            uint4 cw[U][R];
+            uint4 cw[U][CPL][R];
             uint16_t sr[U][R], br[U][R];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (s0 + u >= S) break;
-                const int c = min((s0 + u) * LPR + sl, C - 1);
+                const int c = min(((s0 + u) * LPR + sl) * CPL, C - CPL);
                 const SegInfo si = info[c];
                 const int qs = si.qstride < 0 ? -si.qstride : si.qstride;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int n = min(tile * ROWS + r * RPI + seg, a.H - 1);
-                    cw[u][r] = *(const uint4*)(si.q + (int64_t)n * qs);
+#pragma unroll
+                    for (int ch = 0; ch < CPL; ++ch)
+                        cw[u][ch][r] = *(const uint4*)(si.q + (int64_t)n * qs + 4 * ch);
                     sr[u][r] = si.s[(int64_t)n * si.gstride];
                     br[u][r] = si.b[(int64_t)n * si.gstride];
                 }
@@ -259,8 +268,8 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (s0 + u >= S) break;
-                const int cu = (s0 + u) * LPR + sl;
-                const int c = min(cu, C - 1);
+                const int cu = ((s0 + u) * LPR + sl) * CPL;
+                const int c = min(cu, C - CPL);
                 const bool live = cu < C && info[c].qstride > 0;
                 float sc[R], bi[R];
 #pragma unroll
@@ -269,7 +278,10 @@ __global__ __launch_bounds__(256) void moe_down_kernel(MoeBArgs a) {
                     sc[r] = ok ? h2f(sr[u][r]) : 0.f;
                     bi[r] = ok ? h2f(br[u][r]) : 0.f;
                 }
-                chunk_rows<4, 1, 1, R>(cw[u], sc, bi, lds, 1, C, c, magic, y);
+                int slot[CPL];
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, C);
+                group_rows<4, 1, 1, R, CPL>(cw[u], sc, bi, lds, 1, C, slot, magic, y);
             }
         }
 #pragma unroll
@@ -288,7 +300,26 @@ size_t moe_decode_workspace_bytes(const MoeArgs& m, int k) {
     return ((size_t)k * m.I + m.Is) * sizeof(float);
 }
 
+#ifdef QD_TUNING
+// Tuning builds only: force the decode launch shapes (all zero = default).
+int qd_tune_moe[3] = {0, 0, 0};
+extern "C" int* qd_tune_moe_ptr() { return qd_tune_moe; }
+#endif
+
 namespace {
+
+// Launch shapes of the two decode kernels (workgroup waves, rows per tile).
+struct MoeCfg {
+    int gu_nw, dn_nw, dn_r;
+};
+
+MoeCfg moe_cfg() {
+    MoeCfg c{4, 16, 1};
+#ifdef QD_TUNING
+    if (qd_tune_moe[0]) c = MoeCfg{qd_tune_moe[0], qd_tune_moe[1], qd_tune_moe[2]};
+#endif
+    return c;
+}
 
 template <typename Kern>
 int grid_for(Kern kern, int threads, size_t lds, int ntiles_waves) {
@@ -300,29 +331,40 @@ int grid_for(Kern kern, int threads, size_t lds, int ntiles_waves) {
 
 template <int XF>
 hipError_t launch_gateup(const MoeAArgs& a, hipStream_t st) {
-    constexpr int LPR = 32, U = 3;
+    constexpr int LPR = 32, U = 3, CPL = 1;
     const size_t lds = Stage<4, XF>::bytes(1, a.H / 32);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     const int npairs = a.k * a.I + a.Is;
     const int ntiles = (npairs + (64 / LPR) - 1) / (64 / LPR);
-    auto kern = moe_gateup_kernel<XF, LPR, U>;
-    const int grid = grid_for(kern, 256, lds, ntiles);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
+    auto kern = moe_gateup_kernel<XF, LPR, U, CPL>;
+    const int threads = 64 * moe_cfg().gu_nw;
+    const int grid = grid_for(kern, threads, lds, ntiles);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_down(const MoeBArgs& a, hipStream_t st) {
-    constexpr int LPR = 64, R = 4, U = 4;
+template <int R>
+hipError_t launch_down_r(const MoeBArgs& a, int nw, hipStream_t st) {
+    constexpr int LPR = 64, U = 2, CPL = 2;
     const int C = a.k * (a.I / 32) + a.Is / 32;
     const size_t lds = ((Stage<4, 1>::bytes(1, C) + 15) & ~(size_t)15) + (size_t)C * sizeof(SegInfo);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     const int ntiles = (a.H + (64 / LPR) * R - 1) / ((64 / LPR) * R);
-    auto kern = moe_down_kernel<LPR, R, U>;
-    // every workgroup stages all k*I + Is activations, so keep one per CU; a
-    // wave's four rows x four steps are one round of 16 loads
-    const int grid = std::min(grid_for(kern, 256, lds, ntiles), device_info().cus);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
+    auto kern = moe_down_kernel<LPR, R, U, CPL>;
+    // every workgroup stages all k*I + Is activations: at most one per CU
+    const int threads = 64 * nw;
+    const int grid = std::min(grid_for(kern, threads, lds, ntiles), device_info().cus);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
     return hipGetLastError();
+}
+
+hipError_t launch_down(const MoeBArgs& a, hipStream_t st) {
+    const MoeCfg c = moe_cfg();
+#ifdef QD_TUNING
+    if (c.dn_r == 4) return launch_down_r<4>(a, c.dn_nw, st);
+    if (c.dn_r == 2) return launch_down_r<2>(a, c.dn_nw, st);
+#endif
+    return launch_down_r<1>(a, c.dn_nw, st);
 }
 
 }  // namespace
