@@ -1,7 +1,9 @@
 """Build libqdecode.so (HIP kernels + C ABI) for gfx950, in-tree.
 
-Every translation unit is compiled with hipcc for --offload-arch=gfx950 and
-with packed-fp32 VALU instructions disabled; the objects are linked into
+Every translation unit is compiled with hipcc for --offload-arch=gfx950, with
+packed-fp32 VALU instructions disabled and matrix-core results kept in
+ordinary VGPRs (no accumulation registers: reading results back from those
+costs one VALU instruction per value); the objects are linked into
 affine_quantized_gemv_qgemv_amd/libqdecode.so.
 """
 from __future__ import annotations
@@ -20,7 +22,8 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("QD_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form", "-Wall",
          "-Wno-unused-command-line-argument"]
 
 
