@@ -371,6 +371,10 @@ extern "C" int qd_tune_gemv[6] = {0, 0, 0, 0, 1, 4};
 hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                        const void* x, int xkind, float* y, int N, int K, int batch,
                        hipStream_t st) {
+    // a chunk of tokens through 8-bit weights (prefill routers): one
+    // matrix-core launch instead of slices of 8
+    if (bits == 8 && batch > 8 && (xkind == X_F16 || xkind == X_BF16))
+        return launch_gemm8_tokens(wq, s, b, (const uint16_t*)x, xkind, y, N, K, batch, st);
     for (int b0 = 0; b0 < batch; b0 += 8) {
         GemvArgs a{};
         a.wq = wq;

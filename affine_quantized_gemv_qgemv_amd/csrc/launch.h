@@ -53,6 +53,11 @@ hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float*
                               const void* x, int xkind, float* y, void* ws, size_t ws_bytes,
                               hipStream_t st);
 
+// 8-bit weights over T > 8 tokens (f16 or bf16 activations) on the matrix core.
+hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                               const uint16_t* x, int xkind, float* y, int N, int K, int T,
+                               hipStream_t st);
+
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x_bf16, float* y, int M, int N, int K,
                              hipStream_t st);

@@ -70,6 +70,47 @@ def test_router_prefill_batch_128():
         assert_within(y, yr, a, f"router T=128 {xdt}")
 
 
+# 8-bit weights over more than 8 tokens take the matrix-core path: ragged
+# token / output tiles (32 x 32) and group counts that leave some of the
+# 8 K-waves with fewer groups or none.
+@pytest.mark.parametrize("T", [9, 16, 33, 100])
+@pytest.mark.parametrize("N,K", [(1, 64), (37, 704), (128, 2112), (200, 4096)])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_int8_token_chunk(T, N, K, xdt):
+    w = synth.affine_weights(8, N, K, cfg=210, set_id=T * 7 + N)
+    xb = draw_x(T, K, xdt, T * 13 + N)
+    y = run_gemv(8, w, xb, xdt).cpu().numpy()
+    yr, a = ref_gemv(w, xb, xdt)
+    print(f"int8 chunk T={T} N={N} K={K} {xdt}", flush=True)
+    assert_within(y, yr, a, f"int8 chunk T={T} N={N} K={K} {xdt}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_int8_token_chunk_extreme_codes(xdt):
+    K, T = 1024, 24
+    for kind, c in (("zero", 0), ("const", 15), ("const", 16), ("const", 255)):
+        w = synth.affine_weights(8, 70, K, cfg=211, set_id=c, codes=kind, const_code=c)
+        xb = draw_x(T, K, xdt, c)
+        y = run_gemv(8, w, xb, xdt).cpu().numpy()
+        yr, a = ref_gemv(w, xb, xdt)
+        assert_within(y, yr, a, f"{kind} {c} {xdt}")
+
+
+def test_int8_token_chunk_deterministic_and_in_bounds():
+    N, K, T = 130, 2816, 45
+    w = synth.affine_weights(8, N, K, cfg=212, set_id=0)
+    xb = draw_x(T, K, "bf16", 3)
+    guard = 4096
+    buf = torch.full((guard + T * N + guard,), float("nan"), device="cuda")
+    out = buf[guard:guard + T * N].view(T, N)
+    y1 = run_gemv(8, w, xb, "bf16", out=out).clone()
+    y2 = run_gemv(8, w, xb, "bf16").clone()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + T * N:]).all()
+    assert torch.equal(y1, y2)
+    yr, a = ref_gemv(w, xb, "bf16")
+    assert_within(y1.cpu().numpy(), yr, a, "int8 chunk")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_one_hot_is_bit_exact(bits):
     N, K = 64, 2048
