@@ -36,6 +36,7 @@ struct GemvArgs {
     int nb;              // activation vectors in this launch (<= B)
     int chunks_split;    // chunks per K split (grid dimension y)
     int atomic_out;
+    int interleave;      // tile order: 1 = wave w takes tiles w, w + W, ...; 0 = a contiguous block
 };
 
 // One round of loads: U steps of R rows; a step gives each lane CPL
@@ -69,10 +70,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     const int S = (nc + LPR * CPL - 1) / (LPR * CPL);  // steps per row
     const int RPT = (S + U - 1) / U;               // rounds per tile
     const int ntiles = (a.N + ROWS - 1) / ROWS;
-    // contiguous, balanced share of tiles for this wave
-    const int t0 = (int)((int64_t)ntiles * gw / W);
-    const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
-    const int nrounds = (t1 - t0) * RPT;
+    // This wave's tiles: interleaved (all waves together sweep one window of
+    // the matrix, as a streaming read does) or a contiguous, balanced block.
+    int t0, tstep, ntl;
+    if (a.interleave) {
+        t0 = gw;
+        tstep = W;
+        ntl = gw < ntiles ? (ntiles - gw + W - 1) / W : 0;
+    } else {
+        t0 = (int)((int64_t)ntiles * gw / W);
+        tstep = 1;
+        ntl = (int)((int64_t)ntiles * (gw + 1) / W) - t0;
+    }
+    const int nrounds = ntl * RPT;
 
     // Loads are unconditional inside a wave-uniform step test: rows past N and
     // chunks past the staged range read a clamped, valid address and get a
@@ -80,7 +90,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     // loads would make the compiler wait for every load in flight.)
     auto issue = [&](Round<R, U, CPL>& buf, int rd) {
         if (rd >= nrounds) return;
-        const int tile = t0 + rd / RPT;
+        const int tile = t0 + (rd / RPT) * tstep;
         const int sg = rd - (rd / RPT) * RPT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     const uint32_t magic = in_vgpr(kMagic16);
     auto consume = [&](const Round<R, U, CPL>& buf, int rd) {
         if (rd >= nrounds) return;
-        const int tile = t0 + rd / RPT;
+        const int tile = t0 + (rd / RPT) * tstep;
         const int sg = rd - (rd / RPT) * RPT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -237,6 +247,7 @@ hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
 
 struct Cfg {
     int lpr, r, u, wpe, cpl, nw;
+    int il = 0;   // interleaved tile order
 };
 
 // Lanes per row: the largest segment width that wastes the fewest lane
@@ -269,6 +280,7 @@ int pow2_floor(int v) {
 
 Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
     Cfg c;
+    c.il = 1;   // waves sweep the matrix together (measured faster on every shape)
     const int chunks = K * bits / 128;
     c.lpr = pick_lpr(chunks);
     c.wpe = 1;
@@ -365,7 +377,8 @@ hipError_t run_batch(const GemvArgs& a, const Cfg& c, hipStream_t st) {
 
 #ifdef QD_TUNING
 // Tuning builds only: force a configuration (all zero = the default policy).
-extern "C" int qd_tune_gemv[6] = {0, 0, 0, 0, 1, 4};
+// Entry 6 >= 0 forces the tile order alone.
+extern "C" int qd_tune_gemv[7] = {0, 0, 0, 0, 1, 4, -1};
 #endif
 
 hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
@@ -392,8 +405,10 @@ hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const ui
 #ifdef QD_TUNING
         if (qd_tune_gemv[0])
             c = Cfg{qd_tune_gemv[0], qd_tune_gemv[1], qd_tune_gemv[2], qd_tune_gemv[3],
-                    qd_tune_gemv[4], qd_tune_gemv[5]};
+                    qd_tune_gemv[4], qd_tune_gemv[5], c.il};
+        if (qd_tune_gemv[6] >= 0) c.il = qd_tune_gemv[6];
 #endif
+        a.interleave = c.il;
         hipError_t e;
         if (bits == 4)
             e = xf == 0 ? run_batch<4, 0>(a, c, st) : run_batch<4, 1>(a, c, st);
