@@ -10,20 +10,27 @@
 // Four launches:
 //   1. prep: a counting sort of the T*k (token, slot) pairs by expert
 //      (offsets, sorted pair list, each pair's position; pairs with an expert
-//      id outside [0, E) are dropped), and the per-group row sums of x;
-//   2. gate+up: one workgroup per (expert, 64 columns of I) computes gate and
-//      up for the expert's gathered token rows on MFMA (exact codes as the
-//      matrix operand, as in chunk.hip), then h' = p * GELU(gate) * up, split
-//      into bf16 hi + lo (16 significant bits) for the next MFMA, plus the
-//      per-group row sums of hi + lo. The shared expert is one more item with
-//      all T tokens and weight one;
-//   3. down: one workgroup per (expert, 128 columns of H) runs two MFMA chains
-//      (hi and lo activations) against the same codes and writes each pair's
-//      output row;
+//      id outside [0, E) are dropped), and a table of the experts' 32-row
+//      blocks of sorted pairs;
+//   2. gate+up: one workgroup per (32-row block, 64 columns of I): two gate
+//      waves and two up waves each stream their 32 weight rows against the
+//      block's gathered activation rows (staged once in LDS) on the matrix
+//      core (exact codes as the operand, as in chunk.hip), then
+//      h' = p * GELU(gate) * up is split into bf16 hi + lo (16 significant
+//      bits) for the next MFMA. The shared expert adds row blocks of all T
+//      tokens with weight one;
+//   3. down: one workgroup per (32-row block, 128 columns of H) runs hi and
+//      lo MFMA chains against the same codes and writes each pair's output
+//      row;
 //   4. combine: y[t] = o_shared[t] + sum over the token's slots of its
 //      (already weighted) pair rows, in slot order.
-// Every expert's weights are read once per chunk; nothing uses atomics on
-// the data path, so results are run-to-run deterministic.
+// Every expert's weights are read once per 32 of its pairs; nothing uses
+// atomics on the data path, so results are run-to-run deterministic. The
+// expert kernels have no barrier in their main loop: codes, scales and
+// biases run several groups ahead in a register ring and activations a few
+// groups ahead, so each wave keeps its loads in flight while it computes.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -36,18 +43,22 @@ struct PrefillWs {
     int* sorted_pair;   // [T*k] pair ids (t*k + j) grouped by expert
     int* pos;           // [T*k] sorted position of each pair, -1 if dropped
     int* offs;          // [E+1] first sorted position of each expert
-    float* xsum;        // [T][H/64] row sums of x per group
+    int* rbs;           // [E+1] first 32-row block of each expert
+    int4* rbinfo;       // [row blocks] (expert, first sorted row, rows, 0)
+    int* stok;          // [T*k] token of each sorted row
     uint16_t* hhi;      // [T*k][I] bf16 high part of h' (sorted rows)
     uint16_t* hlo;      // [T*k][I] bf16 low part
-    float* hsum;        // [T*k][I/64]
     uint16_t* shhi;     // [T][Is]
     uint16_t* shlo;     // [T][Is]
-    float* shsum;       // [T][Is/64]
     float* O;           // [T*k][H] weighted routed outputs (sorted rows)
     float* Os;          // [T][H] shared-expert outputs
 };
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Routed 32-row blocks: at most ceil(P / 32) full ones plus one partial block
+// per expert.
+static int max_row_blocks(int P, int E) { return (P + 31) / 32 + E; }
 
 static PrefillWs carve(void* base, const MoeArgs& m, int T, int k, size_t* total) {
     PrefillWs w{};
@@ -62,13 +73,13 @@ static PrefillWs carve(void* base, const MoeArgs& m, int T, int k, size_t* total
     w.sorted_pair = (int*)take(P * 4);
     w.pos = (int*)take(P * 4);
     w.offs = (int*)take(((size_t)m.E + 1) * 4);
-    w.xsum = (float*)take((size_t)T * (m.H / 64) * 4);
+    w.rbs = (int*)take(((size_t)m.E + 1) * 4);
+    w.rbinfo = (int4*)take((size_t)max_row_blocks((int)P, m.E) * 16);
+    w.stok = (int*)take(P * 4);
     w.hhi = (uint16_t*)take(P * m.I * 2);
     w.hlo = (uint16_t*)take(P * m.I * 2);
-    w.hsum = (float*)take(P * (m.I / 64) * 4);
     w.shhi = (uint16_t*)take((size_t)T * m.Is * 2);
     w.shlo = (uint16_t*)take((size_t)T * m.Is * 2);
-    w.shsum = (float*)take((size_t)T * (m.Is / 64) * 4);
     w.O = (float*)take(P * m.H * 4);
     w.Os = (float*)take((size_t)T * m.H * 4);
     if (total) *total = off;
@@ -88,10 +99,10 @@ constexpr int PREP_MAX_PAIRS = 128 * 32;
 constexpr int PREP_MAX_E = 1024;
 
 __global__ __launch_bounds__(1024) void moe_prep_kernel(const int32_t* __restrict__ idx, int T,
-                                                        int k, int E, const void* __restrict__ x,
-                                                        int xkind, int H, PrefillWs w) {
+                                                        int k, int E, PrefillWs w) {
     __shared__ int sidx[PREP_MAX_PAIRS];
     __shared__ int cnt[PREP_MAX_E + 1];
+    __shared__ int rbl[PREP_MAX_E + 1];
     const int P = T * k;
     const int tid = threadIdx.x, bs = blockDim.x;
     for (int i = tid; i < P; i += bs) sidx[i] = idx[i];
@@ -103,16 +114,27 @@ __global__ __launch_bounds__(1024) void moe_prep_kernel(const int32_t* __restric
     }
     __syncthreads();
     if (tid == 0) {
-        int run = 0;
+        int run = 0, rb = 0;
         for (int e = 0; e < E; ++e) {
             const int c = cnt[e];
             cnt[e] = run;
+            rbl[e] = rb;
             run += c;
+            rb += (c + 31) / 32;
         }
         cnt[E] = run;
+        rbl[E] = rb;
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += bs) w.offs[e] = cnt[e];
+    for (int e = tid; e <= E; e += bs) {
+        w.offs[e] = cnt[e];
+        w.rbs[e] = rbl[e];
+    }
+    for (int e = tid; e < E; e += bs)
+        for (int r = rbl[e]; r < rbl[e + 1]; ++r) {
+            const int r0 = cnt[e] + 32 * (r - rbl[e]);
+            w.rbinfo[r] = make_int4(e, r0, min(32, cnt[e + 1] - r0), 0);
+        }
     __syncthreads();  // offsets are read before the counters advance
     // placement: a slot inside the expert's range from an LDS counter. The
     // order inside an expert's rows does not change any result (every output
@@ -123,35 +145,15 @@ __global__ __launch_bounds__(1024) void moe_prep_kernel(const int32_t* __restric
             const int ps = atomicAdd(&cnt[e], 1);
             w.pos[p] = ps;
             w.sorted_pair[ps] = p;
+            w.stok[ps] = p / k;
         } else {
             w.pos[p] = -1;
         }
     }
-    // per-group row sums of x: one (token, group) per thread, 8 x 16-byte loads
-    const int G = H / 64;
-    for (int item = tid; item < T * G; item += bs) {
-        const int t = item / G, g = item - t * G;
-        const uint4* src = (const uint4*)((const uint16_t*)x + (int64_t)t * H + g * 64);
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 v = src[i];
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (xkind == X_F16)
-                    s += h2f(wv[j] & 0xFFFF) + h2f(wv[j] >> 16);
-                else
-                    s += bf2f(wv[j] & 0xFFFF) + bf2f(wv[j] >> 16);
-            }
-        }
-        w.xsum[item] = s;
-    }
 }
 
 // ---------------------------------------------------------------------------
-// Shared MFMA pieces: stage the group slice of up to 128 gathered rows, then
-// run one 32-column block per wave over ceil(M/32) row blocks.
+// Shared pieces
 // ---------------------------------------------------------------------------
 template <bool F16>
 __device__ __forceinline__ floatx16 mfma16(const uint4& a, const uint4& b, const floatx16& c) {
@@ -163,15 +165,275 @@ __device__ __forceinline__ floatx16 mfma16(const uint4& a, const uint4& b, const
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// 8 codes of one word -> 16-bit (offset + q), natural k order; magic is the
-// offset's bit pattern in both halves (bf16 128.0 or fp16 1024.0).
-__device__ __forceinline__ uint4 codes_to_16(uint32_t w, uint32_t magic) {
-    const uint32_t t = w & 0x0F0F0F0Fu;
-    const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;
-    return make_uint4(__builtin_amdgcn_perm(u, t, 0x0C040C00u) | magic,
-                      __builtin_amdgcn_perm(u, t, 0x0C050C01u) | magic,
-                      __builtin_amdgcn_perm(u, t, 0x0C060C02u) | magic,
-                      __builtin_amdgcn_perm(u, t, 0x0C070C03u) | magic);
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Keeps the compiler from sinking an accumulator update past later groups
+// (which would hold several groups' partial products live at once).
+__device__ __forceinline__ void pin(floatx16& v) { asm volatile("" : "+v"(v)); }
+
+// A copy of v the compiler cannot see through or hoist out of a loop: keeps
+// per-group LDS offsets as immediates on a per-stage base.
+__device__ __forceinline__ int opaque_i(int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// 8 codes of one word -> 16-bit (offset + q) in the k order
+// [0, 4, 1, 5, 2, 6, 3, 7]: one v_and_or_b32 per pair (magic = the offset's
+// bit pattern in both halves, bf16 128.0 or fp16 1024.0, kept in a VGPR).
+// The activations are staged in LDS in the same order (perm8 below).
+__device__ __forceinline__ uint4 codes_to_16p(uint32_t w, uint32_t magic) {
+    return make_uint4((w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
+                      ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic);
+}
+
+// 8 16-bit values e0..e7 -> e0 e4 e1 e5 e2 e6 e3 e7 (matches codes_to_16p).
+__device__ __forceinline__ uint4 perm8(uint4 v) {
+    // v_perm_b32(src0, src1, sel): selector bytes 0..3 pick src1's bytes, 4..7 src0's
+    return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
+                      __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                      __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                      __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+}
+
+// Both expert kernels: a workgroup of 4 waves owns one 32-row block and 4
+// weight-row tiles of 32 (one per wave). The block's activation rows are
+// staged in LDS a stage of XSG groups at a time (double buffered, one barrier
+// per stage; the next stage is read into registers while the current one is
+// consumed), permuted to the codes' k order and with their per-group row
+// sums, so each activation byte is fetched once per workgroup rather than
+// once per wave. Each wave keeps its codes, scales and biases XD groups
+// ahead in a register ring. Per group a wave runs one MFMA chain per
+// activation plane and adds s P; the bias term, (b - off s) Xsum, is added
+// once per stage on the matrix core.
+constexpr int XSG = 4;       // groups per stage
+constexpr int XD = 4;        // groups of codes in flight per wave (whole stages)
+constexpr int XPF = 1;       // stages of activations in flight (1 or 2)
+constexpr int GU_WAVES = 4;  // gate+up workgroup: 2 gate + 2 up waves
+constexpr int DN_WAVES = 4;  // down workgroup: 4 column tiles
+// two waves per SIMD: two workgroups share a CU, so one's latency-bound
+// phases (start, stage barriers) overlap the other's work
+constexpr int XWPE = 2;
+
+// LDS: [2 buffers][PLANES][XSG groups][32 rows][XS_STRIDE] uint4, then the
+// per-group row sums (over the planes) twice, as xsum [2 buffers][32 rows]
+// [XSG] and xsumT [2 buffers][XSG][32 rows] fp32. NW waves stage: TPG =
+// NW / 2 threads share a (row, group) and each holds UPT = 8 / TPG of its
+// 16-byte chunks.
+template <int PLANES, bool F16, int NW>
+struct XStage {
+    static constexpr int PER = XSG * 32 * XS_STRIDE;   // uint4 per plane per buffer
+    static constexpr int BUF = PLANES * PER;
+    static constexpr int SUMS = 2 * 32 * XSG;          // floats per copy (both buffers)
+    static constexpr int LDS_UINT4 = 2 * BUF + (2 * SUMS) / 4;
+    static constexpr int TPG = NW / 2;
+    static constexpr int UPT = 8 / TPG;
+    static_assert(TPG * XSG * 32 == 64 * NW, "staging split");
+    // thread t: row t / (TPG XSG), group (t / TPG) % XSG, chunks UPT (t % TPG) ..
+    __device__ static __forceinline__ void load(const uint16_t* const (&row)[PLANES], int g0, int G,
+                                                uint4 (&r)[PLANES][UPT]) {
+        const int part = threadIdx.x % (TPG * XSG);
+        const int g = min(g0 + part / TPG, G - 1);
+        const int c = UPT * (part % TPG);
+#pragma unroll
+        for (int pl = 0; pl < PLANES; ++pl) {
+            const uint4* src = (const uint4*)(row[pl] + (int64_t)g * 64 + 8 * c);
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                // a value temporary: a struct copy between pointers becomes a
+                // memcpy that keeps the array in scratch memory
+                const uint4 v = src[i];
+                r[pl][i] = v;
+            }
+        }
+    }
+    __device__ static __forceinline__ void store(uint4* buf, float* xsum, const uint4 (&r)[PLANES][UPT]) {
+        const int rr = threadIdx.x / (TPG * XSG), part = threadIdx.x % (TPG * XSG);
+        const int gi = part / TPG, c = UPT * (part % TPG);
+        float acc = 0.f;
+#pragma unroll
+        for (int pl = 0; pl < PLANES; ++pl) {
+            uint4* dst = buf + pl * PER + (gi * 32 + rr) * XS_STRIDE + c;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                const uint4 v = r[pl][i];
+                dst[i] = perm8(v);
+                const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc = F16 ? dot2(vv[j], 0x3C003C00u, acc) : bf16_pair_sum(vv[j], acc);
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < TPG; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        // the TPG threads of (row, group) store the same sum
+        xsum[rr * XSG + gi] = acc;
+        xsum[SUMS + gi * 32 + rr] = acc;
+    }
+};
+
+// Per-wave ring of one weight row's codes, scales and biases (lane: words
+// 4h..4h+3 of each group).
+template <int D>
+struct CodeRing {
+    uint4 q[D];
+    uint32_t s[D], b[D];
+    const uint32_t* wrow;
+    const uint16_t *srow, *brow;
+    int G;
+    __device__ __forceinline__ void init(const uint32_t* w, const uint16_t* sr, const uint16_t* br, int g) {
+        wrow = w;
+        srow = sr;
+        brow = br;
+        G = g;
+#pragma unroll
+        for (int d = 0; d < D; ++d) fill(d, d);
+    }
+    __device__ __forceinline__ void fill(int d, int g) {
+        g = min(g, G - 1);
+        q[d] = *(const uint4*)(wrow + (int64_t)g * 8);
+        s[d] = srow[g];
+        b[d] = brow[g];
+    }
+};
+
+// Streams the G groups of a wave's weight row against the staged activation
+// planes: acc (D layout, 32 rows x this lane's column) += sum over groups of
+// s (P_g - off Xsum_g) + b Xsum_g. The first part runs in fp32 per group (P_g
+// and off Xsum_g nearly cancel, so it needs full precision); b Xsum_g, of the
+// size of the result, runs once per stage on the matrix core. NQ = row
+// quarters (8 rows) that hold data: the per-group scaling skips the others. Whole rounds of XD groups run with no
+// data-dependent exits (an exit inside a round would make the compiler wait
+// for every load in flight where the paths join); the last partial round runs
+// with checks.
+template <int PLANES, bool F16, int NW, int NQ>
+__device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t* const (&row)[PLANES],
+                                              CodeRing<XD>& ring, float off, floatx16& acc) {
+    using XS = XStage<PLANES, F16, NW>;
+    constexpr int SPR = XD / XSG;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5, l32 = lane & 31;
+    float* xsum_raw = (float*)(lds + 2 * XS::BUF);
+    const int NS = (G + XSG - 1) / XSG;
+    const uint32_t magic = in_vgpr(F16 ? 0x64006400u : 0x43004300u);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    auto split = [](float a0, float a1, uint32_t& hi, uint32_t& lo) __attribute__((always_inline)) {
+        const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
+        hi = __builtin_bit_cast(uint32_t, hv);
+        const bf16x2_t lv = {(__bf16)(a0 - __uint_as_float(hi << 16)),
+                             (__bf16)(a1 - __uint_as_float(hi & 0xFFFF0000u))};
+        lo = __builtin_bit_cast(uint32_t, lv);
+    };
+
+    // activations run XPF stages ahead. XPF = 2: register set st & 1 receives
+    // stage st + 2 while set (st + 1) & 1 holds stage st + 1 until it is
+    // stored; XPF = 1: one set, loaded at the stage's start, stored at its end.
+    static_assert(XPF == 1 || (XPF == 2 && SPR % 2 == 0), "prefetch depth");
+    uint4 xr0[PLANES][XS::UPT], xr1[PLANES][XS::UPT];
+    XS::load(row, 0, G, xr0);
+    if constexpr (XPF == 2) XS::load(row, XSG, G, xr1);
+    XS::store(lds, xsum_raw, xr0);
+    __syncthreads();
+    auto stage = [&](const int st, auto sjc, auto checked) __attribute__((always_inline)) {
+        constexpr int sj = decltype(sjc)::value;   // st mod SPR (rounds hold SPR stages)
+        constexpr bool chk = decltype(checked)::value;
+        const int buf = st & 1;
+        auto& xin = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 1) return xr1; else return xr0; }();
+        auto& xout = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 0) return xr1; else return xr0; }();
+        XS::load(row, (st + XPF) * XSG, G, xin);
+        // bias of the stage's groups as one MFMA: factors split into bf16
+        // hi + lo; lane half h supplies K slots 8h..8h+7 as A = (x_h, x_h)
+        // over the 4 groups (x_0 = hi, x_1 = lo) and B = (hi, lo), so the
+        // slots sum to (xhi + xlo)(bhi + blo), each product exact in fp32
+        {
+            float bv[4];
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                bv[gi] = h2f((uint16_t)ring.b[sj * XSG + gi]);
+                if constexpr (chk)
+                    if (st * XSG + gi >= G) bv[gi] = 0.f;
+            }
+            uint32_t bh01, bl01, bh23, bl23;
+            split(bv[0], bv[1], bh01, bl01);
+            split(bv[2], bv[3], bh23, bl23);
+            const float4 xv =
+                *(const float4*)(xsum_raw + buf * 32 * XSG + opaque_i(l32 * XSG));
+            uint32_t xh01, xl01, xh23, xl23;
+            split(xv.x, xv.y, xh01, xl01);
+            split(xv.z, xv.w, xh23, xl23);
+            const uint32_t a01 = h ? xl01 : xh01, a23 = h ? xl23 : xh23;
+            acc = mfma16<false>(make_uint4(a01, a23, a01, a23), make_uint4(bh01, bh23, bl01, bl23), acc);
+        }
+        const uint4* xs = lds + opaque_i(buf * XS::BUF + l32 * XS_STRIDE + 4 * h);
+        // row sums in the accumulator layout: rows 8 q + 4 h + (0..3) of group gi
+        const float* xt = xsum_raw + opaque_i(XS::SUMS + buf * 32 * XSG + 4 * h);
+        static_for<0, XSG>([&](auto gic) __attribute__((always_inline)) {
+            constexpr int gi = decltype(gic)::value;
+            constexpr int d = sj * XSG + gi;
+            const int g = st * XSG + gi;
+            if (chk && g >= G) return;
+            floatx16 P;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) P[i] = 0.f;
+            const uint32_t wv[4] = {ring.q[d].x, ring.q[d].y, ring.q[d].z, ring.q[d].w};
+#pragma unroll
+            for (int stp = 0; stp < 4; ++stp) {
+                const uint4 bfrag = codes_to_16p(wv[stp], magic);
+#pragma unroll
+                for (int pl = 0; pl < PLANES; ++pl)
+                    P = mfma16<F16>(xs[pl * XS::PER + gi * 32 * XS_STRIDE + stp], bfrag, P);
+            }
+            const float sf = h2f((uint16_t)ring.s[d]);
+            const float mo = -off * sf;
+            // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) {
+                const float4 xq = *(const float4*)(xt + gi * 32 + 8 * qq);
+                acc[4 * qq + 0] = fmaf(sf, P[4 * qq + 0], fmaf(mo, xq.x, acc[4 * qq + 0]));
+                acc[4 * qq + 1] = fmaf(sf, P[4 * qq + 1], fmaf(mo, xq.y, acc[4 * qq + 1]));
+                acc[4 * qq + 2] = fmaf(sf, P[4 * qq + 2], fmaf(mo, xq.z, acc[4 * qq + 2]));
+                acc[4 * qq + 3] = fmaf(sf, P[4 * qq + 3], fmaf(mo, xq.w, acc[4 * qq + 3]));
+            }
+            pin(acc);
+            ring.fill(d, g + XD);   // the slot's contents are dead now
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        XS::store(lds + (buf ^ 1) * XS::BUF, xsum_raw + (buf ^ 1) * 32 * XSG, xout);
+        __syncthreads();
+    };
+    const int rounds = G / XD;
+    for (int r = 0; r < rounds; ++r)
+        static_for<0, SPR>([&](auto sjc) __attribute__((always_inline)) {
+            stage(r * SPR + decltype(sjc)::value, sjc, std::false_type{});
+        });
+    static_for<0, SPR>([&](auto sjc) __attribute__((always_inline)) {
+        const int st = rounds * SPR + decltype(sjc)::value;
+        if (st < NS) stage(st, sjc, std::true_type{});
+    });
+}
+
+// Runs stream_expert with NQ = ceil(M / 8) fixed at compile time.
+template <int PLANES, bool F16, int NW>
+__device__ __forceinline__ void stream_expert_m(int M, int G, uint4* lds,
+                                                const uint16_t* const (&row)[PLANES],
+                                                CodeRing<XD>& ring, float off, floatx16& acc) {
+    const int nq = (M + 7) / 8;
+    if (nq <= 1)
+        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, off, acc);
+    else if (nq == 2)
+        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, off, acc);
+    else if (nq == 3)
+        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, off, acc);
+    else
+        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, off, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,206 +445,105 @@ struct GuArgs {
     const uint16_t* x;   // [T][H] fp16 or bf16 bits
     const float* p;      // [T*k] routing weights in pair order
     int E, H, I, Is, k, T, act;
+    int rbmax;           // size of the row-block table
     PrefillWs w;
 };
 
+// Workgroup = (32-row block, GT = NW / 2 column tiles of 32): waves 0..GT-1
+// the gate rows of tiles GT q + w, waves GT..NW-1 the matching up rows.
+// Routed blocks come first (expert from the row-block table), then the
+// shared expert's blocks of all T tokens.
 template <bool F16>
-__global__ __launch_bounds__(256) void moe_gu_kernel(GuArgs a) {
-    __shared__ __align__(16) uint4 xs_raw[2][128 * XS_STRIDE];
-    __shared__ __align__(16) float xsum_raw[2][128];
-    __shared__ __align__(16) float zb[128][64];
-    __shared__ int tokrow[128];
-    __shared__ float prow[128];
-    const int ntI = a.I / 64;
-    const bool shared = (int)blockIdx.x >= a.E * ntI;
-    int e = 0, nt, rb, M, Iw;
+__global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(XWPE, XWPE))) void moe_gu_kernel(GuArgs a) {
+    constexpr int NW = GU_WAVES, GT = NW / 2;
+    __shared__ __align__(16) uint4 lds[XStage<1, F16, NW>::LDS_UINT4];
+    __shared__ float zb[GT][32][33];
+    const int ntc = a.I / 32, ntcs = a.Is / 32;
+    const int nq = (ntc + GT - 1) / GT, nqs = (ntcs + GT - 1) / GT;
+    const int item = blockIdx.x;
+    // both loads issued together: the block record is read speculatively
+    // (any index below the table size is valid memory)
+    const int R = a.w.rbs[a.E];
+    const int4 info = a.w.rbinfo[min(item / nq, a.rbmax - 1)];
+    const int items_r = R * nq;
+    const int items = items_r + ((a.T + 31) / 32) * nqs;
+    if (item >= items) return;   // the whole workgroup leaves together
+    const bool shared = item >= items_r;
+    int row0, M, q, Iw, ntl;
     const uint32_t* Wq;
     const uint16_t *Ws, *Wb;
     if (!shared) {
-        e = blockIdx.x / ntI;
-        nt = blockIdx.x - e * ntI;
-        rb = a.w.offs[e];
-        M = a.w.offs[e + 1] - rb;
+        const int rbi = item / nq;
+        q = item - rbi * nq;
+        const int e = info.x;
+        row0 = info.y;
+        M = info.z;
         Iw = a.I;
+        ntl = ntc;
         const int64_t rows = 2 * (int64_t)a.I;
         Wq = a.gu_q + (int64_t)e * rows * (a.H / 8);
         Ws = a.gu_s + (int64_t)e * rows * (a.H / 64);
         Wb = a.gu_b + (int64_t)e * rows * (a.H / 64);
     } else {
-        nt = blockIdx.x - a.E * ntI;
-        rb = 0;
-        M = a.T;
+        const int j = item - items_r;
+        const int rbk = j / nqs;
+        q = j - rbk * nqs;
+        row0 = 32 * rbk;
+        M = min(32, a.T - row0);
         Iw = a.Is;
+        ntl = ntcs;
         Wq = a.sgu_q;
         Ws = a.sgu_s;
         Wb = a.sgu_b;
     }
-    if (M <= 0) return;  // the whole workgroup leaves together
-    const int nmb = (M + 31) / 32;
-    const int Mp = nmb * 32;
     const int tid = threadIdx.x;
-    if (tid < 128) {
-        if (tid < M) {
-            const int pr = shared ? -1 : a.w.sorted_pair[rb + tid];
-            tokrow[tid] = shared ? tid : pr / a.k;
-            prow[tid] = shared ? 1.f : a.p[pr];
-        } else {
-            tokrow[tid] = 0;
-            prow[tid] = 0.f;
-        }
-    }
-    __syncthreads();
-
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int G = a.H / 64;
-    const int64_t wpr = a.H / 8;
-    const int col = ((wave >> 1) ? Iw : 0) + 64 * nt + 32 * (wave & 1) + l32;  // row of W
-    const uint32_t* wrow = Wq + (int64_t)col * wpr + 4 * h;
-    const uint16_t* srow = Ws + (int64_t)col * G;
-    const uint16_t* brow = Wb + (int64_t)col * G;
-    const uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
-    const float offset = F16 ? 1024.f : 128.f;
+    const int tile = min(GT * q + wave % GT, ntl - 1);   // clamped: waves past the last tile store nothing
+    const int col = (wave >= GT ? Iw : 0) + 32 * tile + l32;   // weight row of this lane
+    CodeRing<XD> ring;
+    ring.init(Wq + (int64_t)col * (a.H / 8) + 4 * h, Ws + (int64_t)col * G, Wb + (int64_t)col * G, G);
+    // staged row of this thread (rows past M repeat row M - 1; their results
+    // are never stored)
+    const int sr = min(tid / (NW * 2), M - 1);
+    const int tok = shared ? row0 + sr : a.w.stok[row0 + sr];
+    const uint16_t* const xrow[1] = {a.x + (int64_t)tok * a.H};
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, F16 ? 1024.f : 128.f, acc);
 
-    auto load_x = [&](int g, uint4 (&xr)[4]) {
+    // up waves -> LDS; each gate wave forms h' = p GELU(gate) up
+    if (wave >= GT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = tid + 256 * i;  // (row, 16-byte chunk) of the 128 x 8 tile
-            const int r = item >> 3, c = item & 7;
-            if (r < M)
-                xr[i] = *(const uint4*)(a.x + (int64_t)tokrow[r] * a.H + (int64_t)g * 64 + 8 * c);
-            else
-                xr[i] = make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_x = [&](int buf, int g, const uint4 (&xr)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = tid + 256 * i;
-            const int r = item >> 3, c = item & 7;
-            if (r < Mp) xs_raw[buf][r * XS_STRIDE + c] = xr[i];
-        }
-        if (tid < Mp) xsum_raw[buf][tid] = tid < M ? a.w.xsum[(int64_t)tokrow[tid] * G + g] : 0.f;
-    };
-
-    floatx16 acc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-
-    uint4 xr[4];
-    load_x(0, xr);
-    uint4 bw = *(const uint4*)wrow;
-    uint16_t sv = srow[0], bv = brow[0];
-    store_x(0, 0, xr);
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        uint4 bw_next = bw;
-        uint16_t sv_next = sv, bv_next = bv;
-        if (g + 1 < G) {
-            load_x(g + 1, xr);
-            bw_next = *(const uint4*)(wrow + (int64_t)(g + 1) * 8);
-            sv_next = srow[g + 1];
-            bv_next = brow[g + 1];
-        }
-        floatx16 P[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) P[mb][i] = 0.f;
-        const uint32_t wv[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 bfrag = codes_to_16(wv[st], magic);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                if (mb < nmb) {
-                    const uint4 afrag = xs_raw[buf][(32 * mb + l32) * XS_STRIDE + 4 * h + st];
-                    P[mb] = mfma16<F16>(afrag, bfrag, P[mb]);
-                }
-            }
-        }
-        const float sf = h2f(sv);
-        const float bf = h2f(bv) - offset * sf;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            if (mb < nmb) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 xb = *(const float4*)(&xsum_raw[buf][32 * mb + 8 * j + 4 * h]);
-                    acc[mb][4 * j + 0] = fmaf(bf, xb.x, fmaf(sf, P[mb][4 * j + 0], acc[mb][4 * j + 0]));
-                    acc[mb][4 * j + 1] = fmaf(bf, xb.y, fmaf(sf, P[mb][4 * j + 1], acc[mb][4 * j + 1]));
-                    acc[mb][4 * j + 2] = fmaf(bf, xb.z, fmaf(sf, P[mb][4 * j + 2], acc[mb][4 * j + 2]));
-                    acc[mb][4 * j + 3] = fmaf(bf, xb.w, fmaf(sf, P[mb][4 * j + 3], acc[mb][4 * j + 3]));
-                }
-            }
-        }
-        if (g + 1 < G) store_x(buf ^ 1, g + 1, xr);
-        __syncthreads();
-        bw = bw_next;
-        sv = sv_next;
-        bv = bv_next;
-    }
-
-    // up rows (waves 2, 3) -> LDS; gate rows (waves 0, 1) combine in place
-    const int c = 32 * (wave & 1) + l32;
-    if (wave >= 2) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-            if (mb < nmb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    zb[32 * mb + 8 * (i / 4) + 4 * h + (i % 4)][c] = acc[mb][i];
+        for (int i = 0; i < 16; ++i) zb[wave - GT][8 * (i / 4) + 4 * h + (i % 4)][l32] = acc[i];
     }
     __syncthreads();
-    if (wave < 2) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-            if (mb < nmb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 32 * mb + 8 * (i / 4) + 4 * h + (i % 4);
-                    float gl;
-                    const float u = acc[mb][i];
-                    if (a.act == 1) {
-                        const float cc = 0.7978845608028654f;
-                        gl = 0.5f * u * (1.f + tanhf(cc * (u + 0.044715f * u * u * u)));
-                    } else {
-                        gl = 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
-                    }
-                    zb[r][c] = r < M ? prow[r] * gl * zb[r][c] : 0.f;
-                }
-    }
-    __syncthreads();
-    // bf16 hi/lo split and per-group row sums of h'
+    if (wave >= GT || GT * q + wave >= ntl) return;
     uint16_t* dhi = shared ? a.w.shhi : a.w.hhi;
     uint16_t* dlo = shared ? a.w.shlo : a.w.hlo;
-    float* dsum = shared ? a.w.shsum : a.w.hsum;
-    for (int item = tid; item < M * 16; item += 256) {
-        const int r = item >> 4, c4 = (item & 15) * 4;
-        uint16_t hi[4], lo[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v = zb[r][c4 + i];
-            hi[i] = f2bf_rne(v);
-            lo[i] = f2bf_rne(v - bf2f_bits(hi[i]));
-        }
-        const int64_t o = (int64_t)(rb + r) * Iw + 64 * nt + c4;
-        *(uint2*)(dhi + o) = make_uint2(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]));
-        *(uint2*)(dlo + o) = make_uint2(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]));
-    }
-    if (tid < M) {
-        float s = 0.f;
-        for (int cc = 0; cc < 64; ++cc) {
-            const float v = zb[tid][cc];
+    for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i / 4) + 4 * h + (i % 4);
+        if (r < M) {
+            const float u = acc[i];
+            float gl;
+            if (a.act == 1) {
+                const float cc = 0.7978845608028654f;
+                gl = 0.5f * u * (1.f + tanhf(cc * (u + 0.044715f * u * u * u)));
+            } else {
+                gl = 0.5f * u * (1.f + erff(u * 0.7071067811865476f));
+            }
+            const float pw = shared ? 1.f : a.p[a.w.sorted_pair[row0 + r]];
+            const float v = pw * gl * zb[wave][r][l32];
             const uint16_t hi = f2bf_rne(v);
             const uint16_t lo = f2bf_rne(v - bf2f_bits(hi));
-            s += bf2f_bits(hi) + bf2f_bits(lo);
+            const int64_t o = (int64_t)(row0 + r) * Iw + 32 * tile + l32;
+            dhi[o] = hi;
+            dlo[o] = lo;
         }
-        dsum[(int64_t)(rb + tid) * (Iw / 64) + nt] = s;
     }
 }
 
@@ -393,159 +554,72 @@ struct DnArgs {
     const uint32_t *dn_q, *sdn_q;
     const uint16_t *dn_s, *dn_b, *sdn_s, *sdn_b;
     int E, H, I, Is, T;
+    int rbmax;
     PrefillWs w;
 };
 
-__global__ __launch_bounds__(256) void moe_dn_kernel(DnArgs a) {
-    __shared__ __align__(16) uint4 hs_raw[2][2][128 * XS_STRIDE];   // [buf][hi, lo]
-    __shared__ __align__(16) float hsum_raw[2][128];
-    const int ntH = (a.H + 127) / 128;
-    const bool shared = (int)blockIdx.x >= a.E * ntH;
-    int e = 0, nt, rb, M, K;
+// Workgroup = (32-row block, 32 NW columns of H); wave w takes columns
+// 32 NW o + 32 w + (0..31). The activation h' arrives as bf16 hi + lo planes,
+// so each step runs two MFMAs against the same codes.
+__global__ __launch_bounds__(64 * DN_WAVES) __attribute__((amdgpu_waves_per_eu(XWPE, XWPE))) void moe_dn_kernel(DnArgs a) {
+    constexpr int NW = DN_WAVES;
+    __shared__ __align__(16) uint4 lds[XStage<2, false, NW>::LDS_UINT4];
+    const int ntH = (a.H + 32 * NW - 1) / (32 * NW);
+    const int item = blockIdx.x;
+    const int rbi = item / ntH, o8 = item - rbi * ntH;
+    const int R = a.w.rbs[a.E];
+    const int4 info = a.w.rbinfo[min(rbi, a.rbmax - 1)];   // speculative, as in gate+up
+    const int items = (R + (a.T + 31) / 32) * ntH;
+    if (item >= items) return;
+    const bool shared = rbi >= R;
+    int row0, M, K;
     const uint32_t* Wq;
-    const uint16_t *Ws, *Wb;
-    const uint16_t *Ahi, *Alo;
-    const float* Asum;
+    const uint16_t *Ws, *Wb, *Ahi, *Alo;
     float* Out;
     if (!shared) {
-        e = blockIdx.x / ntH;
-        nt = blockIdx.x - e * ntH;
-        rb = a.w.offs[e];
-        M = a.w.offs[e + 1] - rb;
+        const int e = info.x;
+        row0 = info.y;
+        M = info.z;
         K = a.I;
         Wq = a.dn_q + (int64_t)e * a.H * (a.I / 8);
         Ws = a.dn_s + (int64_t)e * a.H * (a.I / 64);
         Wb = a.dn_b + (int64_t)e * a.H * (a.I / 64);
         Ahi = a.w.hhi;
         Alo = a.w.hlo;
-        Asum = a.w.hsum;
         Out = a.w.O;
     } else {
-        nt = blockIdx.x - a.E * ntH;
-        rb = 0;
-        M = a.T;
+        row0 = 32 * (rbi - R);
+        M = min(32, a.T - row0);
         K = a.Is;
         Wq = a.sdn_q;
         Ws = a.sdn_s;
         Wb = a.sdn_b;
         Ahi = a.w.shhi;
         Alo = a.w.shlo;
-        Asum = a.w.shsum;
         Out = a.w.Os;
     }
-    if (M <= 0) return;
-    const int nmb = (M + 31) / 32;
-    const int Mp = nmb * 32;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     const int G = K / 64;
-    const int64_t wpr = K / 8;
-    const int n = 128 * nt + 32 * wave + l32;
+    const int n = 32 * NW * o8 + 32 * wave + l32;
     const int nc = min(n, a.H - 1);
-    const uint32_t* wrow = Wq + (int64_t)nc * wpr + 4 * h;
-    const uint16_t* srow = Ws + (int64_t)nc * G;
-    const uint16_t* brow = Wb + (int64_t)nc * G;
+    CodeRing<XD> ring;
+    ring.init(Wq + (int64_t)nc * (K / 8) + 4 * h, Ws + (int64_t)nc * G, Wb + (int64_t)nc * G, G);
+    const int64_t sro = (int64_t)(row0 + min(tid / (NW * 2), M - 1)) * K;
+    const uint16_t* const arow[2] = {Ahi + sro, Alo + sro};
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, 128.f, acc);
 
-    auto load_a = [&](int g, uint4 (&ar)[2][4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = tid + 256 * i;
-            const int r = item >> 3, c = item & 7;
-            if (r < M) {
-                const int64_t o = (int64_t)(rb + r) * K + (int64_t)g * 64 + 8 * c;
-                ar[0][i] = *(const uint4*)(Ahi + o);
-                ar[1][i] = *(const uint4*)(Alo + o);
-            } else {
-                ar[0][i] = make_uint4(0, 0, 0, 0);
-                ar[1][i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_a = [&](int buf, int g, const uint4 (&ar)[2][4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int item = tid + 256 * i;
-            const int r = item >> 3, c = item & 7;
-            if (r < Mp) {
-                hs_raw[buf][0][r * XS_STRIDE + c] = ar[0][i];
-                hs_raw[buf][1][r * XS_STRIDE + c] = ar[1][i];
-            }
-        }
-        if (tid < Mp) hsum_raw[buf][tid] = tid < M ? Asum[(int64_t)(rb + tid) * G + g] : 0.f;
-    };
-
-    floatx16 acc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-
-    uint4 ar[2][4];
-    load_a(0, ar);
-    uint4 bw = *(const uint4*)wrow;
-    uint16_t sv = srow[0], bv = brow[0];
-    store_a(0, 0, ar);
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        uint4 bw_next = bw;
-        uint16_t sv_next = sv, bv_next = bv;
-        if (g + 1 < G) {
-            load_a(g + 1, ar);
-            bw_next = *(const uint4*)(wrow + (int64_t)(g + 1) * 8);
-            sv_next = srow[g + 1];
-            bv_next = brow[g + 1];
-        }
-        floatx16 P[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) P[mb][i] = 0.f;
-        const uint32_t wv[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const uint4 bfrag = codes_to_16(wv[st], 0x43004300u);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                if (mb < nmb) {
-                    const int ai = (32 * mb + l32) * XS_STRIDE + 4 * h + st;
-                    P[mb] = mfma16<false>(hs_raw[buf][0][ai], bfrag, P[mb]);
-                    P[mb] = mfma16<false>(hs_raw[buf][1][ai], bfrag, P[mb]);
-                }
-            }
-        }
-        const float sf = h2f(sv);
-        const float bf = h2f(bv) - 128.f * sf;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            if (mb < nmb) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 xb = *(const float4*)(&hsum_raw[buf][32 * mb + 8 * j + 4 * h]);
-                    acc[mb][4 * j + 0] = fmaf(bf, xb.x, fmaf(sf, P[mb][4 * j + 0], acc[mb][4 * j + 0]));
-                    acc[mb][4 * j + 1] = fmaf(bf, xb.y, fmaf(sf, P[mb][4 * j + 1], acc[mb][4 * j + 1]));
-                    acc[mb][4 * j + 2] = fmaf(bf, xb.z, fmaf(sf, P[mb][4 * j + 2], acc[mb][4 * j + 2]));
-                    acc[mb][4 * j + 3] = fmaf(bf, xb.w, fmaf(sf, P[mb][4 * j + 3], acc[mb][4 * j + 3]));
-                }
-            }
-        }
-        if (g + 1 < G) store_a(buf ^ 1, g + 1, ar);
-        __syncthreads();
-        bw = bw_next;
-        sv = sv_next;
-        bv = bv_next;
-    }
     if (n < a.H) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-            if (mb < nmb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 32 * mb + 8 * (i / 4) + 4 * h + (i % 4);
-                    if (r < M) Out[(int64_t)(rb + r) * a.H + n] = acc[mb][i];
-                }
+        for (int i = 0; i < 16; ++i) {
+            const int r = 8 * (i / 4) + 4 * h + (i % 4);
+            if (r < M) Out[(int64_t)(row0 + r) * a.H + n] = acc[i];
+        }
     }
 }
 
@@ -568,10 +642,16 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const PrefillWs w, int
 hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float* wts, int T, int k,
                               const void* x, int xkind, float* y, void* ws, hipStream_t st) {
     if (T * k > PREP_MAX_PAIRS || m.E > PREP_MAX_E || T > 128) return hipErrorInvalidValue;
+    if (m.I % 32 != 0 || m.Is % 32 != 0) return hipErrorInvalidValue;
     const PrefillWs w = carve(ws, m, T, k, nullptr);
-    hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(1024), 0, st, idx, T, k, m.E, x, xkind, m.H, w);
+    hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(1024), 0, st, idx, T, k, m.E, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+
+    // grids cover the most row blocks the routing can produce; workgroups
+    // past the actual count (known on the device) leave at once
+    const int rb_max = max_row_blocks(T * k, m.E);
+    const int rb_shared = (T + 31) / 32;
 
     GuArgs ga{};
     ga.gu_q = m.gu_q;
@@ -589,12 +669,14 @@ hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float*
     ga.k = k;
     ga.T = T;
     ga.act = m.act;
+    ga.rbmax = rb_max;
     ga.w = w;
-    const int gu_items = m.E * (m.I / 64) + m.Is / 64;
+    constexpr int GT = GU_WAVES / 2;
+    const int gu_items = rb_max * ((m.I / 32 + GT - 1) / GT) + rb_shared * ((m.Is / 32 + GT - 1) / GT);
     if (xkind == X_F16)
-        hipLaunchKernelGGL(moe_gu_kernel<true>, dim3(gu_items), dim3(256), 0, st, ga);
+        hipLaunchKernelGGL(moe_gu_kernel<true>, dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
     else
-        hipLaunchKernelGGL(moe_gu_kernel<false>, dim3(gu_items), dim3(256), 0, st, ga);
+        hipLaunchKernelGGL(moe_gu_kernel<false>, dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -610,9 +692,10 @@ hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float*
     da.I = m.I;
     da.Is = m.Is;
     da.T = T;
+    da.rbmax = rb_max;
     da.w = w;
-    const int ntH = (m.H + 127) / 128;
-    hipLaunchKernelGGL(moe_dn_kernel, dim3(m.E * ntH + ntH), dim3(256), 0, st, da);
+    const int ntH = (m.H + 32 * DN_WAVES - 1) / (32 * DN_WAVES);
+    hipLaunchKernelGGL(moe_dn_kernel, dim3((rb_max + rb_shared) * ntH), dim3(64 * DN_WAVES), 0, st, da);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
