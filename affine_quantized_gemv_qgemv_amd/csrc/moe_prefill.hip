@@ -375,35 +375,50 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
         const uint4* xs = lds + opaque_i(buf * XS::BUF + l32 * XS_STRIDE + 4 * h);
         // row sums in the accumulator layout: rows 8 q + 4 h + (0..3) of group gi
         const float* xt = xsum_raw + opaque_i(XS::SUMS + buf * 32 * XSG + 4 * h);
-        static_for<0, XSG>([&](auto gic) __attribute__((always_inline)) {
-            constexpr int gi = decltype(gic)::value;
-            constexpr int d = sj * XSG + gi;
-            const int g = st * XSG + gi;
+        // groups in pairs: two independent MFMA chains interleave on the matrix
+        // core (one chain alone would wait on each MFMA's result)
+        static_for<0, XSG / 2>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int g0i = 2 * decltype(pc)::value;
+            constexpr int d0 = sj * XSG + g0i, d1 = d0 + 1;
+            const int g = st * XSG + g0i;
             if (chk && g >= G) return;
-            floatx16 P;
+            const bool second = !chk || g + 1 < G;   // uniform
+            floatx16 P0, P1;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) P[i] = 0.f;
-            const uint32_t wv[4] = {ring.q[d].x, ring.q[d].y, ring.q[d].z, ring.q[d].w};
+            for (int i = 0; i < 16; ++i) {
+                P0[i] = 0.f;
+                P1[i] = 0.f;
+            }
+            const uint32_t w0[4] = {ring.q[d0].x, ring.q[d0].y, ring.q[d0].z, ring.q[d0].w};
+            const uint32_t w1[4] = {ring.q[d1].x, ring.q[d1].y, ring.q[d1].z, ring.q[d1].w};
 #pragma unroll
             for (int stp = 0; stp < 4; ++stp) {
-                const uint4 bfrag = codes_to_16p(wv[stp], magic);
+                const uint4 b0 = codes_to_16p(w0[stp], magic);
+                const uint4 b1 = codes_to_16p(w1[stp], magic);
 #pragma unroll
-                for (int pl = 0; pl < PLANES; ++pl)
-                    P = mfma16<F16>(xs[pl * XS::PER + gi * 32 * XS_STRIDE + stp], bfrag, P);
+                for (int pl = 0; pl < PLANES; ++pl) {
+                    P0 = mfma16<F16>(xs[pl * XS::PER + g0i * 32 * XS_STRIDE + stp], b0, P0);
+                    P1 = mfma16<F16>(xs[pl * XS::PER + (g0i + 1) * 32 * XS_STRIDE + stp], b1, P1);
+                }
             }
-            const float sf = h2f((uint16_t)ring.s[d]);
-            const float mo = -off * sf;
-            // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
+            auto epilogue = [&](const floatx16& P, int gi, int d) __attribute__((always_inline)) {
+                const float sf = h2f((uint16_t)ring.s[d]);
+                const float mo = -off * sf;
+                // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
 #pragma unroll
-            for (int qq = 0; qq < NQ; ++qq) {
-                const float4 xq = *(const float4*)(xt + gi * 32 + 8 * qq);
-                acc[4 * qq + 0] = fmaf(sf, P[4 * qq + 0], fmaf(mo, xq.x, acc[4 * qq + 0]));
-                acc[4 * qq + 1] = fmaf(sf, P[4 * qq + 1], fmaf(mo, xq.y, acc[4 * qq + 1]));
-                acc[4 * qq + 2] = fmaf(sf, P[4 * qq + 2], fmaf(mo, xq.z, acc[4 * qq + 2]));
-                acc[4 * qq + 3] = fmaf(sf, P[4 * qq + 3], fmaf(mo, xq.w, acc[4 * qq + 3]));
-            }
+                for (int qq = 0; qq < NQ; ++qq) {
+                    const float4 xq = *(const float4*)(xt + gi * 32 + 8 * qq);
+                    acc[4 * qq + 0] = fmaf(sf, P[4 * qq + 0], fmaf(mo, xq.x, acc[4 * qq + 0]));
+                    acc[4 * qq + 1] = fmaf(sf, P[4 * qq + 1], fmaf(mo, xq.y, acc[4 * qq + 1]));
+                    acc[4 * qq + 2] = fmaf(sf, P[4 * qq + 2], fmaf(mo, xq.z, acc[4 * qq + 2]));
+                    acc[4 * qq + 3] = fmaf(sf, P[4 * qq + 3], fmaf(mo, xq.w, acc[4 * qq + 3]));
+                }
+            };
+            epilogue(P0, g0i, d0);
+            if (second) epilogue(P1, g0i + 1, d1);
             pin(acc);
-            ring.fill(d, g + XD);   // the slot's contents are dead now
+            ring.fill(d0, g + XD);   // the slots' contents are dead now
+            ring.fill(d1, g + 1 + XD);
             __builtin_amdgcn_sched_barrier(0);
         });
         XS::store(lds + (buf ^ 1) * XS::BUF, xsum_raw + (buf ^ 1) * 32 * XSG, xout);
