@@ -288,8 +288,30 @@ Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
     c.nw = 4;
     (void)xf;
     if (nb > 1) {
-        c.r = nb <= 4 ? 2 : 1;
-        c.u = 2;
+        // several activation vectors: more rows per tile, so each staged
+        // activation read from LDS serves more code words, one step per round
+        // (measured on the 70B shapes, K = 8192 and 28672)
+        c.u = 1;
+        c.nw = 8;
+        if (nb <= 4 && K < 16384) {
+            c.lpr = 64;
+            c.r = 2;
+            c.cpl = 2;
+        } else if (nb <= 2) {
+            c.lpr = 32;
+            c.r = 2;
+            c.cpl = 2;
+            c.nw = 16;
+        } else if (nb <= 4) {
+            c.lpr = 32;
+            c.r = 4;
+            c.cpl = 1;
+            c.nw = 16;
+        } else {
+            c.lpr = 32;
+            c.r = 2;
+            c.cpl = 2;
+        }
         return c;
     }
     const bool even = chunks % 128 == 0;   // LPR 64 x CPL 2 covers whole steps
@@ -355,9 +377,23 @@ hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
         }
 #endif
     } else if constexpr (B == 2 || B == 4) {
+        QD_TRY(64, 2, 1, 1, 2) QD_TRY(32, 2, 1, 1, 2) QD_TRY(32, 4, 1, 1, 1)
+#ifdef QD_TUNING
         QD_LPRS(2, 2, 1)
+        if constexpr (BITS == 4 && XF == 0) {
+            QD_LPRS(4, 1, 1) QD_LPRS(4, 2, 1) QD_LPRS(2, 1, 1) QD_LPRS(1, 2, 1) QD_LPRS(1, 4, 1)
+            QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(4, 1, 1) QD_LPRS2(1, 2, 1)
+        }
+#endif
     } else {
+        QD_TRY(32, 2, 1, 1, 2)
+#ifdef QD_TUNING
         QD_LPRS(1, 2, 1)
+        if constexpr (BITS == 4 && XF == 0) {
+            QD_LPRS(2, 1, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1) QD_LPRS(1, 1, 1) QD_LPRS(1, 4, 1)
+            QD_LPRS2(1, 1, 1) QD_LPRS2(2, 1, 1) QD_LPRS2(1, 2, 1) QD_LPRS2(4, 1, 1)
+        }
+#endif
     }
     return hipErrorInvalidConfiguration;
 }
