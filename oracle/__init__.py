@@ -11,6 +11,10 @@ Definitions followed (jeff.news/article/5193, TurboFieldfare; sections
 부분" (internals)): affine 4-bit group-64 weights with an 8-bit router,
 w = s*q + b; top-8 routing with renormalized weights; shared and routed
 expert outputs combined; prefill in chunks of at most 128 tokens.
+Mirai-M and Mirai-L weights follow the uzu page on discuss.pytorch.kr
+(section on model conversion and the Mirai quantization formats): 4-bit
+asymmetric codes with a 4-bit zero point and a bf16 scale per group of 64,
+w = s*(q - z); 8-bit symmetric codes, w = s*q.
 """
 from __future__ import annotations
 
@@ -51,6 +55,8 @@ def _load():
     lib.qo_gelu.argtypes = [ctypes.c_double, ctypes.c_int]
     lib.qo_gelu.restype = ctypes.c_double
     lib.qo_moe_experts.argtypes = [_P, _P, _I64, _I64, _P, _P, ctypes.c_int, _P, _P, _P, _P]
+    lib.qo_mirai_dequant.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _I64, _P]
+    lib.qo_mirai_gemv.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
     lib.qo_set_threads.argtypes = [ctypes.c_int]
     lib.qo_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -135,6 +141,54 @@ def gemv_f16(w, x_bits, rows=None):
 def gemm_chunk(w, x_bits_bf16, rows=None):
     """Prefill chunk: Y[M][N] = X W^T with bf16 activations X[M][K] (raw bits)."""
     return gemv(w, bf16_to_f64(np.atleast_2d(x_bits_bf16)), rows)
+
+
+MIRAI_FMT = {"M": 1, "L": 2}
+
+
+def _mirai_ptrs(w):
+    q, pq = _c(w.wq, np.uint32)
+    s, ps = _c(w.scales, np.uint16)
+    if w.zeros is None:
+        return (q, s), pq, ps, None
+    z, pz = _c(w.zeros, np.uint32)
+    return (q, s, z), pq, ps, pz
+
+
+def mirai_dequant(w) -> np.ndarray:
+    """Dequantized fp64 matrix [N][K] of a ``synth.MiraiWeights``."""
+    out = np.empty((w.N, w.K), dtype=np.float64)
+    keep, pq, ps, pz = _mirai_ptrs(w)
+    _load().qo_mirai_dequant(MIRAI_FMT[w.fmt], pq, ps, pz, w.N, w.K, out.ctypes.data_as(_P))
+    return out
+
+
+def mirai_gemv(w, x, rows=None):
+    """y[T][N] = W x and A = sum_k |w x| for a Mirai-M / Mirai-L matrix and fp64 x[T][K]."""
+    x2, px = _c(np.atleast_2d(x), np.float64)
+    T = x2.shape[0]
+    if x2.shape[1] != w.K:
+        raise ValueError("x has the wrong length")
+    keep, pq, ps, pz = _mirai_ptrs(w)
+    if rows is None:
+        m, pr = w.N, None
+    else:
+        r, pr = _c(rows, np.int64)
+        keep = keep + (r,)
+        if r.size and (r.min() < 0 or r.max() >= w.N):
+            raise ValueError("row out of range")
+        m = r.size
+    y = np.empty((T, m), dtype=np.float64)
+    a = np.empty((T, m), dtype=np.float64)
+    _load().qo_mirai_gemv(MIRAI_FMT[w.fmt], pq, ps, pz, px, T, w.N, w.K, pr, m,
+                          y.ctypes.data_as(_P), a.ctypes.data_as(_P))
+    return y, a
+
+
+def mirai_gemv_x(w, x_bits, x_dtype: str = "f16", rows=None):
+    """Mirai GEMV on fp16 or bf16 activations given as raw bits [T][K]."""
+    xd = f16_to_f64(np.atleast_2d(x_bits)) if x_dtype == "f16" else bf16_to_f64(np.atleast_2d(x_bits))
+    return mirai_gemv(w, xd, rows)
 
 
 def route_topk(logits, k: int):

@@ -49,6 +49,26 @@ def dense(w) -> np.ndarray:
     return s * q + b
 
 
+def mirai_dense(w) -> np.ndarray:
+    """fp64 matrix [N][K] of a synth.MiraiWeights.
+
+    Mirai-M: s * (q - z) with the zero points decoded by the same division
+    route as the codes; Mirai-L: s * q with q the byte read as numpy int8.
+    """
+    G = w.K // 64
+    s = np.repeat(bf16(w.scales), 64, axis=1)
+    if w.fmt == "M":
+        q = codes(4, w.wq, w.K)
+        z = codes(4, w.zeros, G)
+        return s * (q - np.repeat(z, 64, axis=1))
+    q = np.ascontiguousarray(w.wq, dtype=np.uint32).view(np.int8).astype(np.float64)
+    return s * q
+
+
+def mirai_gemv(w, x: np.ndarray) -> np.ndarray:
+    return np.atleast_2d(x) @ mirai_dense(w).T
+
+
 def gemv(w, x: np.ndarray) -> np.ndarray:
     return np.atleast_2d(x) @ dense(w).T
 

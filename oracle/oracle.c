@@ -7,6 +7,9 @@
  *   [TF]   jeff.news/article/5193 (TurboFieldfare running Gemma 4 26B-A4B on
  *          Apple Silicon), sections "성능과 제약" (performance and constraints)
  *          and "내부 구조가 진짜 흥미로운 부분" (internals).
+ *   [uzu]  discuss.pytorch.kr/t/uzu-mac-iphone-llm-apple-silicon-rust/12363
+ *          (uzu, an on-device engine), section "uzu의 모델 변환과 Mirai 양자화
+ *          형식" (model conversion and the Mirai quantization formats).
  * Plain loops, fp64 throughout; OpenMP only splits independent output rows
  * (each row's sum is still taken in ascending k).
  */
@@ -249,4 +252,62 @@ void qo_moe_experts(const qo_moe* w, const double* x, int64_t T, int64_t k,
     free(hh);
     free(o);
     free(oa);
+}
+
+/*
+ * Mirai formats ([uzu] quantization-format section): Mirai-M is asymmetric
+ * 4-bit integer quantization with a 4-bit zero point and a bf16 scale per
+ * group of 64 inputs; Mirai-L is symmetric 8-bit quantization.
+ * Readings where the page is silent:
+ *   - Mirai-M: w = s * (q - z), q and z in [0, 15]. The zero points are
+ *     packed the way codes are, eight per uint32 along the groups of a row,
+ *     LSB-first, each row padded to whole words: zp[N][ceil(G/8)]; padding
+ *     nibbles carry no meaning.
+ *   - Mirai-L: codes are two's-complement signed bytes packed as the 8-bit
+ *     codes are; one bf16 scale per group of 64 (the group size and scale
+ *     type of the sibling format); w = s * q.
+ */
+static double mirai_weight(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_t* zp,
+                           int64_t K, int64_t n, int64_t k) {
+    const int64_t groups = K / 64;
+    const int64_t grp = k / 64;
+    double sc = qo_bf16_to_f64(s[n * groups + grp]);
+    if (fmt == QO_MIRAI_M) {
+        int64_t zwords = (groups + 7) / 8;
+        int q = qo_code(4, wq + n * (K / 8), k);
+        int z = qo_code(4, zp + n * zwords, grp);
+        return sc * (double)(q - z);
+    }
+    int u = qo_code(8, wq + n * (K / 4), k);
+    int q = u >= 128 ? u - 256 : u;
+    return sc * (double)q;
+}
+
+void qo_mirai_dequant(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_t* zp,
+                      int64_t N, int64_t K, double* w) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) w[n * K + k] = mirai_weight(fmt, wq, s, zp, K, n, k);
+}
+
+void qo_mirai_gemv(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_t* zp,
+                   const double* x, int64_t T, int64_t N, int64_t K,
+                   const int64_t* rows, int64_t nrows, double* y, double* a) {
+    int nt = qo_get_threads();
+    (void)nt;
+    int64_t m = rows ? nrows : N;
+    for (int64_t t = 0; t < T; ++t) {
+        const double* xt = x + t * K;
+#pragma omp parallel for schedule(static) num_threads(nt)
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t n = rows ? rows[i] : i;
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double prod = mirai_weight(fmt, wq, s, zp, K, n, k) * xt[k];
+                acc += prod;
+                aacc += fabs(prod);
+            }
+            y[t * m + i] = acc;
+            if (a) a[t * m + i] = aacc;
+        }
+    }
 }

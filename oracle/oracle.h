@@ -19,7 +19,11 @@
  *     routed output are combined): y = sum_j p_j * down_j(GELU(gate_j x)
  *     * up_j x) + down_s(GELU(gate_s x) * up_s x);
  *   - prefill chunk (internals section: prompts run in chunks of at most
- *     128 tokens): Y[m][n] = sum_k w[n][k] * X[m][k].
+ *     128 tokens): Y[m][n] = sum_k w[n][k] * X[m][k];
+ *   - Mirai-M / Mirai-L weights (uzu page on discuss.pytorch.kr, section on
+ *     model conversion and the Mirai quantization formats): 4-bit
+ *     asymmetric with a zero point and a bf16 scale per group of 64, and
+ *     8-bit symmetric.
  *
  * Readings where the pages are silent (nibble order LSB-first; separate
  * fp16 scale and bias arrays [N][K/64]; gate rows before up rows; exact
@@ -75,6 +79,24 @@ typedef struct {
 void qo_moe_experts(const qo_moe* w, const double* x, int64_t T, int64_t k,
                     const int32_t* idx, const double* p, int act,
                     double* y, double* a, double* h, double* hs);
+
+/*
+ * Mirai formats (uzu page, quantization-format section): QO_MIRAI_M = 4-bit
+ * codes q, bf16 scale s and 4-bit zero point z per group of 64,
+ * w = s * (q - z), zp[N][ceil(K/512)] packed eight per word LSB-first;
+ * QO_MIRAI_L = signed 8-bit codes, bf16 scale per group of 64, w = s * q
+ * (zp unused, may be NULL).
+ */
+enum { QO_MIRAI_M = 1, QO_MIRAI_L = 2 };
+
+void qo_mirai_dequant(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_t* zp,
+                      int64_t N, int64_t K, double* w);
+
+/* y[T][m] and a[T][m] = sum_k |w x| for rows[0..nrows) (m = nrows), or all N rows
+ * (m = N) when rows is NULL. */
+void qo_mirai_gemv(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_t* zp,
+                   const double* x, int64_t T, int64_t N, int64_t K,
+                   const int64_t* rows, int64_t nrows, double* y, double* a);
 
 /* Number of OpenMP threads the oracle uses (0 = runtime default). */
 void qo_set_threads(int n);

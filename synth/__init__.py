@@ -20,6 +20,16 @@ Distributions (the workload description the build targets):
     as int4 ones;
   * decode activations fp16(N(0, 1)); prefill activations bf16(N(0, 1)).
 
+Mirai formats (uzu page on discuss.pytorch.kr, section on model conversion
+and the Mirai quantization formats): Mirai-M has 4-bit codes, a bf16 scale
+and a 4-bit zero point per group of 64; Mirai-L has signed 8-bit codes and
+a bf16 scale per group of 64. Drawn as:
+  * Mirai-M scales bf16(U[0.002, 0.02]); zero points uniform in [0, 15],
+    packed eight per uint32 along the groups of a row, rows padded to whole
+    words (the padding nibbles are random too);
+  * Mirai-L scales bf16(U[0.002, 0.02] / 16); codes uniform bytes, so
+    every signed value in [-128, 127] occurs.
+
 Every stream is numpy Generator(PCG64(SeedSequence([cfg, set, tensor]))).
 """
 from __future__ import annotations
@@ -96,6 +106,78 @@ def affine_weights(bits: int, N: int, K: int, cfg: int, set_id: int, tensor_base
     noise = rng(cfg, set_id, tensor_base + T_BIAS).normal(0.0, 1e-3, size=(N, G))
     b16 = (-mid * s16.astype(np.float64) + noise).astype(np.float16)
     return AffineWeights(bits, N, K, wq, s16.view(np.uint16), b16.view(np.uint16))
+
+
+@dataclass
+class MiraiWeights:
+    """Packed Mirai-M ("M") or Mirai-L ("L") matrix [N][K].
+
+    wq: uint32 [N][K/8] (M) or [N][K/4] (L, signed bytes); scales: bf16 bits
+    [N][K/64]; zeros: uint32 [N][ceil(K/512)] (M) or None (L).
+    """
+    fmt: str
+    N: int
+    K: int
+    wq: np.ndarray
+    scales: np.ndarray
+    zeros: np.ndarray | None
+
+    @property
+    def bits(self) -> int:
+        return 4 if self.fmt == "M" else 8
+
+    @property
+    def nbytes(self) -> int:
+        return self.wq.nbytes + self.scales.nbytes + (0 if self.zeros is None else self.zeros.nbytes)
+
+
+def _const_words(N: int, words: int, bits: int, value: int) -> np.ndarray:
+    word = 0
+    for i in range(32 // bits):
+        word |= (value & ((1 << bits) - 1)) << (bits * i)
+    return np.full((N, words), word, dtype=np.uint32)
+
+
+def mirai_weights(fmt: str, N: int, K: int, cfg: int, set_id: int, tensor_base: int = 0,
+                  codes: str = "uniform", const_code: int = 0,
+                  zeros: str = "uniform", const_zero: int = 0) -> MiraiWeights:
+    """Draw one packed Mirai-M / Mirai-L matrix.
+
+    codes: "uniform" or "const" (every code ``const_code``: 0..15 for M,
+    -128..127 for L); zeros (M only): "uniform" or "const" (``const_zero``).
+    """
+    if fmt not in ("M", "L"):
+        raise ValueError("fmt must be 'M' or 'L'")
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 64")
+    bits = 4 if fmt == "M" else 8
+    G = K // GROUP
+    words = K * bits // 32
+    if codes == "uniform":
+        wq = rng(cfg, set_id, tensor_base + T_CODES).integers(0, 2**32, size=(N, words), dtype=np.uint32)
+    elif codes == "const":
+        lo, hi = (0, 15) if fmt == "M" else (-128, 127)
+        if not lo <= const_code <= hi:
+            raise ValueError("const_code out of range")
+        wq = _const_words(N, words, bits, int(const_code))
+    else:
+        raise ValueError(codes)
+    su = rng(cfg, set_id, tensor_base + T_SCALE).uniform(0.002, 0.02, size=(N, G))
+    if fmt == "L":
+        su = su / 16.0
+    sb = f32_to_bf16_bits(su.astype(np.float32))
+    zq = None
+    if fmt == "M":
+        zw = (G + 7) // 8
+        if zeros == "uniform":
+            zq = rng(cfg, set_id, tensor_base + T_BIAS).integers(0, 2**32, size=(N, zw), dtype=np.uint32)
+        elif zeros == "const":
+            if not 0 <= const_zero <= 15:
+                raise ValueError("const_zero out of range")
+            zq = _const_words(N, zw, 4, int(const_zero))
+        else:
+            raise ValueError(zeros)
+    return MiraiWeights(fmt, N, K, wq, sb, zq)
 
 
 def x_f16(T: int, K: int, cfg: int, set_id: int, tensor: int = T_X) -> np.ndarray:

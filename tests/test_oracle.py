@@ -306,3 +306,166 @@ def test_generator_is_deterministic_and_in_range():
     x = synth.x_bf16(4, 256, cfg=1, set_id=0)
     xd = brute.bf16(x)
     assert abs(xd.mean()) < 0.2 and 0.8 < xd.std() < 1.2
+
+
+# ---------------------------------------------------------------- Mirai formats
+# uzu page (discuss.pytorch.kr), section on model conversion and the Mirai
+# quantization formats: Mirai-M = 4-bit asymmetric codes, 4-bit zero point,
+# bf16 scale, group 64; Mirai-L = 8-bit symmetric.
+
+MIRAI_SHAPES = [(1, 64, 1), (3, 128, 2), (5, 704, 3), (4, 1024, 8), (2, 576, 5)]
+
+
+@pytest.mark.parametrize("fmt", ["M", "L"])
+@pytest.mark.parametrize("N,K,T", MIRAI_SHAPES)
+def test_mirai_gemv_matches_bruteforce(fmt, N, K, T):
+    w = synth.mirai_weights(fmt, N, K, cfg=120, set_id=N * 1000 + K + T)
+    xb = synth.x_f16(T, K, cfg=120, set_id=N * 1000 + K + T)
+    y, a = oracle.mirai_gemv_x(w, xb)
+    d = brute.mirai_dense(w)
+    assert np.array_equal(oracle.mirai_dequant(w), d)
+    yb = brute.f16(xb) @ d.T
+    assert np.all(np.abs(y - yb) <= 1e-12 * a + 1e-300)
+    assert np.allclose(a, np.abs(brute.f16(xb)) @ np.abs(d).T, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("fmt", ["M", "L"])
+def test_mirai_gemv_against_exact_rationals(fmt):
+    N, K, T = 3, 192, 2
+    w = synth.mirai_weights(fmt, N, K, cfg=121, set_id=0)
+    xb = synth.x_f16(T, K, cfg=121, set_id=0)
+    y, a = oracle.mirai_gemv_x(w, xb)
+    G = K // 64
+    s = [[Fraction(float(v)) for v in row] for row in brute.bf16(w.scales)]
+    x = [[Fraction(float(v)) for v in row] for row in xb.view(np.float16)]
+    for n in range(N):
+        raw = [int(v) for v in np.ascontiguousarray(w.wq[n]).view(np.uint8)]
+        if fmt == "M":
+            # code k is nibble k of the row's little-endian byte stream
+            q = [(raw[k // 2] >> (4 * (k % 2))) & 15 for k in range(K)]
+            zb = [int(v) for v in np.ascontiguousarray(w.zeros[n]).view(np.uint8)]
+            z = [(zb[g // 2] >> (4 * (g % 2))) & 15 for g in range(G)]
+            wk = [s[n][k // 64] * (q[k] - z[k // 64]) for k in range(K)]
+        else:
+            q = [v - 256 if v >= 128 else v for v in raw]
+            wk = [s[n][k // 64] * q[k] for k in range(K)]
+        for t in range(T):
+            exact = sum(wk[k] * x[t][k] for k in range(K))
+            assert abs(float(exact) - y[t, n]) <= 4 * K * 2.0 ** -53 * a[t, n]
+
+
+def test_mirai_m_explicit_decode():
+    # one row, K = 512 (8 groups): codes all 15, zero point of group g is g
+    K = 512
+    w = synth.MiraiWeights("M", 1, K, np.full((1, K // 8), 0xFFFFFFFF, np.uint32),
+                           np.full((1, 8), 0x3F80, np.uint16),           # bf16 1.0
+                           np.array([[0x76543210]], np.uint32))
+    d = oracle.mirai_dequant(w)
+    assert np.array_equal(d[0], np.repeat(15.0 - np.arange(8), 64))
+    # scale 0.5 (bf16 0x3F00), zero point 8 everywhere, codes k mod 16
+    row = np.array([[0x76543210, 0xFEDCBA98] * (K // 16)], np.uint32)
+    w2 = synth.MiraiWeights("M", 1, K, row, np.full((1, 8), 0x3F00, np.uint16),
+                            np.array([[0x88888888]], np.uint32))
+    assert np.array_equal(oracle.mirai_dequant(w2)[0], 0.5 * (np.arange(K) % 16 - 8))
+
+
+def test_mirai_l_explicit_decode():
+    # bytes FF 01 7F 80 -> -1, 1, 127, -128 (two's complement), scale 2.0 (bf16 0x4000)
+    K = 64
+    w = synth.MiraiWeights("L", 1, K, np.full((1, K // 4), 0x807F01FF, np.uint32),
+                           np.array([[0x4000]], np.uint16), None)
+    assert np.array_equal(oracle.mirai_dequant(w)[0], np.tile([-2.0, 2.0, 254.0, -256.0], 16))
+
+
+def test_mirai_m_zero_point_padding_is_ignored():
+    # K = 704: 11 groups, so nibbles 11..15 of the second zero-point word are padding
+    w = synth.mirai_weights("M", 6, 704, cfg=122, set_id=0)
+    xb = synth.x_f16(2, 704, cfg=122, set_id=0)
+    y1, _ = oracle.mirai_gemv_x(w, xb)
+    z2 = w.zeros.copy()
+    z2[:, 1] ^= np.uint32(0xFFFFF000)
+    y2, _ = oracle.mirai_gemv_x(synth.MiraiWeights("M", 6, 704, w.wq, w.scales, z2), xb)
+    assert np.array_equal(y1, y2)
+    z3 = w.zeros.copy()
+    z3[:, 1] ^= np.uint32(0x00000F00)      # group 10's zero point does matter
+    y3, _ = oracle.mirai_gemv_x(synth.MiraiWeights("M", 6, 704, w.wq, w.scales, z3), xb)
+    assert not np.array_equal(y1, y3)
+
+
+def test_mirai_m_equals_affine_with_bias_minus_s_z():
+    # With scales of at most 7 significant bits, s and -s*z are exact in fp16,
+    # so Mirai-M (s, z) is the affine format (s, b = -s*z) weight for weight:
+    # both oracle routes must agree bit for bit.
+    N, K = 9, 1024
+    w = synth.mirai_weights("M", N, K, cfg=123, set_id=0)
+    sb = (w.scales & np.uint16(0xFFFE)).astype(np.uint16)
+    w = synth.MiraiWeights("M", N, K, w.wq, sb, w.zeros)
+    s = brute.bf16(sb)
+    z = brute.codes(4, w.zeros, K // 64).astype(np.float64)
+    s16, b16 = s.astype(np.float16), (-s * z).astype(np.float16)
+    assert np.array_equal(s16.astype(np.float64), s) and np.array_equal(b16.astype(np.float64), -s * z)
+    aw = synth.AffineWeights(4, N, K, w.wq, s16.view(np.uint16), b16.view(np.uint16))
+    xb = synth.x_f16(3, K, cfg=123, set_id=0)
+    ym, am = oracle.mirai_gemv_x(w, xb)
+    ya, aa = oracle.gemv_f16(aw, xb)
+    assert np.array_equal(ym, ya) and np.array_equal(am, aa)
+
+
+def test_mirai_l_equals_affine8_with_offset_codes():
+    # signed byte q = (q XOR 0x80) - 128, so Mirai-L (s) is the affine 8-bit
+    # format with codes XOR 0x80 and bias -128*s (exact in fp16 for bf16 s)
+    N, K = 7, 832
+    w = synth.mirai_weights("L", N, K, cfg=124, set_id=0)
+    s = brute.bf16(w.scales)
+    s16, b16 = s.astype(np.float16), (-128.0 * s).astype(np.float16)
+    assert np.array_equal(s16.astype(np.float64), s) and np.array_equal(b16.astype(np.float64), -128 * s)
+    aw = synth.AffineWeights(8, N, K, w.wq ^ np.uint32(0x80808080), s16.view(np.uint16),
+                             b16.view(np.uint16))
+    xb = synth.x_f16(2, K, cfg=124, set_id=0)
+    ym, _ = oracle.mirai_gemv_x(w, xb)
+    ya, _ = oracle.gemv_f16(aw, xb)
+    assert np.array_equal(ym, ya)
+
+
+def test_mirai_l_is_symmetric():
+    # negating every code (none is -128) negates every output exactly
+    N, K = 5, 512
+    w = synth.mirai_weights("L", N, K, cfg=125, set_id=0)
+    b = np.ascontiguousarray(w.wq).view(np.int8).copy()
+    b[b == -128] = 127
+    wpos = synth.MiraiWeights("L", N, K, b.view(np.uint32), w.scales, None)
+    wneg = synth.MiraiWeights("L", N, K, (-b).view(np.uint32), w.scales, None)
+    xb = synth.x_f16(2, K, cfg=125, set_id=0)
+    yp, _ = oracle.mirai_gemv_x(wpos, xb)
+    yn, _ = oracle.mirai_gemv_x(wneg, xb)
+    assert np.array_equal(yp, -yn)
+
+
+def test_mirai_code_equal_to_zero_point_gives_zero():
+    w = synth.mirai_weights("M", 4, 512, cfg=126, set_id=0, codes="const", const_code=9,
+                            zeros="const", const_zero=9)
+    xb = synth.x_f16(2, 512, cfg=126, set_id=0)
+    y, a = oracle.mirai_gemv_x(w, xb)
+    assert np.all(y == 0.0) and np.all(a == 0.0)
+
+
+def test_mirai_rows_variant_matches_full():
+    w = synth.mirai_weights("M", 40, 704, cfg=127, set_id=0)
+    xb = synth.x_bf16(3, 704, cfg=127, set_id=0)
+    y, a = oracle.mirai_gemv_x(w, xb, "bf16")
+    rows = np.array([0, 7, 39, 13])
+    yr, ar = oracle.mirai_gemv_x(w, xb, "bf16", rows=rows)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(ar, a[:, rows])
+
+
+def test_mirai_generator_ranges():
+    m = synth.mirai_weights("M", 8, 1024, cfg=2, set_id=0)
+    s = brute.bf16(m.scales)
+    assert s.min() >= 0.00199 and s.max() <= 0.0201
+    z = brute.codes(4, m.zeros, 16)
+    assert z.min() == 0 and z.max() == 15
+    el = synth.mirai_weights("L", 8, 1024, cfg=2, set_id=0)
+    q = np.ascontiguousarray(el.wq).view(np.int8)
+    assert q.min() == -128 and q.max() == 127
+    assert brute.bf16(el.scales).max() <= 0.0201 / 16
+    assert m.nbytes == 8 * (512 + 32 + 8)

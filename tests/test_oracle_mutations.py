@@ -39,6 +39,15 @@ MUTATIONS = {
     "gate and up swapped": ("h[i] = qo_gelu(z[i], act) * z[I + i];",
                             "h[i] = qo_gelu(z[I + i], act) * z[i];"),
     "routing weight ignored": ("yt[n] += pj * o[n];", "yt[n] += o[n] + 0.0 * pj;"),
+    "mirai zero point ignored": ("return sc * (double)(q - z);", "return sc * (double)(q - 0 * z);"),
+    "mirai zero point of the wrong group": ("int z = qo_code(4, zp + n * zwords, grp);",
+                                            "int z = qo_code(4, zp + n * zwords, (grp + 1) % groups);"),
+    "mirai zero point added": ("return sc * (double)(q - z);", "return sc * (double)(q + z);"),
+    "mirai scale read as fp16": ("double sc = qo_bf16_to_f64(s[n * groups + grp]);",
+                                 "double sc = qo_f16_to_f64(s[n * groups + grp]);"),
+    "mirai wrong scale group": ("const int64_t grp = k / 64;", "const int64_t grp = (k / 64 + 1) % groups;"),
+    "mirai-l codes unsigned": ("int q = u >= 128 ? u - 256 : u;", "int q = u;"),
+    "mirai-l sign threshold": ("int q = u >= 128 ? u - 256 : u;", "int q = u > 128 ? u - 256 : u;"),
     "shared expert halved": ("yt[n] += o[n];\n            if (at) at[n] += oa[n];\n        }\n    }",
                              "yt[n] += 0.5 * o[n];\n            if (at) at[n] += oa[n];\n        }\n    }"),
 }
@@ -60,6 +69,13 @@ PIN_CALLS = [
     (pins.test_gelu_textbook_values_and_identities, {}),
     (pins.test_moe_block_matches_bruteforce, {"act": 0}),
     (pins.test_moe_identical_experts_do_not_depend_on_routing, {}),
+    (pins.test_mirai_gemv_matches_bruteforce, {"fmt": "M", "N": 5, "K": 704, "T": 3}),
+    (pins.test_mirai_gemv_matches_bruteforce, {"fmt": "L", "N": 4, "K": 1024, "T": 8}),
+    (pins.test_mirai_m_explicit_decode, {}),
+    (pins.test_mirai_l_explicit_decode, {}),
+    (pins.test_mirai_m_equals_affine_with_bias_minus_s_z, {}),
+    (pins.test_mirai_l_equals_affine8_with_offset_codes, {}),
+    (pins.test_mirai_code_equal_to_zero_point_gives_zero, {}),
 ]
 
 
