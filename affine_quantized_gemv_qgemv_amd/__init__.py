@@ -7,7 +7,9 @@ fails, a ``QDecodeError`` is raised.
 
 Tensor conventions (see include/qdecode.h for the full contract):
   * packed codes: int32 (or uint32) tensor [N][K*bits/32], LSB-first codes;
-  * scales / biases: float16 tensors [N][K/64];
+  * scales / biases: float16 tensors [N][K/64] (bfloat16 scales and packed
+    int32 zero points [N][ceil(K/512)] for the Mirai-M format; bfloat16
+    scales and signed byte codes for Mirai-L);
   * activations: float16 (decode) or bfloat16 (prefill) [batch][K];
   * outputs: float32.
 """
@@ -26,8 +28,9 @@ QD_OK, QD_ERR_INVALID_ARGUMENT, QD_ERR_MISALIGNED, QD_ERR_UNSUPPORTED, QD_ERR_WO
 QD_F16, QD_BF16 = 0, 1
 QD_GELU_ERF, QD_GELU_TANH = 0, 1
 
-EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qmoe_route_topk", "qmoe_expert_workspace_bytes",
-           "qmoe_expert_gemv", "qgemm_affine4_chunk", "qd_status_string", "qd_last_error")
+EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qmoe_route_topk",
+           "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
+           "qd_status_string", "qd_last_error")
 
 
 class QDecodeError(RuntimeError):
@@ -63,6 +66,8 @@ def lib() -> ctypes.CDLL:
     gemv_args = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
     L.qgemv_affine4.argtypes = gemv_args
     L.qgemv_affine8.argtypes = gemv_args
+    L.qgemv_mirai_m.argtypes = gemv_args
+    L.qgemv_mirai_l.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
     L.qmoe_route_topk.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P]
     L.qmoe_expert_workspace_bytes.argtypes = [ctypes.POINTER(MoeWeightsC), _I32, _I32]
     L.qmoe_expert_workspace_bytes.restype = ctypes.c_size_t
@@ -73,8 +78,8 @@ def lib() -> ctypes.CDLL:
     L.qd_status_string.restype = ctypes.c_char_p
     L.qd_last_error.argtypes = []
     L.qd_last_error.restype = ctypes.c_char_p
-    for fn in ("qgemv_affine4", "qgemv_affine8", "qmoe_route_topk", "qmoe_expert_gemv",
-               "qgemm_affine4_chunk"):
+    for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
+               "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -155,6 +160,48 @@ def qgemv_affine4(wq, scales, biases, x, out=None):
 def qgemv_affine8(wq, scales, biases, x, out=None):
     """Same with 8-bit codes (router); batch <= 128."""
     return _qgemv(8, wq, scales, biases, x, out)
+
+
+def _mirai(fmt: str, wq, scales, zeros, x, out):
+    bits = 4 if fmt == "M" else 8
+    squeeze = x.dim() == 1
+    x2 = x.unsqueeze(0) if squeeze else x
+    _need(wq, "wq", _CODES, 2)
+    _need(scales, "scales", (torch.bfloat16,), 2)
+    _need(x2, "x", (torch.float16, torch.bfloat16), 2)
+    N = wq.shape[0]
+    K = wq.shape[1] * (32 // bits)
+    batch = x2.shape[0]
+    if x2.shape[1] != K:
+        raise ValueError(f"x has {x2.shape[1]} columns, the codes imply K = {K}")
+    if tuple(scales.shape) != (N, K // 64):
+        raise ValueError("scales must be [N][K/64]")
+    if fmt == "M":
+        _need(zeros, "zeros", _CODES, 2)
+        if tuple(zeros.shape) != (N, (K // 64 + 7) // 8):
+            raise ValueError("zeros must be [N][ceil(K/512)]")
+    if out is None:
+        out = torch.empty((batch, N), dtype=torch.float32, device=x2.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (batch, N):
+        raise ValueError("out must be [batch][N]")
+    if fmt == "M":
+        _check(lib().qgemv_mirai_m(_ptr(wq), _ptr(scales), _ptr(zeros), _ptr(x2), _x_dtype(x2),
+                                   _ptr(out), N, K, batch, 64, _stream()))
+    else:
+        _check(lib().qgemv_mirai_l(_ptr(wq), _ptr(scales), _ptr(x2), _x_dtype(x2), _ptr(out), N, K,
+                                   batch, 64, _stream()))
+    return out[0] if squeeze else out
+
+
+def qgemv_mirai_m(wq, scales, zeros, x, out=None):
+    """y[b][n] = sum_k s*(q - z) x[b][k]: 4-bit codes, bf16 scales, packed 4-bit zero points."""
+    return _mirai("M", wq, scales, zeros, x, out)
+
+
+def qgemv_mirai_l(wq, scales, x, out=None):
+    """y[b][n] = sum_k s*q x[b][k]: signed 8-bit codes, bf16 scales; batch <= 8."""
+    return _mirai("L", wq, scales, None, x, out)
 
 
 def qmoe_route_topk(logits, k: int, idx=None, weights=None):

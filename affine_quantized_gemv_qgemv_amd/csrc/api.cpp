@@ -60,10 +60,11 @@ qd_status check_matrix(const char* fn, int32_t N, int32_t K, int32_t group_size)
     return QD_OK;
 }
 
-qd_status gemv_common(const char* fn, int bits, int max_batch, const uint32_t* wq,
-                      const uint16_t* scales, const uint16_t* biases, const uint16_t* x,
-                      qd_dtype x_dtype, float* y, int32_t N, int32_t K, int32_t batch,
-                      int32_t group_size, qd_stream stream) {
+// fmt: 0 = affine (biases), 1 = Mirai-M (zeros), 2 = Mirai-L (neither).
+qd_status gemv_common(const char* fn, int bits, int fmt, int max_batch, const uint32_t* wq,
+                      const uint16_t* scales, const uint16_t* biases, const uint32_t* zeros,
+                      const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
+                      int32_t batch, int32_t group_size, qd_stream stream) {
     qd_status st = check_matrix(fn, N, K, group_size);
     if (st != QD_OK) return st;
     if (batch < 1 || batch > max_batch)
@@ -73,12 +74,13 @@ qd_status gemv_common(const char* fn, int bits, int max_batch, const uint32_t* w
         return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
     CHECK_PTR(wq);
     CHECK_PTR(scales);
-    CHECK_PTR(biases);
+    if (fmt == 0) CHECK_PTR(biases);
+    if (fmt == 1) CHECK_PTR(zeros);
     CHECK_PTR(x);
     CHECK_PTR(y);
     const int xkind = x_dtype == QD_F16 ? 0 : 1;
-    return from_hip(qd::launch_gemv(bits, wq, scales, biases, x, xkind, y, N, K, batch,
-                                    (hipStream_t)stream),
+    return from_hip(qd::launch_gemv(bits, fmt, wq, scales, biases, zeros, x, xkind, y, N, K,
+                                    batch, (hipStream_t)stream),
                     fn);
 }
 
@@ -195,15 +197,29 @@ extern "C" {
 qd_status qgemv_affine4(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                         const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
                         int32_t batch, int32_t group_size, qd_stream stream) {
-    return gemv_common("qgemv_affine4", 4, 8, wq, scales, biases, x, x_dtype, y, N, K, batch,
-                       group_size, stream);
+    return gemv_common("qgemv_affine4", 4, 0, 8, wq, scales, biases, nullptr, x, x_dtype, y, N, K,
+                       batch, group_size, stream);
 }
 
 qd_status qgemv_affine8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                         const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
                         int32_t batch, int32_t group_size, qd_stream stream) {
-    return gemv_common("qgemv_affine8", 8, 128, wq, scales, biases, x, x_dtype, y, N, K, batch,
-                       group_size, stream);
+    return gemv_common("qgemv_affine8", 8, 0, 128, wq, scales, biases, nullptr, x, x_dtype, y, N,
+                       K, batch, group_size, stream);
+}
+
+qd_status qgemv_mirai_m(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                        const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
+                        int32_t batch, int32_t group_size, qd_stream stream) {
+    return gemv_common("qgemv_mirai_m", 4, 1, 8, wq, scales, nullptr, zeros, x, x_dtype, y, N, K,
+                       batch, group_size, stream);
+}
+
+qd_status qgemv_mirai_l(const uint32_t* wq, const uint16_t* scales, const uint16_t* x,
+                        qd_dtype x_dtype, float* y, int32_t N, int32_t K, int32_t batch,
+                        int32_t group_size, qd_stream stream) {
+    return gemv_common("qgemv_mirai_l", 8, 2, 8, wq, scales, nullptr, nullptr, x, x_dtype, y, N, K,
+                       batch, group_size, stream);
 }
 
 qd_status qmoe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* idx,

@@ -20,6 +20,18 @@
 //  * When the staged activations would not fit LDS, the chunk range is split
 //    across a second grid dimension and the partial rows are added into a
 //    zeroed y with fp32 atomics.
+//
+// Weight formats (template parameter FMT); all reduce to the per-group
+// epilogue y += s * sum(u x) + c * sum(x) with unsigned codes u:
+//  * W_AFFINE: MLX affine (above), fp16 s and c = fp16 b.
+//  * W_MIRAI_M and W_MIRAI_L, from discuss.pytorch.kr/t/uzu-mac-iphone-llm-
+//    apple-silicon-rust/12363 (uzu), section "uzu의 모델 변환과 Mirai 양자화
+//    형식" (model conversion and the Mirai quantization formats): Mirai-M has
+//    4-bit codes with a 4-bit zero point z and a bf16 scale per group of 64,
+//    w = s (q - z), so c = -s z (exact in fp32: 8 x 4 significant bits);
+//    the zero points are packed eight per uint32 along a row's groups.
+//    Mirai-L has signed 8-bit codes and a bf16 scale per group, w = s q;
+//    flipping each code's top bit gives u = q + 128, so c = -128 s.
 #include "common.h"
 #include "launch.h"
 
@@ -37,17 +49,21 @@ struct GemvArgs {
     int chunks_split;    // chunks per K split (grid dimension y)
     int atomic_out;
     int interleave;      // tile order: 1 = wave w takes tiles w, w + W, ...; 0 = a contiguous block
+    const uint8_t* zp;   // Mirai-M zero points, zstride bytes per row
+    int zstride;
 };
+
+enum WFmt : int { W_AFFINE = 0, W_MIRAI_M = 1, W_MIRAI_L = 2 };
 
 // One round of loads: U steps of R rows; a step gives each lane CPL
 // consecutive 16-byte chunks of one group.
 template <int R, int U, int CPL>
 struct Round {
     uint4 cw[U][CPL][R];
-    uint16_t sc[U][R], bi[U][R];   // raw fp16 bits; masked when consumed
+    uint16_t sc[U][R], bi[U][R];   // raw scale / bias (or zero-point byte) bits; masked when consumed
 };
 
-template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL>
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL, int FMT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
     GemvArgs a) {
     extern __shared__ uint4 lds[];
@@ -107,7 +123,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
                         *(const uint4*)(a.wq + (int64_t)rc * wpr + (int64_t)(gc + ch) * 4);
                 const int64_t gi = (int64_t)rc * G + gc / CPG;
                 buf.sc[u][r] = a.s[gi];
-                buf.bi[u][r] = a.b[gi];
+                if constexpr (FMT == W_AFFINE)
+                    buf.bi[u][r] = a.b[gi];
+                else if constexpr (FMT == W_MIRAI_M)   // byte holding groups 2j, 2j + 1
+                    buf.bi[u][r] = a.zp[(int64_t)rc * a.zstride + (gc / CPG) / 2];
             }
         }
     };
@@ -132,13 +151,36 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const bool ok = (cu < nc) && (tile * ROWS + r * RPI + seg < a.N);
-                sc[r] = ok ? h2f(buf.sc[u][r]) : 0.f;
-                bi[r] = ok ? h2f(buf.bi[u][r]) : 0.f;
+                if constexpr (FMT == W_AFFINE) {
+                    sc[r] = ok ? h2f(buf.sc[u][r]) : 0.f;
+                    bi[r] = ok ? h2f(buf.bi[u][r]) : 0.f;
+                } else if constexpr (FMT == W_MIRAI_M) {
+                    const int zsh = (((c0 + c) / CPG) & 1) * 4;
+                    const float z = (float)((buf.bi[u][r] >> zsh) & 15u);
+                    sc[r] = ok ? bf2f(buf.sc[u][r]) : 0.f;
+                    bi[r] = -sc[r] * z;
+                } else {
+                    sc[r] = ok ? bf2f(buf.sc[u][r]) : 0.f;
+                    bi[r] = -128.f * sc[r];
+                }
             }
             int slot[CPL];
 #pragma unroll
             for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, nc);
-            group_rows<BITS, XF, B, R, CPL>(buf.cw[u], sc, bi, lds, a.nb, nc, slot, magic, y);
+            if constexpr (FMT == W_MIRAI_L) {
+                uint4 cw[CPL][R];   // signed bytes -> offset-128 unsigned codes
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint4 v = buf.cw[u][ch][r];
+                        cw[ch][r] = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u,
+                                               v.z ^ 0x80808080u, v.w ^ 0x80808080u);
+                    }
+                group_rows<BITS, XF, B, R, CPL>(cw, sc, bi, lds, a.nb, nc, slot, magic, y);
+            } else {
+                group_rows<BITS, XF, B, R, CPL>(buf.cw[u], sc, bi, lds, a.nb, nc, slot, magic, y);
+            }
         }
         if (sg == RPT - 1) {
 #pragma unroll
@@ -209,11 +251,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL>
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL, int FMT>
 hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     using St = Stage<BITS, XF>;
     const DeviceInfo& dev = device_info();
-    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL>;
+    auto kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT>;
     const int C16 = base.K / St::CC;
     // Split the chunk range when the staged activations exceed the LDS budget
     // per workgroup (half the CU's LDS, so two workgroups stay resident).
@@ -356,19 +398,19 @@ Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
 
 #define QD_TRY(LPR_, R_, U_, WPE_, CPL_)                                                  \
     if (c.lpr == LPR_ && c.r == R_ && c.u == U_ && c.wpe == WPE_ && c.cpl == CPL_)         \
-        return run_cfg<BITS, XF, B, LPR_, R_, U_, WPE_, CPL_>(a, c.nw, st);
+        return run_cfg<BITS, XF, B, LPR_, R_, U_, WPE_, CPL_, FMT>(a, c.nw, st);
 #define QD_LPRS(R_, U_, WPE_)                                                    \
     QD_TRY(64, R_, U_, WPE_, 1) QD_TRY(32, R_, U_, WPE_, 1) QD_TRY(16, R_, U_, WPE_, 1) \
     QD_TRY(8, R_, U_, WPE_, 1)
 #define QD_LPRS2(R_, U_, WPE_) QD_TRY(64, R_, U_, WPE_, 2) QD_TRY(32, R_, U_, WPE_, 2)
 
-template <int BITS, int XF, int B>
+template <int BITS, int XF, int B, int FMT>
 hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     if constexpr (B == 1) {
         QD_LPRS(1, 4, 1) QD_LPRS(1, 8, 1)
         QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(1, 4, 1) QD_LPRS2(1, 8, 1)
 #ifdef QD_TUNING
-        if constexpr (BITS == 4 && XF == 0) {
+        if constexpr (BITS == 4 && XF == 0 && FMT == W_AFFINE) {
             QD_LPRS(4, 2, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1)
             QD_LPRS2(4, 1, 1) QD_LPRS2(1, 2, 1) QD_LPRS2(4, 2, 1) QD_LPRS2(2, 4, 1) QD_LPRS2(8, 1, 1)
             QD_LPRS(2, 4, 1) QD_LPRS(8, 1, 1) QD_LPRS(2, 8, 1) QD_LPRS(8, 2, 1)
@@ -379,8 +421,8 @@ hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     } else if constexpr (B == 2 || B == 4) {
         QD_TRY(64, 2, 1, 1, 2) QD_TRY(32, 2, 1, 1, 2) QD_TRY(32, 4, 1, 1, 1)
 #ifdef QD_TUNING
-        QD_LPRS(2, 2, 1)
-        if constexpr (BITS == 4 && XF == 0) {
+        if constexpr (FMT == W_AFFINE) QD_LPRS(2, 2, 1)
+        if constexpr (BITS == 4 && XF == 0 && FMT == W_AFFINE) {
             QD_LPRS(4, 1, 1) QD_LPRS(4, 2, 1) QD_LPRS(2, 1, 1) QD_LPRS(1, 2, 1) QD_LPRS(1, 4, 1)
             QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(4, 1, 1) QD_LPRS2(1, 2, 1)
         }
@@ -388,8 +430,8 @@ hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     } else {
         QD_TRY(32, 2, 1, 1, 2)
 #ifdef QD_TUNING
-        QD_LPRS(1, 2, 1)
-        if constexpr (BITS == 4 && XF == 0) {
+        if constexpr (FMT == W_AFFINE) QD_LPRS(1, 2, 1)
+        if constexpr (BITS == 4 && XF == 0 && FMT == W_AFFINE) {
             QD_LPRS(2, 1, 1) QD_LPRS(2, 2, 1) QD_LPRS(4, 1, 1) QD_LPRS(1, 1, 1) QD_LPRS(1, 4, 1)
             QD_LPRS2(1, 1, 1) QD_LPRS2(2, 1, 1) QD_LPRS2(1, 2, 1) QD_LPRS2(4, 1, 1)
         }
@@ -401,12 +443,12 @@ hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
 #undef QD_LPRS
 #undef QD_TRY
 
-template <int BITS, int XF>
+template <int BITS, int XF, int FMT>
 hipError_t run_batch(const GemvArgs& a, const Cfg& c, hipStream_t st) {
-    if (a.nb <= 1) return run_b<BITS, XF, 1>(a, c, st);
-    if (a.nb <= 2) return run_b<BITS, XF, 2>(a, c, st);
-    if (a.nb <= 4) return run_b<BITS, XF, 4>(a, c, st);
-    return run_b<BITS, XF, 8>(a, c, st);
+    if (a.nb <= 1) return run_b<BITS, XF, 1, FMT>(a, c, st);
+    if (a.nb <= 2) return run_b<BITS, XF, 2, FMT>(a, c, st);
+    if (a.nb <= 4) return run_b<BITS, XF, 4, FMT>(a, c, st);
+    return run_b<BITS, XF, 8, FMT>(a, c, st);
 }
 
 }  // namespace
@@ -417,12 +459,15 @@ hipError_t run_batch(const GemvArgs& a, const Cfg& c, hipStream_t st) {
 extern "C" int qd_tune_gemv[7] = {0, 0, 0, 0, 1, 4, -1};
 #endif
 
-hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                       const void* x, int xkind, float* y, int N, int K, int batch,
-                       hipStream_t st) {
+hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
+                       const uint16_t* b, const uint32_t* zp, const void* x, int xkind, float* y,
+                       int N, int K, int batch, hipStream_t st) {
+    if ((fmt == W_MIRAI_M && bits != 4) || (fmt == W_MIRAI_L && bits != 8) ||
+        (fmt != W_AFFINE && batch > 8))
+        return hipErrorInvalidValue;
     // a chunk of tokens through 8-bit weights (prefill routers): one
     // matrix-core launch instead of slices of 8
-    if (bits == 8 && batch > 8 && (xkind == X_F16 || xkind == X_BF16))
+    if (fmt == W_AFFINE && bits == 8 && batch > 8 && (xkind == X_F16 || xkind == X_BF16))
         return launch_gemm8_tokens(wq, s, b, (const uint16_t*)x, xkind, y, N, K, batch, st);
     for (int b0 = 0; b0 < batch; b0 += 8) {
         GemvArgs a{};
@@ -436,6 +481,8 @@ hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const ui
         a.N = N;
         a.K = K;
         a.nb = std::min(8, batch - b0);
+        a.zp = (const uint8_t*)zp;
+        a.zstride = 4 * ((K / 64 + 7) / 8);
         const int xf = xkind == X_F16 ? 0 : 1;
         Cfg c = default_cfg(bits, xf, a.nb, N, K);
 #ifdef QD_TUNING
@@ -446,10 +493,14 @@ hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const ui
 #endif
         a.interleave = c.il;
         hipError_t e;
-        if (bits == 4)
-            e = xf == 0 ? run_batch<4, 0>(a, c, st) : run_batch<4, 1>(a, c, st);
+        if (fmt == W_MIRAI_M)
+            e = xf == 0 ? run_batch<4, 0, W_MIRAI_M>(a, c, st) : run_batch<4, 1, W_MIRAI_M>(a, c, st);
+        else if (fmt == W_MIRAI_L)
+            e = xf == 0 ? run_batch<8, 0, W_MIRAI_L>(a, c, st) : run_batch<8, 1, W_MIRAI_L>(a, c, st);
+        else if (bits == 4)
+            e = xf == 0 ? run_batch<4, 0, W_AFFINE>(a, c, st) : run_batch<4, 1, W_AFFINE>(a, c, st);
         else
-            e = xf == 0 ? run_batch<8, 0>(a, c, st) : run_batch<8, 1>(a, c, st);
+            e = xf == 0 ? run_batch<8, 0, W_AFFINE>(a, c, st) : run_batch<8, 1, W_AFFINE>(a, c, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

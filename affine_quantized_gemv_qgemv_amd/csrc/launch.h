@@ -25,9 +25,12 @@ int occupancy(const void* func, int threads, size_t lds_bytes);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // x kinds: 0 = fp16 bits, 1 = bf16 bits, 2 = fp32.
-hipError_t launch_gemv(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                       const void* x, int xkind, float* y, int N, int K, int batch,
-                       hipStream_t st);
+// fmt: 0 = affine (fp16 s, b); 1 = Mirai-M (bits 4, bf16 s, zero points zp,
+// b unused); 2 = Mirai-L (bits 8, signed codes, bf16 s, b and zp unused).
+// The Mirai formats take batch <= 8.
+hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
+                       const uint16_t* b, const uint32_t* zp, const void* x, int xkind, float* y,
+                       int N, int K, int batch, hipStream_t st);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              hipStream_t st);

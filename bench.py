@@ -16,6 +16,9 @@ timed on a bounded sample of the same workload.
 
 Other workloads (``--config``): c1 (4096x4096 GEMV), c3 (MoE decode layer),
 c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8).
+``--format mirai-m`` / ``mirai-l`` runs c1, c2 and c5 on the Mirai weight
+formats of the uzu engine (4-bit codes with bf16 scale and 4-bit zero point
+per group of 64; signed 8-bit codes with bf16 scale per group of 64).
 """
 from __future__ import annotations
 
@@ -44,18 +47,27 @@ def parse():
     p.add_argument("--config", default="c2",
                    choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "stream"])
     p.add_argument("--sets", type=int, default=0, help="weight sets cycled (0 = workload default)")
+    p.add_argument("--format", default="affine", choices=["affine", "mirai-m", "mirai-l"],
+                   help="weight format of the dense GEMV workloads (c1, c2, c5)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
 
 
-def matrix_bytes(N: int, K: int, bits: int = 4) -> int:
-    """Algorithmic bytes of one packed matrix: codes + fp16 scale + fp16 bias per group."""
-    return N * K * bits // 8 + 2 * 2 * N * (K // 64)
+def matrix_bytes(N: int, K: int, bits: int = 4, fmt: str = "affine") -> int:
+    """Algorithmic bytes of one packed matrix: codes + per-group parameters
+    (affine: fp16 scale + fp16 bias; Mirai-M: bf16 scale + packed 4-bit zero
+    points, rows padded to whole words; Mirai-L: bf16 scale)."""
+    G = K // 64
+    if fmt == "mirai-m":
+        return N * K // 2 + 2 * N * G + 4 * N * ((G + 7) // 8)
+    if fmt == "mirai-l":
+        return N * K + 2 * N * G
+    return N * K * bits // 8 + 2 * 2 * N * G
 
 
-def gemv_bytes(N: int, K: int, batch: int, bits: int = 4) -> int:
-    return matrix_bytes(N, K, bits) + batch * K * 2 + batch * N * 4
+def gemv_bytes(N: int, K: int, batch: int, bits: int = 4, fmt: str = "affine") -> int:
+    return matrix_bytes(N, K, bits, fmt) + batch * K * 2 + batch * N * 4
 
 
 def source_hash(files) -> str:
@@ -141,8 +153,12 @@ def cpu_baseline_gemv(mats, seconds: float):
     t0 = time.perf_counter()
     while True:
         for w, xb in mats:
-            oracle.gemv_f16(w, xb)
-            nbytes += gemv_bytes(w.N, w.K, xb.shape[0], w.bits)
+            if hasattr(w, "fmt"):
+                oracle.mirai_gemv_x(w, xb)
+                nbytes += gemv_bytes(w.N, w.K, xb.shape[0], fmt="mirai-" + w.fmt.lower())
+            else:
+                oracle.gemv_f16(w, xb)
+                nbytes += gemv_bytes(w.N, w.K, xb.shape[0], w.bits)
         done += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -159,11 +175,36 @@ def to_dev_half(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.float16)
 
 
-def make_sets(torch, shapes, nsets, cfg_id):
+def to_dev_bf16(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def device_mirai(torch, gen, fmt, shape_nk):
+    """Mirai weights with the synth distributions, drawn on the device: uniform
+    code (and zero-point) words, scales U[0.002, 0.02] (/16 for Mirai-L)
+    rounded to bf16."""
+    N, K = shape_nk
+    G = K // 64
+    bits = 4 if fmt == "mirai-m" else 8
+    wq = torch.randint(-2**31, 2**31 - 1, (N, K * bits // 32), dtype=torch.int32, device="cuda",
+                       generator=gen)
+    su = torch.rand((N, G), device="cuda", generator=gen) * 0.018 + 0.002
+    if fmt == "mirai-l":
+        su = su / 16.0
+    zq = None
+    if fmt == "mirai-m":
+        zq = torch.randint(-2**31, 2**31 - 1, (N, (G + 7) // 8), dtype=torch.int32, device="cuda",
+                           generator=gen)
+    return (wq, su.to(torch.bfloat16), zq, None)
+
+
+def make_sets(torch, shapes, nsets, cfg_id, fmt="affine"):
     """Weight sets cycled by the dense benchmarks. Set 0 comes from the seeded
     host generator (the CPU baseline and the parity tests use the same
     recipe); sets 1.. are drawn on the device with the same distributions
-    (device_affine), which keeps the 21 GB of the 70B sweep quick to build."""
+    (device_affine / device_mirai), which keeps the 21 GB of the 70B sweep
+    quick to build. Each entry: (codes, scales, biases or zero points or
+    None, host weights or None)."""
     import synth
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7919 * cfg_id + 1)
@@ -171,17 +212,24 @@ def make_sets(torch, shapes, nsets, cfg_id):
     for s in range(nsets):
         mats = []
         for j, (K, N) in enumerate(shapes):
-            if s == 0:
+            if s == 0 and fmt == "affine":
                 w = synth.affine_weights(4, N, K, cfg=cfg_id, set_id=s, tensor_base=8 * j)
                 mats.append((to_dev_codes(torch, w.wq), to_dev_half(torch, w.scales),
                              to_dev_half(torch, w.biases), w))
-            else:
+            elif s == 0:
+                w = synth.mirai_weights("M" if fmt == "mirai-m" else "L", N, K, cfg=cfg_id,
+                                        set_id=s, tensor_base=8 * j)
+                mats.append((to_dev_codes(torch, w.wq), to_dev_bf16(torch, w.scales),
+                             None if w.zeros is None else to_dev_codes(torch, w.zeros), w))
+            elif fmt == "affine":
                 mats.append(device_affine(torch, gen, 4, (N, K)))
+            else:
+                mats.append(device_mirai(torch, gen, fmt, (N, K)))
         sets.append(mats)
     return sets
 
 
-def run_dense(args, torch, qd, shapes, batch, sets, cfg_id):
+def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine"):
     import synth
     nsets = len(sets)
     xs, ys, xbits = [], [], []
@@ -196,21 +244,26 @@ def run_dense(args, torch, qd, shapes, batch, sets, cfg_id):
             for j in range(len(shapes)):
                 if only is not None and j != only:
                     continue
-                wq, sc, bi = sets[s][j][:3]
-                qd.qgemv_affine4(wq, sc, bi, xs[j], out=ys[j])
+                wq, sc, third = sets[s][j][:3]
+                if fmt == "affine":
+                    qd.qgemv_affine4(wq, sc, third, xs[j], out=ys[j])
+                elif fmt == "mirai-m":
+                    qd.qgemv_mirai_m(wq, sc, third, xs[j], out=ys[j])
+                else:
+                    qd.qgemv_mirai_l(wq, sc, xs[j], out=ys[j])
         return f
 
     timer = Timer(torch)
     steps = args.steps
     secs, wall = timer.run([step_fn(s) for s in range(nsets)], steps, args.warmup)
-    step_bytes = sum(gemv_bytes(N, K, batch) for K, N in shapes)
+    step_bytes = sum(gemv_bytes(N, K, batch, fmt=fmt) for K, N in shapes)
     per_shape = []
     for j, (K, N) in enumerate(shapes):
         sj, _ = timer.run([step_fn(s, j) for s in range(nsets)], max(nsets, steps // 2),
                           min(args.warmup, nsets))
         n = max(nsets, steps // 2)
         per_shape.append(dict(K=K, N=N, us=sj / n * 1e6,
-                              gbs=gemv_bytes(N, K, batch) * n / sj / 1e9))
+                              gbs=gemv_bytes(N, K, batch, fmt=fmt) * n / sj / 1e9))
     return dict(secs=secs, wall=wall, step_bytes=step_bytes, per_shape=per_shape,
                 launches_per_step=len(shapes), cpu_mats=[(sets[0][j][3], xbits[j]) for j in range(len(shapes))])
 
@@ -398,12 +451,21 @@ def main():
             shapes, batches, nsets, cfg_id = [(8192, 28672), (28672, 8192)], [1, 2, 4, 8], 80, 5
             wl = ("c5: 70B-shaped decode, K=8192 -> N=28672 and K=28672 -> N=8192, int4 g64, "
                   "80 weight-set pairs cycled (21.1 GB)")
+        fmt = args.format
+        if fmt != "affine":
+            # same shapes; the Mirai-L matrices hold twice the code bytes, so
+            # half as many sets keep the cycled footprint alike
+            if fmt == "mirai-l":
+                nsets = max(2, nsets // 2)
+            wl = wl.replace("int4 g64", "Mirai-M (int4, bf16 scale, 4-bit zero point, g64)"
+                            if fmt == "mirai-m" else "Mirai-L (signed int8, bf16 scale, g64)")
+            wl = wl.split(";")[0] + f"; {nsets if not args.sets else args.sets} weight sets cycled"
         if args.sets:
             nsets = args.sets
-        sets = make_sets(torch, shapes, nsets, cfg_id)
+        sets = make_sets(torch, shapes, nsets, cfg_id, fmt)
         results = []
         for batch in batches:
-            r = run_dense(args, torch, qd, shapes, batch, sets, cfg_id)
+            r = run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt)
             results.append((batch, r))
         batch, r = results[0]
         secs = r["secs"]
@@ -411,12 +473,16 @@ def main():
         # dominant kernel: the largest projection of the step, timed on its own
         dom = max(range(len(shapes)), key=lambda j: shapes[j][0] * shapes[j][1])
         dK, dN = shapes[dom]
-        bytes_per_launch = gemv_bytes(dN, dK, batch)
+        bytes_per_launch = gemv_bytes(dN, dK, batch, fmt=fmt)
         launch_s = r["per_shape"][dom]["us"] / 1e6
         achieved = bytes_per_launch / launch_s / 1e9
-        traffic = stored_traffic(f"qgemv_affine4_{args.config}_traffic.json", GEMV_SOURCES)
+        kname = {"affine": "qgemv_affine4", "mirai-m": "qgemv_mirai_m",
+                 "mirai-l": "qgemv_mirai_l"}[fmt]
+        traffic = stored_traffic(f"{kname}_{args.config}_traffic.json", GEMV_SOURCES)
+        metric = METRIC if fmt == "affine" else \
+            f"achieved HBM GB/s (% of peak) for {fmt} GEMV at batch 1"
         out = {
-            "metric": METRIC,
+            "metric": metric,
             "value": round(gbs, 1),
             "unit": "GB/s",
             "n_gpus": 1,
@@ -428,7 +494,7 @@ def main():
             "vs_baseline": None,
             "dtype": "f16",
             "data": "synthetic",
-            "config": {"workload": wl, "batch": batch, "weight_sets": nsets,
+            "config": {"workload": wl, "format": fmt, "batch": batch, "weight_sets": nsets,
                        "step_bytes": r["step_bytes"],
                        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                        "per_shape": [{k: (round(v, 3) if isinstance(v, float) else v)
@@ -436,7 +502,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic,
-                         "kernel": f"qgemv_affine4 K={dK} -> N={dN}, batch {batch}",
+                         "kernel": f"{kname} K={dK} -> N={dN}, batch {batch}",
                          "bytes_per_launch": bytes_per_launch,
                          "avg_launch_us": round(launch_s * 1e6, 3)},
         }

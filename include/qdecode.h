@@ -14,6 +14,10 @@
  *   [uzu] fiv.co.kr/repos/uzu-deep-dive.html, sections 4-3 and 4-4 (tensors
  *         checked by shape and dtype; errors returned as values) and 7-1
  *         (a CPU reference matmul that rejects unsupported layouts).
+ *   [Mirai] discuss.pytorch.kr/t/uzu-mac-iphone-llm-apple-silicon-rust/12363
+ *         (uzu), section "uzu의 모델 변환과 Mirai 양자화 형식" (model
+ *         conversion and the Mirai quantization formats): Mirai-M and
+ *         Mirai-L, the two weight formats its checkpoints ship in.
  *
  * Data layout (all row-major, rows along the output dimension N):
  *   codes   uint32_t wq[N][K*bits/32]; code k of a row sits in word
@@ -80,6 +84,34 @@ qd_status qgemv_affine4(const uint32_t* wq, const uint16_t* scales, const uint16
  *   chunk of tokens); otherwise as qgemv_affine4.
  */
 qd_status qgemv_affine8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                        const uint16_t* x, qd_dtype x_dtype, float* y,
+                        int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                        qd_stream stream);
+
+/*
+ * Mirai-M weights ([Mirai] quantization-format section: asymmetric 4-bit
+ * codes with a 4-bit zero point and a bf16 scale per group of 64):
+ *   y[t][n] = sum_k s[n][g] * (q[n][k] - z[n][g]) * x[t][k],  g = k / 64.
+ *   wq     [N][K/8] uint32, codes packed as for qgemv_affine4;
+ *   scales [N][K/64] bf16 bits;
+ *   zeros  [N][ceil(K/512)] uint32: z[n][g] is nibble g mod 8 of word g/8 of
+ *          row n (LSB-first); nibbles past the row's last group are ignored;
+ *   x [batch][K] fp16 (QD_F16) or bf16 (QD_BF16) bits, y [batch][N] fp32;
+ *   1 <= batch <= 8, K % 64 == 0, group_size == 64.
+ */
+qd_status qgemv_mirai_m(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                        const uint16_t* x, qd_dtype x_dtype, float* y,
+                        int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                        qd_stream stream);
+
+/*
+ * Mirai-L weights ([Mirai] quantization-format section: symmetric 8-bit):
+ *   y[t][n] = sum_k s[n][g] * q[n][k] * x[t][k], q a two's-complement byte.
+ *   wq [N][K/4] uint32, four signed codes per word, LSB-first;
+ *   scales [N][K/64] bf16 bits (the scale type and group of the sibling
+ *   format); otherwise as qgemv_mirai_m.
+ */
+qd_status qgemv_mirai_l(const uint32_t* wq, const uint16_t* scales,
                         const uint16_t* x, qd_dtype x_dtype, float* y,
                         int32_t N, int32_t K, int32_t batch, int32_t group_size,
                         qd_stream stream);

@@ -71,6 +71,31 @@ def test_affine4_batch_limit_is_eight():
     assert gemv("qgemv_affine4", batch=9) == qd.QD_ERR_INVALID_ARGUMENT
 
 
+def mirai_l(wq=A, s=A, x=A, dt=0, y=A, N=16, K=128, batch=1, g=64):
+    return qd.lib().qgemv_mirai_l(wq, s, x, dt, y, N, K, batch, g, None)
+
+
+def test_mirai_argument_errors():
+    E = qd
+    # Mirai-M: the third pointer is the zero-point array
+    assert gemv("qgemv_mirai_m", g=128) == E.QD_ERR_UNSUPPORTED
+    assert gemv("qgemv_mirai_m", K=96) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv("qgemv_mirai_m", batch=9) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv("qgemv_mirai_m", b=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert "zeros" in qd.last_error()
+    assert gemv("qgemv_mirai_m", b=MIS) == E.QD_ERR_MISALIGNED
+    assert gemv("qgemv_mirai_m", s=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert gemv("qgemv_mirai_m", dt=2) == E.QD_ERR_UNSUPPORTED
+    # Mirai-L
+    assert mirai_l(g=32) == E.QD_ERR_UNSUPPORTED
+    assert mirai_l(N=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert mirai_l(batch=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert mirai_l(batch=9) == E.QD_ERR_INVALID_ARGUMENT
+    assert mirai_l(wq=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert mirai_l(x=MIS) == E.QD_ERR_MISALIGNED
+    assert mirai_l(dt=5) == E.QD_ERR_UNSUPPORTED
+
+
 def test_route_argument_errors():
     L = qd.lib()
     assert L.qmoe_route_topk(A, 0, 128, 8, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
