@@ -57,6 +57,8 @@ def _load():
     lib.qo_moe_experts.argtypes = [_P, _P, _I64, _I64, _P, _P, ctypes.c_int, _P, _P, _P, _P]
     lib.qo_mirai_dequant.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _I64, _P]
     lib.qo_mirai_gemv.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+    lib.qo_rht.argtypes = [_P, _I64, _P, _P]
+    lib.qo_rmsnorm.argtypes = [_P, _I64, _P, ctypes.c_double, _P]
     lib.qo_set_threads.argtypes = [ctypes.c_int]
     lib.qo_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -189,6 +191,49 @@ def mirai_gemv_x(w, x_bits, x_dtype: str = "f16", rows=None):
     """Mirai GEMV on fp16 or bf16 activations given as raw bits [T][K]."""
     xd = f16_to_f64(np.atleast_2d(x_bits)) if x_dtype == "f16" else bf16_to_f64(np.atleast_2d(x_bits))
     return mirai_gemv(w, xd, rows)
+
+
+def rht(x, signs=None) -> np.ndarray:
+    """Block-32 random Hadamard transform of each row of x[T][K] (fp64)."""
+    x2, px = _c(np.atleast_2d(x), np.float64)
+    T, K = x2.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    sg, ps = (None, None) if signs is None else _c(signs, np.uint32)
+    if sg is not None and sg.size != K // 32:
+        raise ValueError("signs must hold K/32 words")
+    out = np.empty_like(x2)
+    for t in range(T):
+        _load().qo_rht(x2[t].ctypes.data_as(_P), K, ps, out[t].ctypes.data_as(_P))
+    return out
+
+
+def rmsnorm(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm of each row of x[T][K] with weight gamma[K] (fp64; None = 1)."""
+    x2, px = _c(np.atleast_2d(x), np.float64)
+    T, K = x2.shape
+    g, pg = (None, None) if gamma is None else _c(gamma, np.float64)
+    out = np.empty_like(x2)
+    for t in range(T):
+        _load().qo_rmsnorm(x2[t].ctypes.data_as(_P), K, pg, float(eps), out[t].ctypes.data_as(_P))
+    return out
+
+
+def mirai_gemv_rht(w, x_bits, x_dtype="f16", signs=None, gamma_bits=None, eps: float = 1e-6,
+                   rows=None):
+    """GEMV with the rotation prologue: y = W' (H D rmsnorm(x)).
+
+    gamma_bits None skips the RMSNorm (a projection whose input does not come
+    from a norm); gamma is given in the activations' dtype. Returns
+    (y, A, x') with A = sum_k |w'_k x'_k| and x' the rotated activations.
+    """
+    dec = f16_to_f64 if x_dtype == "f16" else bf16_to_f64
+    xd = dec(np.atleast_2d(x_bits))
+    if gamma_bits is not None:
+        xd = rmsnorm(xd, dec(gamma_bits), eps)
+    xr = rht(xd, signs)
+    y, a = mirai_gemv(w, xr, rows)
+    return y, a, xr
 
 
 def route_topk(logits, k: int):

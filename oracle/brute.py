@@ -69,6 +69,25 @@ def mirai_gemv(w, x: np.ndarray) -> np.ndarray:
     return np.atleast_2d(x) @ mirai_dense(w).T
 
 
+def rotation(K: int, signs) -> np.ndarray:
+    """The block-diagonal rotation R [K][K] = diag over blocks of H_32 D_b / sqrt(32),
+    from scipy's Hadamard matrix and the sign bits read with divmod."""
+    from scipy.linalg import hadamard
+    H = hadamard(32).astype(np.float64) / math.sqrt(32.0)
+    R = np.zeros((K, K))
+    for b in range(K // 32):
+        word = int(signs[b]) if signs is not None else 0
+        d = np.array([-1.0 if (word // 2 ** j) % 2 else 1.0 for j in range(32)])
+        R[32 * b:32 * b + 32, 32 * b:32 * b + 32] = H * d[None, :]
+    return R
+
+
+def rmsnorm(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    g = np.ones(x.shape[1]) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps) * g[None, :]
+
+
 def gemv(w, x: np.ndarray) -> np.ndarray:
     return np.atleast_2d(x) @ dense(w).T
 

@@ -311,3 +311,42 @@ void qo_mirai_gemv(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_
         }
     }
 }
+
+/*
+ * Block-32 random Hadamard transform ([uzu] quantization-format section:
+ * both Mirai formats suppress outliers with a random Hadamard transform of
+ * block size 32 before quantization; the transform is fused into the
+ * RMSNorm and matmul kernels). Reading: for each block of 32 consecutive
+ * inputs, out = (1/sqrt(32)) * H * D * x with H the Sylvester Hadamard
+ * matrix, H[i][j] = (-1)^popcount(i & j), and D = diag(d) the random signs,
+ * d_j = -1 where bit j of signs[block] is set. Weights stored in the
+ * rotated basis then give W' (H D x) = W x. Written as the plain 32 x 32
+ * matrix-vector product (no fast transform).
+ */
+void qo_rht(const double* x, int64_t K, const uint32_t* signs, double* out) {
+    const double c = 1.0 / sqrt(32.0);
+    for (int64_t blk = 0; blk < K / 32; ++blk) {
+        const double* xb = x + 32 * blk;
+        double v[32];
+        for (int j = 0; j < 32; ++j) {
+            int neg = signs ? (int)((signs[blk] >> j) & 1u) : 0;
+            v[j] = neg ? -xb[j] : xb[j];
+        }
+        for (int i = 0; i < 32; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < 32; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -v[j] : v[j];
+            out[32 * blk + i] = c * acc;
+        }
+    }
+}
+
+/*
+ * RMSNorm (the norm the rotation is fused with, [uzu] same section):
+ * out_k = x_k / sqrt(mean_k(x_k^2) + eps) * gamma_k; gamma NULL means 1.
+ */
+void qo_rmsnorm(const double* x, int64_t K, const double* gamma, double eps, double* out) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) ss += x[k] * x[k];
+    const double r = 1.0 / sqrt(ss / (double)K + eps);
+    for (int64_t k = 0; k < K; ++k) out[k] = x[k] * r * (gamma ? gamma[k] : 1.0);
+}

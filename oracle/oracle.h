@@ -98,6 +98,16 @@ void qo_mirai_gemv(int fmt, const uint32_t* wq, const uint16_t* s, const uint32_
                    const double* x, int64_t T, int64_t N, int64_t K,
                    const int64_t* rows, int64_t nrows, double* y, double* a);
 
+/*
+ * Block-32 random Hadamard transform of x[K] (K % 32 == 0):
+ * out[32b + i] = 2^-2.5 * sum_j (-1)^popcount(i & j) * d_j * x[32b + j], d_j = -1 where
+ * bit j of signs[b] is set (signs NULL = all +1). out must not alias x.
+ */
+void qo_rht(const double* x, int64_t K, const uint32_t* signs, double* out);
+
+/* RMSNorm: out = x / sqrt(mean(x^2) + eps) * gamma (gamma NULL = 1). */
+void qo_rmsnorm(const double* x, int64_t K, const double* gamma, double eps, double* out);
+
 /* Number of OpenMP threads the oracle uses (0 = runtime default). */
 void qo_set_threads(int n);
 int qo_get_threads(void);

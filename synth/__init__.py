@@ -41,7 +41,7 @@ import numpy as np
 GROUP = 64
 
 # tensor ids inside one weight set
-T_CODES, T_SCALE, T_BIAS, T_X = 0, 1, 2, 3
+T_CODES, T_SCALE, T_BIAS, T_X, T_SIGNS, T_GAMMA = 0, 1, 2, 3, 4, 5
 
 
 def rng(cfg: int, set_id: int, tensor: int) -> np.random.Generator:
@@ -178,6 +178,22 @@ def mirai_weights(fmt: str, N: int, K: int, cfg: int, set_id: int, tensor_base: 
         else:
             raise ValueError(zeros)
     return MiraiWeights(fmt, N, K, wq, sb, zq)
+
+
+def rht_signs(K: int, cfg: int, set_id: int) -> np.ndarray:
+    """Random signs of a block-32 Hadamard rotation: uint32 [K/32], bit j of word b
+    set = input 32b + j negated (each bit an independent fair coin)."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    return rng(cfg, set_id, T_SIGNS).integers(0, 2**32, size=K // 32, dtype=np.uint32)
+
+
+def rmsnorm_gamma(K: int, cfg: int, set_id: int, dtype: str = "f16") -> np.ndarray:
+    """RMSNorm weights U[0.5, 1.5] as fp16 or bf16 bits [K]."""
+    g = rng(cfg, set_id, T_GAMMA).uniform(0.5, 1.5, size=K)
+    if dtype == "f16":
+        return g.astype(np.float16).view(np.uint16)
+    return f32_to_bf16_bits(g.astype(np.float32))
 
 
 def x_f16(T: int, K: int, cfg: int, set_id: int, tensor: int = T_X) -> np.ndarray:

@@ -469,3 +469,92 @@ def test_mirai_generator_ranges():
     assert q.min() == -128 and q.max() == 127
     assert brute.bf16(el.scales).max() <= 0.0201 / 16
     assert m.nbytes == 8 * (512 + 32 + 8)
+
+
+# ---------------------------------------------------------------- rotation prologue
+# uzu page (discuss.pytorch.kr), quantization-format section: a block-32
+# random Hadamard transform applied before quantization, fused with RMSNorm
+# and the matmul.
+
+def test_rht_columns_are_scipy_hadamard():
+    from scipy.linalg import hadamard
+    K = 64
+    eye = np.eye(K)
+    cols = oracle.rht(eye)                      # row j = transform of unit vector j
+    R = cols.T
+    H = hadamard(32) / math.sqrt(32.0)
+    assert np.allclose(R[:32, :32], H, rtol=0, atol=1e-15)
+    assert np.allclose(R[32:, 32:], H, rtol=0, atol=1e-15)
+    assert np.all(R[:32, 32:] == 0) and np.all(R[32:, :32] == 0)
+
+
+def test_rht_with_signs_matches_explicit_rotation():
+    K = 256
+    sg = synth.rht_signs(K, cfg=130, set_id=0)
+    x = np.random.default_rng(0).standard_normal((3, K))
+    R = brute.rotation(K, sg)
+    assert np.allclose(oracle.rht(x, sg), x @ R.T, rtol=0, atol=1e-13)
+    # signs act on the inputs: rotate(x, d) = rotate(d * x, none)
+    d = np.concatenate([[-1.0 if (int(w) >> j) & 1 else 1.0 for j in range(32)] for w in sg])
+    assert np.allclose(oracle.rht(x, sg), oracle.rht(x * d[None, :]), rtol=0, atol=1e-13)
+
+
+def test_rht_is_orthogonal_and_self_inverse_without_signs():
+    K = 512
+    x = np.random.default_rng(1).standard_normal((2, K))
+    y = oracle.rht(x)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    assert np.allclose(oracle.rht(y), x, rtol=0, atol=1e-13)
+    sg = synth.rht_signs(K, cfg=131, set_id=0)
+    assert np.allclose(np.linalg.norm(oracle.rht(x, sg), axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+
+
+def test_rotated_weights_preserve_the_product():
+    # W' = W R^T gives W' (R x) = W x: the reason the rotation can be fused
+    K, N = 128, 5
+    sg = synth.rht_signs(K, cfg=132, set_id=0)
+    rng = np.random.default_rng(2)
+    W, x = rng.standard_normal((N, K)), rng.standard_normal((1, K))
+    R = brute.rotation(K, sg)
+    assert np.allclose((W @ R.T) @ oracle.rht(x, sg)[0], W @ x[0], rtol=0, atol=1e-12)
+
+
+def test_rmsnorm_closed_forms():
+    K = 192
+    c, eps = 3.0, 1e-6
+    out = oracle.rmsnorm(np.full((1, K), c), None, eps)
+    assert np.allclose(out, c / math.sqrt(c * c + eps), rtol=1e-15)
+    x = np.random.default_rng(3).standard_normal((2, K))
+    g = np.random.default_rng(4).uniform(0.5, 1.5, K)
+    assert np.allclose(oracle.rmsnorm(x, g, 1e-5), brute.rmsnorm(x, g, 1e-5), rtol=1e-14)
+    assert np.array_equal(oracle.rmsnorm(np.zeros((1, K)), g, eps), np.zeros((1, K)))
+    # scale invariance when eps = 0
+    assert np.allclose(oracle.rmsnorm(5 * x, g, 0.0), oracle.rmsnorm(x, g, 0.0), rtol=1e-14)
+
+
+@pytest.mark.parametrize("fmt", ["M", "L"])
+def test_mirai_gemv_with_rotation_prologue_matches_bruteforce(fmt):
+    N, K, T = 7, 704, 2
+    w = synth.mirai_weights(fmt, N, K, cfg=133, set_id=0)
+    xb = synth.x_bf16(T, K, cfg=133, set_id=0)
+    sg = synth.rht_signs(K, cfg=133, set_id=0)
+    gb = synth.rmsnorm_gamma(K, cfg=133, set_id=0, dtype="bf16")
+    y, a, xr = oracle.mirai_gemv_rht(w, xb, "bf16", sg, gb, 1e-5)
+    xn = brute.rmsnorm(brute.bf16(xb), brute.bf16(gb), 1e-5)
+    R = brute.rotation(K, sg)
+    d = brute.mirai_dense(w)
+    assert np.allclose(xr, xn @ R.T, rtol=0, atol=1e-13)
+    yb = (xn @ R.T) @ d.T
+    assert np.all(np.abs(y - yb) <= 1e-12 * a)
+    # without the norm, only the rotation
+    y2, _, _ = oracle.mirai_gemv_rht(w, xb, "bf16", sg, None)
+    assert np.allclose(y2, (brute.bf16(xb) @ R.T) @ d.T, rtol=1e-12, atol=1e-12)
+
+
+def test_rht_generators():
+    sg = synth.rht_signs(1024, cfg=3, set_id=0)
+    assert sg.shape == (32,) and sg.dtype == np.uint32
+    bits = np.unpackbits(sg.view(np.uint8))
+    assert 0.4 < bits.mean() < 0.6
+    g = brute.f16(synth.rmsnorm_gamma(1024, cfg=3, set_id=0))
+    assert g.min() >= 0.5 and g.max() <= 1.5

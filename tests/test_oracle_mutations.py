@@ -48,6 +48,17 @@ MUTATIONS = {
     "mirai wrong scale group": ("const int64_t grp = k / 64;", "const int64_t grp = (k / 64 + 1) % groups;"),
     "mirai-l codes unsigned": ("int q = u >= 128 ? u - 256 : u;", "int q = u;"),
     "mirai-l sign threshold": ("int q = u >= 128 ? u - 256 : u;", "int q = u > 128 ? u - 256 : u;"),
+    "hadamard sign rule": ("acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -v[j] : v[j];",
+                           "acc += (__builtin_popcount((unsigned)(i | j)) & 1) ? -v[j] : v[j];"),
+    "hadamard not normalized": ("out[32 * blk + i] = c * acc;", "out[32 * blk + i] = acc + 0.0 * c;"),
+    "hadamard signs ignored": ("int neg = signs ? (int)((signs[blk] >> j) & 1u) : 0;", "int neg = 0;"),
+    "hadamard signs on outputs": ("int neg = signs ? (int)((signs[blk] >> j) & 1u) : 0;",
+                                  "int neg = signs ? (int)((signs[blk] >> (31 - j)) & 1u) : 0;"),
+    "rmsnorm eps outside": ("const double r = 1.0 / sqrt(ss / (double)K + eps);",
+                            "const double r = 1.0 / (sqrt(ss / (double)K) + eps);"),
+    "rmsnorm mean over K-1": ("const double r = 1.0 / sqrt(ss / (double)K + eps);",
+                              "const double r = 1.0 / sqrt(ss / (double)(K - 1) + eps);"),
+    "rmsnorm gamma ignored": ("out[k] = x[k] * r * (gamma ? gamma[k] : 1.0);", "out[k] = x[k] * r;"),
     "shared expert halved": ("yt[n] += o[n];\n            if (at) at[n] += oa[n];\n        }\n    }",
                              "yt[n] += 0.5 * o[n];\n            if (at) at[n] += oa[n];\n        }\n    }"),
 }
@@ -76,6 +87,11 @@ PIN_CALLS = [
     (pins.test_mirai_m_equals_affine_with_bias_minus_s_z, {}),
     (pins.test_mirai_l_equals_affine8_with_offset_codes, {}),
     (pins.test_mirai_code_equal_to_zero_point_gives_zero, {}),
+    (pins.test_rht_columns_are_scipy_hadamard, {}),
+    (pins.test_rht_with_signs_matches_explicit_rotation, {}),
+    (pins.test_rht_is_orthogonal_and_self_inverse_without_signs, {}),
+    (pins.test_rmsnorm_closed_forms, {}),
+    (pins.test_mirai_gemv_with_rotation_prologue_matches_bruteforce, {"fmt": "M"}),
 ]
 
 
