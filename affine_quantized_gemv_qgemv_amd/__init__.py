@@ -28,7 +28,8 @@ QD_OK, QD_ERR_INVALID_ARGUMENT, QD_ERR_MISALIGNED, QD_ERR_UNSUPPORTED, QD_ERR_WO
 QD_F16, QD_BF16 = 0, 1
 QD_GELU_ERF, QD_GELU_TANH = 0, 1
 
-EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qmoe_route_topk",
+EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
+           "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
            "qd_status_string", "qd_last_error")
 
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.qgemv_affine8.argtypes = gemv_args
     L.qgemv_mirai_m.argtypes = gemv_args
     L.qgemv_mirai_l.argtypes = [_P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemv_mirai_m_rht.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_int, _P,
+                                    _I32, _I32, _I32, _I32, _P]
+    L.qgemv_mirai_l_rht.argtypes = [_P, _P, _P, _P, ctypes.c_float, _P, ctypes.c_int, _P,
+                                    _I32, _I32, _I32, _I32, _P]
     L.qmoe_route_topk.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P]
     L.qmoe_expert_workspace_bytes.argtypes = [ctypes.POINTER(MoeWeightsC), _I32, _I32]
     L.qmoe_expert_workspace_bytes.restype = ctypes.c_size_t
@@ -79,6 +84,7 @@ def lib() -> ctypes.CDLL:
     L.qd_last_error.argtypes = []
     L.qd_last_error.restype = ctypes.c_char_p
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
+               "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
                "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -162,7 +168,7 @@ def qgemv_affine8(wq, scales, biases, x, out=None):
     return _qgemv(8, wq, scales, biases, x, out)
 
 
-def _mirai(fmt: str, wq, scales, zeros, x, out):
+def _mirai(fmt: str, wq, scales, zeros, x, out, rot=None):
     bits = 4 if fmt == "M" else 8
     squeeze = x.dim() == 1
     x2 = x.unsqueeze(0) if squeeze else x
@@ -185,7 +191,25 @@ def _mirai(fmt: str, wq, scales, zeros, x, out):
     _need(out, "out", (torch.float32,), 2)
     if tuple(out.shape) != (batch, N):
         raise ValueError("out must be [batch][N]")
-    if fmt == "M":
+    if rot is not None:
+        signs, gamma, eps = rot
+        if signs is not None:
+            _need(signs, "signs", _CODES, 1)
+            if signs.numel() != K // 32:
+                raise ValueError("signs must hold K/32 words")
+        if gamma is not None:
+            _need(gamma, "gamma", (x2.dtype,), 1)
+            if gamma.numel() != K:
+                raise ValueError("gamma must hold K values")
+        if fmt == "M":
+            _check(lib().qgemv_mirai_m_rht(_ptr(wq), _ptr(scales), _ptr(zeros), _ptr(signs),
+                                           _ptr(gamma), float(eps), _ptr(x2), _x_dtype(x2), _ptr(out),
+                                           N, K, batch, 64, _stream()))
+        else:
+            _check(lib().qgemv_mirai_l_rht(_ptr(wq), _ptr(scales), _ptr(signs), _ptr(gamma),
+                                           float(eps), _ptr(x2), _x_dtype(x2), _ptr(out), N, K,
+                                           batch, 64, _stream()))
+    elif fmt == "M":
         _check(lib().qgemv_mirai_m(_ptr(wq), _ptr(scales), _ptr(zeros), _ptr(x2), _x_dtype(x2),
                                    _ptr(out), N, K, batch, 64, _stream()))
     else:
@@ -202,6 +226,19 @@ def qgemv_mirai_m(wq, scales, zeros, x, out=None):
 def qgemv_mirai_l(wq, scales, x, out=None):
     """y[b][n] = sum_k s*q x[b][k]: signed 8-bit codes, bf16 scales; batch <= 8."""
     return _mirai("L", wq, scales, None, x, out)
+
+
+def qgemv_mirai_m_rht(wq, scales, zeros, x, signs=None, gamma=None, eps: float = 1e-6, out=None):
+    """Mirai-M GEMV on the rotated activations H D (RMSNorm(x) * gamma), block 32.
+
+    signs: int32 [K/32] sign bits (None = no flips); gamma: [K] in x's dtype
+    (None = no RMSNorm)."""
+    return _mirai("M", wq, scales, zeros, x, out, (signs, gamma, eps))
+
+
+def qgemv_mirai_l_rht(wq, scales, x, signs=None, gamma=None, eps: float = 1e-6, out=None):
+    """Mirai-L GEMV on the rotated activations H D (RMSNorm(x) * gamma), block 32."""
+    return _mirai("L", wq, scales, None, x, out, (signs, gamma, eps))
 
 
 def qmoe_route_topk(logits, k: int, idx=None, weights=None):

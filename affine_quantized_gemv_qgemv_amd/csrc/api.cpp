@@ -64,7 +64,8 @@ qd_status check_matrix(const char* fn, int32_t N, int32_t K, int32_t group_size)
 qd_status gemv_common(const char* fn, int bits, int fmt, int max_batch, const uint32_t* wq,
                       const uint16_t* scales, const uint16_t* biases, const uint32_t* zeros,
                       const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
-                      int32_t batch, int32_t group_size, qd_stream stream) {
+                      int32_t batch, int32_t group_size, qd_stream stream,
+                      const qd::GemvRot* rot = nullptr) {
     qd_status st = check_matrix(fn, N, K, group_size);
     if (st != QD_OK) return st;
     if (batch < 1 || batch > max_batch)
@@ -78,9 +79,16 @@ qd_status gemv_common(const char* fn, int bits, int fmt, int max_batch, const ui
     if (fmt == 1) CHECK_PTR(zeros);
     CHECK_PTR(x);
     CHECK_PTR(y);
+    if (rot) {
+        if (rot->signs) CHECK_PTR(rot->signs);
+        if (rot->gamma) CHECK_PTR(rot->gamma);
+        if (!(rot->eps >= 0.f) || rot->eps > 1e30f)
+            return fail(QD_ERR_INVALID_ARGUMENT, "%s: eps = %g must be finite and >= 0", fn,
+                        (double)rot->eps);
+    }
     const int xkind = x_dtype == QD_F16 ? 0 : 1;
     return from_hip(qd::launch_gemv(bits, fmt, wq, scales, biases, zeros, x, xkind, y, N, K,
-                                    batch, (hipStream_t)stream),
+                                    batch, (hipStream_t)stream, rot),
                     fn);
 }
 
@@ -213,6 +221,24 @@ qd_status qgemv_mirai_m(const uint32_t* wq, const uint16_t* scales, const uint32
                         int32_t batch, int32_t group_size, qd_stream stream) {
     return gemv_common("qgemv_mirai_m", 4, 1, 8, wq, scales, nullptr, zeros, x, x_dtype, y, N, K,
                        batch, group_size, stream);
+}
+
+qd_status qgemv_mirai_m_rht(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                            const uint32_t* signs, const uint16_t* gamma, float eps,
+                            const uint16_t* x, qd_dtype x_dtype, float* y, int32_t N, int32_t K,
+                            int32_t batch, int32_t group_size, qd_stream stream) {
+    const qd::GemvRot rot{signs, gamma, eps};
+    return gemv_common("qgemv_mirai_m_rht", 4, 1, 8, wq, scales, nullptr, zeros, x, x_dtype, y, N,
+                       K, batch, group_size, stream, &rot);
+}
+
+qd_status qgemv_mirai_l_rht(const uint32_t* wq, const uint16_t* scales, const uint32_t* signs,
+                            const uint16_t* gamma, float eps, const uint16_t* x, qd_dtype x_dtype,
+                            float* y, int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                            qd_stream stream) {
+    const qd::GemvRot rot{signs, gamma, eps};
+    return gemv_common("qgemv_mirai_l_rht", 8, 2, 8, wq, scales, nullptr, nullptr, x, x_dtype, y,
+                       N, K, batch, group_size, stream, &rot);
 }
 
 qd_status qgemv_mirai_l(const uint32_t* wq, const uint16_t* scales, const uint16_t* x,

@@ -118,11 +118,16 @@ __device__ __forceinline__ float seg_sum(float v) {
 //   cs[b][c]     float2 (1024*sum_1 + 64*sum_16 (or 1024*sum), sum) on the
 //                fp16 path, float sum on the fp32 path.
 // ---------------------------------------------------------------------------
+//
+// XF = 2 (rotated activations, see stage_x_rot) keeps the fp16 layout twice:
+// planes q < QH hold the fp16 rounding hi of each value, planes QH + q the
+// fp16 remainder lo = fp16(v - hi), and cs holds the class sums of hi + lo.
 template <int BITS, int XF>
 struct Stage {
     static constexpr int CC = 128 / BITS;                               // codes per chunk
-    static constexpr int QPC = XF ? CC / 4 : (BITS == 4 ? 4 : 2);       // uint4 per chunk
-    static constexpr int CSZ = XF ? 4 : 8;                              // const bytes per chunk
+    static constexpr int QH = BITS == 4 ? 4 : 2;                        // fp16 uint4 per chunk
+    static constexpr int QPC = XF == 1 ? CC / 4 : (XF == 2 ? 2 * QH : QH);  // uint4 per chunk
+    static constexpr int CSZ = XF == 1 ? 4 : 8;                         // const bytes per chunk
     __host__ __device__ static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
 };
 
@@ -227,6 +232,234 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
     }
 }
 
+// ---------------------------------------------------------------------------
+// Rotation prologue (XF = 2): discuss.pytorch.kr/t/uzu-mac-iphone-llm-apple-
+// silicon-rust/12363 (uzu), section "uzu의 모델 변환과 Mirai 양자화 형식"
+// (model conversion and the Mirai quantization formats): weights are
+// quantized after a random Hadamard transform of block size 32, and the
+// transform is fused with RMSNorm and the matmul. Each staged block of 32
+// inputs becomes
+//     v = 2^-2.5 * r * H_32 * D * (x * gamma),   r = 1 / sqrt(mean(x^2) + eps),
+// H_32 the Sylvester Hadamard matrix and D the block's random signs. A pair
+// of adjacent lanes takes a block, 16 inputs each: four butterfly stages in
+// registers and the last one across the pair (one DPP move and one fma per
+// value). Staging runs in two passes over LDS: the first writes the
+// unnormalized transform in fp32 while summing x^2 and tracking
+// max |H D (x gamma)|; after one reduction the second scales by
+// r * 2^-2.5 * 2^e (2^e a power of two that keeps |v| below 2^14) and
+// rewrites each lane's own slots in place as two fp16 planes, hi = v rounded
+// toward zero and lo = (v - hi) rounded toward zero, so hi + lo is v to about
+// 2^-20 relative. The kernel multiplies its result by 2^-e. Blocks are 32
+// inputs: one chunk of 4-bit codes or two chunks of 8-bit codes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fwht16(float (&v)[16]) {
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * h)
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+}
+
+// The value of lane ^ 1.
+__device__ __forceinline__ float pair_swap(float v) {
+    // quad_perm [1, 0, 3, 2]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// 8 consecutive elements of x (f16 or bf16 bits) as fp32.
+__device__ __forceinline__ void load8(const uint16_t* p, int kind, float (&o)[8]) {
+    const uint4 raw = *(const uint4*)p;
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t a = w[i] & 0xFFFF, b = w[i] >> 16;
+        o[2 * i] = kind == X_F16 ? h2f(a) : bf2f(a);
+        o[2 * i + 1] = kind == X_F16 ? h2f(b) : bf2f(b);
+    }
+}
+
+// hi/lo fp16 pairs of (a, b), and the fp32 sum of hi + lo added to s.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo, float& s) {
+    typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(a, b);
+    const fp16x2 l = __builtin_amdgcn_cvt_pkrtz(a - (float)h.x, b - (float)h.y);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+    s = dot2(hi, 0x3C003C00u, s);   // (1.0, 1.0)
+    s = dot2(lo, 0x3C003C00u, s);
+}
+
+constexpr int kRotMaxB = 8;    // vectors per launch
+constexpr int kRotWaves = 16;  // waves per workgroup
+// LDS floats the rotation prologue needs besides the staged planes.
+constexpr int kRotShared = 2 * kRotMaxB * kRotWaves + 2 * kRotMaxB;
+
+// Stage chunks [c0, c0 + nc) of the rotated x[b][K] (b < nb); gamma (K, x's
+// kind) and signs (K/32 words) may be NULL. rs is kRotShared floats of LDS;
+// on return rs[kRotMaxB + b] holds 2^-e of vector b. Every thread must call.
+template <int BITS, int CPL = 1>
+__device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, int nb, int c0,
+                                            int nc, const uint16_t* gamma, const uint32_t* signs,
+                                            float eps, float* rs, uint4* lds) {
+    using St = Stage<BITS, 2>;
+    constexpr int CC = St::CC, QH = St::QH, QPC = St::QPC;
+    constexpr int CPB = 32 / CC;   // chunks per block
+    const int nblk = nc / CPB;
+    uint4* xs = lds;
+    float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
+    float* mulv = rs;                        // [kRotMaxB]
+    float* unscale = rs + kRotMaxB;          // [kRotMaxB]
+    float* red = rs + 2 * kRotMaxB;          // [2][kRotMaxB][kRotWaves]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int hh = lane & 1;                 // half of the block this lane holds
+    // Slot i < 4 of this lane's half of block bl: the LDS uint4 that receives
+    // its inputs 4i..4i+3 in pass 1 and the planes built from them in pass 2
+    // (4-bit: hi and lo planes of words 2hh, 2hh + 1; 8-bit: chunk hh).
+    auto slot = [&](int b, int bl, int i) -> uint4* {
+        if constexpr (BITS == 4)
+            return xs + (size_t)(b * QPC + (i & 1) + 2 * hh + QH * (i >> 1)) * nc +
+                   xslot<CPL>(bl, nc);
+        else
+            return xs + (size_t)(b * QPC + i) * nc + xslot<CPL>(bl * 2 + hh, nc);
+    };
+
+    // pass 1: each vector's blocks go to wpb waves, so sums stay per wave
+    const int wpb = max(1, nwaves / nb);
+    const int ngroups = min(nb, nwaves / wpb);
+    if (wave < ngroups * wpb) {
+        const int wg = wave % wpb;
+        const float sgn = hh ? -1.f : 1.f;
+        for (int b = wave / wpb; b < nb; b += ngroups) {
+            const uint16_t* xb = x + (int64_t)b * K;
+            float ss = 0.f, mx = 0.f;
+            // both lanes of a pair run the same iterations
+            for (int bl = (wg * 64 + lane) >> 1; bl < nblk; bl += wpb * 32) {
+                const int k0 = (c0 + bl * CPB) * CC + 16 * hh;
+                const uint32_t sg = signs ? signs[k0 / 32] >> (16 * hh) : 0u;
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    float t[8], g[8];
+                    load8(xb + k0 + 8 * q, kind, t);
+                    if (gamma) {
+                        load8(gamma + k0 + 8 * q, kind, g);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) g[i] = 1.f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        ss = fmaf(t[i], t[i], ss);
+                        const uint32_t neg = (sg << (31 - (8 * q + i))) & 0x80000000u;
+                        v[8 * q + i] = t[i] * __uint_as_float(__float_as_uint(g[i]) ^ neg);
+                    }
+                }
+                fwht16(v);
+                // last stage: even lane a + b, odd lane a - b (a the even lane's)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = fmaf(v[j], sgn, pair_swap(v[j]));
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *slot(b, bl, i) = make_uint4(__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                                                 __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3]));
+            }
+            if (gamma && nc * CC < K) {
+                // a split chunk range: the norm still covers the whole vector
+                for (int kb = wg * 64 + lane; kb < K / 32; kb += wpb * 64) {
+                    if (kb * 32 >= c0 * CC && kb * 32 < (c0 + nc) * CC) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        float t[8];
+                        load8(xb + kb * 32 + 8 * q, kind, t);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ss = fmaf(t[i], t[i], ss);
+                    }
+                }
+            }
+            ss = seg_sum<64>(ss);
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+            if (lane == 0) {
+                red[b * kRotWaves + wg] = ss;
+                red[(kRotMaxB + b) * kRotWaves + wg] = mx;
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) {
+        const int b = threadIdx.x;
+        float S = 0.f, M = 0.f;
+        for (int w = 0; w < wpb; ++w) {
+            S += red[b * kRotWaves + w];
+            M = fmaxf(M, red[(kRotMaxB + b) * kRotWaves + w]);
+        }
+        constexpr float kNorm = 0.17677669529663688f;   // 2^-2.5
+        const float r = gamma ? 1.f / sqrtf(S / (float)K + eps) : 1.f;
+        const float bound = r * M * kNorm;              // max |v|, up to rounding
+        // bound < 2^E with E from the exponent field; then 2^e bound < 2^14
+        int e = 0;
+        if (bound > 0.f && bound <= 3.0e38f) {
+            const int E = max((int)((__float_as_uint(bound) >> 23) & 0xFF), 1) - 126;
+            e = min(max(14 - E, -120), 120);
+        }
+        mulv[b] = r * __uint_as_float((uint32_t)(e + 127) << 23) * kNorm;
+        unscale[b] = __uint_as_float((uint32_t)(127 - e) << 23);
+    }
+    __syncthreads();
+
+    // pass 2: each lane scales its own 16 values and rewrites its slots as
+    // hi/lo planes; class sums of a 4-bit chunk combine across the pair
+    for (int t = threadIdx.x; t < 2 * nb * nblk; t += blockDim.x) {
+        const int item = t >> 1;   // t & 1 == hh, since blockDim.x is even
+        const int b = item / nblk, bl = item - b * nblk;
+        const float m = mulv[b];
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 u = *slot(b, bl, i);
+            v[4 * i] = __uint_as_float(u.x) * m;
+            v[4 * i + 1] = __uint_as_float(u.y) * m;
+            v[4 * i + 2] = __uint_as_float(u.z) * m;
+            v[4 * i + 3] = __uint_as_float(u.w) * m;
+        }
+        float s1 = 0.f, s16 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float* w = v + 8 * q;
+            uint32_t h[4], l[4];
+            if constexpr (BITS == 4) {
+                // pairs (0,4), (2,6) hold the codes of nibbles 0, 2, 4, 6 (class 1)
+                split_pair(w[0], w[4], h[0], l[0], s1);
+                split_pair(w[1], w[5], h[1], l[1], s16);
+                split_pair(w[2], w[6], h[2], l[2], s1);
+                split_pair(w[3], w[7], h[3], l[3], s16);
+            } else {
+                split_pair(w[0], w[2], h[0], l[0], s1);
+                split_pair(w[1], w[3], h[1], l[1], s1);
+                split_pair(w[4], w[6], h[2], l[2], s1);
+                split_pair(w[5], w[7], h[3], l[3], s1);
+            }
+            // hi plane of word q -> slot q, lo plane -> slot 2 + q
+            *slot(b, bl, q) = make_uint4(h[0], h[1], h[2], h[3]);
+            *slot(b, bl, 2 + q) = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+        if constexpr (BITS == 4) {
+            s1 += pair_swap(s1);   // the chunk's 32 inputs span both lanes
+            s16 += pair_swap(s16);
+            if (hh == 0) cs[b * nc + xslot<CPL>(bl, nc)] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+        } else {
+            cs[b * nc + xslot<CPL>(bl * 2 + hh, nc)] = make_float2(1024.f * s1, s1);
+        }
+    }
+}
+
 // Partial dot products of NCH consecutive 16-byte code chunks (one lane's
 // share of a group) of each of R rows with every activation vector b < B,
 // followed by one affine epilogue into y[r][b]:
@@ -240,8 +473,9 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
                                            float (&y)[R][B]) {
     using St = Stage<BITS, XF>;
     constexpr int QPC = St::QPC;
+    constexpr int NPL = XF == 2 ? 2 : 1;   // fp16 planes: value, or hi and lo
     const uint4* xs = lds;
-    if constexpr (XF == 0) {
+    if constexpr (XF == 0 || XF == 2) {
         const float2* cs = (const float2*)(xs + (size_t)nb_staged * QPC * nc);
         float a1[R][B], a16[R][B];
 #pragma unroll
@@ -254,9 +488,11 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
             if constexpr (BITS == 4) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    uint4 xq[B];
+                    uint4 xq[NPL][B];   // plane 1 (if any): the fp16 remainders
 #pragma unroll
-                    for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+                    for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) xq[pl][b] = xs[(b * QPC + pl * 4 + q) * nc + c];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const uint4& w4 = cw[ch][r];
@@ -267,20 +503,24 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
                         const uint32_t p26 = (w8 & 0x000F000Fu) | magic;  // 1024+q2, 1024+q6
                         const uint32_t p37 = (w8 & 0x00F000F0u) | magic;  // 1024+16q3, 1024+16q7
 #pragma unroll
-                        for (int b = 0; b < B; ++b) {
-                            a1[r][b] = dot2(p04, xq[b].x, a1[r][b]);
-                            a16[r][b] = dot2(p15, xq[b].y, a16[r][b]);
-                            a1[r][b] = dot2(p26, xq[b].z, a1[r][b]);
-                            a16[r][b] = dot2(p37, xq[b].w, a16[r][b]);
-                        }
+                        for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                a1[r][b] = dot2(p04, xq[pl][b].x, a1[r][b]);
+                                a16[r][b] = dot2(p15, xq[pl][b].y, a16[r][b]);
+                                a1[r][b] = dot2(p26, xq[pl][b].z, a1[r][b]);
+                                a16[r][b] = dot2(p37, xq[pl][b].w, a16[r][b]);
+                            }
                     }
                 }
             } else {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    uint4 xq[B];
+                    uint4 xq[NPL][B];
 #pragma unroll
-                    for (int b = 0; b < B; ++b) xq[b] = xs[(b * QPC + q) * nc + c];
+                    for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+                        for (int b = 0; b < B; ++b) xq[pl][b] = xs[(b * QPC + pl * 2 + q) * nc + c];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const uint4& w4 = cw[ch][r];
@@ -291,12 +531,14 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
                         const uint32_t r02 = (w1 & 0x00FF00FFu) | magic;
                         const uint32_t r13 = ((w1 >> 8) & 0x00FF00FFu) | magic;
 #pragma unroll
-                        for (int b = 0; b < B; ++b) {
-                            a1[r][b] = dot2(p02, xq[b].x, a1[r][b]);
-                            a16[r][b] = dot2(p13, xq[b].y, a16[r][b]);
-                            a1[r][b] = dot2(r02, xq[b].z, a1[r][b]);
-                            a16[r][b] = dot2(r13, xq[b].w, a16[r][b]);
-                        }
+                        for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                a1[r][b] = dot2(p02, xq[pl][b].x, a1[r][b]);
+                                a16[r][b] = dot2(p13, xq[pl][b].y, a16[r][b]);
+                                a1[r][b] = dot2(r02, xq[pl][b].z, a1[r][b]);
+                                a16[r][b] = dot2(r13, xq[pl][b].w, a16[r][b]);
+                            }
                     }
                 }
             }

@@ -32,6 +32,11 @@
 //    the zero points are packed eight per uint32 along a row's groups.
 //    Mirai-L has signed 8-bit codes and a bf16 scale per group, w = s q;
 //    flipping each code's top bit gives u = q + 128, so c = -128 s.
+//
+// Activation modes (template parameter XF): 0 = fp16 (dot2 on packed
+// halves), 1 = bf16 staged as fp32 (fma), 2 = the rotation prologue of the
+// same page and section (RMSNorm, then a block-32 random Hadamard transform,
+// computed while staging and kept as hi/lo fp16 planes; see stage_x_rot).
 #include "common.h"
 #include "launch.h"
 
@@ -51,7 +56,17 @@ struct GemvArgs {
     int interleave;      // tile order: 1 = wave w takes tiles w, w + W, ...; 0 = a contiguous block
     const uint8_t* zp;   // Mirai-M zero points, zstride bytes per row
     int zstride;
+    const uint32_t* signs;   // XF == 2: rotation signs [K/32] (NULL = none)
+    const uint16_t* gamma;   // XF == 2: RMSNorm weight [K] in x's kind (NULL = no norm)
+    float eps;
 };
+
+// LDS of the rotation prologue (factors per vector and per-wave partial
+// sums). Only kernels that call this allocate it.
+__device__ __forceinline__ float* rot_shared() {
+    __shared__ float buf[kRotShared];
+    return buf;
+}
 
 enum WFmt : int { W_AFFINE = 0, W_MIRAI_M = 1, W_MIRAI_L = 2 };
 
@@ -99,6 +114,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         ntl = (int)((int64_t)ntiles * (gw + 1) / W) - t0;
     }
     const int nrounds = ntl * RPT;
+
+    // Rotation prologue: LDS for the per-vector factors (only kernels with
+    // XF == 2 reference it); rot[kRotMaxB + b] is 2^-e of vector b.
+    float* rot = nullptr;
+    if constexpr (XF == 2) rot = rot_shared();
 
     // Loads are unconditional inside a wave-uniform step test: rows past N and
     // chunks past the staged range read a clamped, valid address and get a
@@ -188,7 +208,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
                 const int row = tile * ROWS + r * RPI + seg;
 #pragma unroll
                 for (int bb = 0; bb < B; ++bb) {
-                    const float v = seg_sum<LPR>(y[r][bb]);
+                    float v = seg_sum<LPR>(y[r][bb]);
+                    if constexpr (XF == 2) v *= rot[kRotMaxB + bb];
                     y[r][bb] = 0.f;
                     if (sl == 0 && row < a.N && bb < a.nb) {
                         float* dst = a.y + (int64_t)bb * a.N + row;
@@ -205,7 +226,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 #ifdef QD_GEMV_DOUBLE_BUFFER
     Round<R, U, CPL> A, Bf;
     issue(A, 0);  // the first weights are in flight while the activations are staged
-    stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    if constexpr (XF == 2)
+        stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
+                               a.eps, rot, lds);
+    else
+        stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; rd += 2) {
         issue(Bf, rd + 1);
@@ -223,7 +248,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     // computes.
     Round<R, U, CPL> A;
     issue(A, 0);  // the first weights are in flight while the activations are staged
-    stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    if constexpr (XF == 2)
+        stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
+                               a.eps, rot, lds);
+    else
+        stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; ++rd) {
         if (rd > 0) issue(A, rd);
@@ -461,9 +490,9 @@ extern "C" int qd_tune_gemv[7] = {0, 0, 0, 0, 1, 4, -1};
 
 hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
                        const uint16_t* b, const uint32_t* zp, const void* x, int xkind, float* y,
-                       int N, int K, int batch, hipStream_t st) {
+                       int N, int K, int batch, hipStream_t st, const GemvRot* rot) {
     if ((fmt == W_MIRAI_M && bits != 4) || (fmt == W_MIRAI_L && bits != 8) ||
-        (fmt != W_AFFINE && batch > 8))
+        (fmt != W_AFFINE && batch > 8) || (rot && (fmt == W_AFFINE || xkind == X_F32)))
         return hipErrorInvalidValue;
     // a chunk of tokens through 8-bit weights (prefill routers): one
     // matrix-core launch instead of slices of 8
@@ -483,8 +512,26 @@ hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
         a.nb = std::min(8, batch - b0);
         a.zp = (const uint8_t*)zp;
         a.zstride = 4 * ((K / 64 + 7) / 8);
+        if (rot) {
+            a.signs = rot->signs;
+            a.gamma = rot->gamma;
+            a.eps = rot->eps;
+        }
         const int xf = xkind == X_F16 ? 0 : 1;
         Cfg c = default_cfg(bits, xf, a.nb, N, K);
+        if (c.cpl == 2 && c.u * c.r > (xf == 0 && !rot ? 4 : 2)) {
+            // Rounds of whole groups beyond these sizes exceed the 128 VGPRs of a
+            // 1024-thread workgroup once the activations are fp32 or two fp16
+            // planes (a spilled load result must wait for its load, which
+            // serializes the round): keep eight single-chunk steps, or one
+            // step of two rows, in flight instead.
+            if (c.r == 1) {
+                c.cpl = 1;
+                c.u = 8;
+            } else {
+                c.u = 1;
+            }
+        }
 #ifdef QD_TUNING
         if (qd_tune_gemv[0])
             c = Cfg{qd_tune_gemv[0], qd_tune_gemv[1], qd_tune_gemv[2], qd_tune_gemv[3],
@@ -493,7 +540,10 @@ hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
 #endif
         a.interleave = c.il;
         hipError_t e;
-        if (fmt == W_MIRAI_M)
+        if (rot)
+            e = fmt == W_MIRAI_M ? run_batch<4, 2, W_MIRAI_M>(a, c, st)
+                                 : run_batch<8, 2, W_MIRAI_L>(a, c, st);
+        else if (fmt == W_MIRAI_M)
             e = xf == 0 ? run_batch<4, 0, W_MIRAI_M>(a, c, st) : run_batch<4, 1, W_MIRAI_M>(a, c, st);
         else if (fmt == W_MIRAI_L)
             e = xf == 0 ? run_batch<8, 0, W_MIRAI_L>(a, c, st) : run_batch<8, 1, W_MIRAI_L>(a, c, st);

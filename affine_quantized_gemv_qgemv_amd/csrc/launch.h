@@ -24,13 +24,21 @@ int occupancy(const void* func, int threads, size_t lds_bytes);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
+// Rotation prologue of the Mirai formats: x -> H D (RMSNorm(x) * gamma) per
+// block of 32 inputs before the contraction.
+struct GemvRot {
+    const uint32_t* signs;   // [K/32], NULL = no sign flips
+    const uint16_t* gamma;   // [K] in x's kind, NULL = no RMSNorm
+    float eps;
+};
+
 // x kinds: 0 = fp16 bits, 1 = bf16 bits, 2 = fp32.
 // fmt: 0 = affine (fp16 s, b); 1 = Mirai-M (bits 4, bf16 s, zero points zp,
 // b unused); 2 = Mirai-L (bits 8, signed codes, bf16 s, b and zp unused).
-// The Mirai formats take batch <= 8.
+// The Mirai formats take batch <= 8 and optionally the rotation prologue.
 hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
                        const uint16_t* b, const uint32_t* zp, const void* x, int xkind, float* y,
-                       int N, int K, int batch, hipStream_t st);
+                       int N, int K, int batch, hipStream_t st, const GemvRot* rot = nullptr);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              hipStream_t st);

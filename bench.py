@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="weight sets cycled (0 = workload default)")
     p.add_argument("--format", default="affine", choices=["affine", "mirai-m", "mirai-l"],
                    help="weight format of the dense GEMV workloads (c1, c2, c5)")
+    p.add_argument("--rht", action="store_true",
+                   help="Mirai formats: fuse RMSNorm + the block-32 random Hadamard rotation "
+                        "ahead of the GEMV (qgemv_mirai_*_rht)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -66,8 +69,11 @@ def matrix_bytes(N: int, K: int, bits: int = 4, fmt: str = "affine") -> int:
     return N * K * bits // 8 + 2 * 2 * N * G
 
 
-def gemv_bytes(N: int, K: int, batch: int, bits: int = 4, fmt: str = "affine") -> int:
-    return matrix_bytes(N, K, bits, fmt) + batch * K * 2 + batch * N * 4
+def gemv_bytes(N: int, K: int, batch: int, bits: int = 4, fmt: str = "affine", rht: bool = False) -> int:
+    """Per launch: the matrix, fp16 activations in, fp32 outputs; with the
+    rotation prologue also the RMSNorm weights (fp16) and the sign bits."""
+    extra = K * 2 + K // 8 if rht else 0
+    return matrix_bytes(N, K, bits, fmt) + batch * K * 2 + batch * N * 4 + extra
 
 
 def source_hash(files) -> str:
@@ -152,8 +158,11 @@ def cpu_baseline_gemv(mats, seconds: float):
     done, nbytes = 0, 0
     t0 = time.perf_counter()
     while True:
-        for w, xb in mats:
-            if hasattr(w, "fmt"):
+        for w, xb, *rot in mats:
+            if rot:
+                oracle.mirai_gemv_rht(w, xb, "f16", rot[0], rot[1], 1e-6)
+                nbytes += gemv_bytes(w.N, w.K, xb.shape[0], fmt="mirai-" + w.fmt.lower(), rht=True)
+            elif hasattr(w, "fmt"):
                 oracle.mirai_gemv_x(w, xb)
                 nbytes += gemv_bytes(w.N, w.K, xb.shape[0], fmt="mirai-" + w.fmt.lower())
             else:
@@ -229,15 +238,19 @@ def make_sets(torch, shapes, nsets, cfg_id, fmt="affine"):
     return sets
 
 
-def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine"):
+def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine", rht=False):
     import synth
     nsets = len(sets)
-    xs, ys, xbits = [], [], []
+    xs, ys, xbits, rots = [], [], [], []
     for j, (K, N) in enumerate(shapes):
         xb = synth.x_f16(batch, K, cfg=cfg_id, set_id=1000 + j)
         xbits.append(xb)
         xs.append(to_dev_half(torch, xb))
         ys.append(torch.empty((batch, N), dtype=torch.float32, device="cuda"))
+        if rht:
+            sg = synth.rht_signs(K, cfg=cfg_id, set_id=1000 + j)
+            gb = synth.rmsnorm_gamma(K, cfg=cfg_id, set_id=1000 + j)
+            rots.append((to_dev_codes(torch, sg), to_dev_half(torch, gb), sg, gb))
 
     def step_fn(s, only=None):
         def f():
@@ -245,7 +258,13 @@ def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine"):
                 if only is not None and j != only:
                     continue
                 wq, sc, third = sets[s][j][:3]
-                if fmt == "affine":
+                if rht:
+                    sg, g = rots[j][:2]
+                    if fmt == "mirai-m":
+                        qd.qgemv_mirai_m_rht(wq, sc, third, xs[j], sg, g, 1e-6, out=ys[j])
+                    else:
+                        qd.qgemv_mirai_l_rht(wq, sc, xs[j], sg, g, 1e-6, out=ys[j])
+                elif fmt == "affine":
                     qd.qgemv_affine4(wq, sc, third, xs[j], out=ys[j])
                 elif fmt == "mirai-m":
                     qd.qgemv_mirai_m(wq, sc, third, xs[j], out=ys[j])
@@ -256,16 +275,18 @@ def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine"):
     timer = Timer(torch)
     steps = args.steps
     secs, wall = timer.run([step_fn(s) for s in range(nsets)], steps, args.warmup)
-    step_bytes = sum(gemv_bytes(N, K, batch, fmt=fmt) for K, N in shapes)
+    step_bytes = sum(gemv_bytes(N, K, batch, fmt=fmt, rht=rht) for K, N in shapes)
     per_shape = []
     for j, (K, N) in enumerate(shapes):
         sj, _ = timer.run([step_fn(s, j) for s in range(nsets)], max(nsets, steps // 2),
                           min(args.warmup, nsets))
         n = max(nsets, steps // 2)
         per_shape.append(dict(K=K, N=N, us=sj / n * 1e6,
-                              gbs=gemv_bytes(N, K, batch, fmt=fmt) * n / sj / 1e9))
+                              gbs=gemv_bytes(N, K, batch, fmt=fmt, rht=rht) * n / sj / 1e9))
+    cpu = [(sets[0][j][3], xbits[j]) + ((rots[j][2], rots[j][3]) if rht else ())
+           for j in range(len(shapes))]
     return dict(secs=secs, wall=wall, step_bytes=step_bytes, per_shape=per_shape,
-                launches_per_step=len(shapes), cpu_mats=[(sets[0][j][3], xbits[j]) for j in range(len(shapes))])
+                launches_per_step=len(shapes), cpu_mats=cpu)
 
 
 def bench_chunk(args, torch, qd):
@@ -452,6 +473,9 @@ def main():
             wl = ("c5: 70B-shaped decode, K=8192 -> N=28672 and K=28672 -> N=8192, int4 g64, "
                   "80 weight-set pairs cycled (21.1 GB)")
         fmt = args.format
+        rht = args.rht
+        if rht and fmt == "affine":
+            raise SystemExit("--rht applies to the Mirai formats (--format mirai-m or mirai-l)")
         if fmt != "affine":
             # same shapes; the Mirai-L matrices hold twice the code bytes, so
             # half as many sets keep the cycled footprint alike
@@ -465,7 +489,7 @@ def main():
         sets = make_sets(torch, shapes, nsets, cfg_id, fmt)
         results = []
         for batch in batches:
-            r = run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt)
+            r = run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt, rht)
             results.append((batch, r))
         batch, r = results[0]
         secs = r["secs"]
@@ -473,14 +497,15 @@ def main():
         # dominant kernel: the largest projection of the step, timed on its own
         dom = max(range(len(shapes)), key=lambda j: shapes[j][0] * shapes[j][1])
         dK, dN = shapes[dom]
-        bytes_per_launch = gemv_bytes(dN, dK, batch, fmt=fmt)
+        bytes_per_launch = gemv_bytes(dN, dK, batch, fmt=fmt, rht=rht)
         launch_s = r["per_shape"][dom]["us"] / 1e6
         achieved = bytes_per_launch / launch_s / 1e9
         kname = {"affine": "qgemv_affine4", "mirai-m": "qgemv_mirai_m",
-                 "mirai-l": "qgemv_mirai_l"}[fmt]
+                 "mirai-l": "qgemv_mirai_l"}[fmt] + ("_rht" if rht else "")
         traffic = stored_traffic(f"{kname}_{args.config}_traffic.json", GEMV_SOURCES)
         metric = METRIC if fmt == "affine" else \
-            f"achieved HBM GB/s (% of peak) for {fmt} GEMV at batch 1"
+            f"achieved HBM GB/s (% of peak) for {fmt} GEMV at batch 1" + \
+            (" with the fused RMSNorm + block-32 Hadamard prologue" if rht else "")
         out = {
             "metric": metric,
             "value": round(gbs, 1),
@@ -494,7 +519,9 @@ def main():
             "vs_baseline": None,
             "dtype": "f16",
             "data": "synthetic",
-            "config": {"workload": wl, "format": fmt, "batch": batch, "weight_sets": nsets,
+            "config": {"workload": wl + ("; RMSNorm + block-32 random Hadamard prologue fused"
+                                         if rht else ""),
+                       "format": fmt, "rht": rht, "batch": batch, "weight_sets": nsets,
                        "step_bytes": r["step_bytes"],
                        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                        "per_shape": [{k: (round(v, 3) if isinstance(v, float) else v)

@@ -117,6 +117,30 @@ qd_status qgemv_mirai_l(const uint32_t* wq, const uint16_t* scales,
                         qd_stream stream);
 
 /*
+ * Mirai GEMVs with the rotation prologue ([Mirai] quantization-format
+ * section: both formats quantize after a random Hadamard transform of
+ * block size 32, fused with RMSNorm and the matmul). For each t:
+ *   u = gamma ? x_t / sqrt(mean_k(x_t[k]^2) + eps) * gamma : x_t,
+ *   x'[32b + i] = 2^-2.5 * sum_j (-1)^popcount(i & j) * d_j * u[32b + j],
+ *   y[t][n] = sum_k w[n][k] * x'[k]   (w as qgemv_mirai_m / qgemv_mirai_l),
+ * with d_j = -1 where bit j of signs[b] is set.
+ *   signs [K/32] uint32 (NULL = no sign flips), gamma [K] in x's dtype
+ *   (NULL = no RMSNorm), eps finite and >= 0; the rest as the plain calls.
+ * The rotated activations never leave the kernel: they are formed in fp32
+ * and held as two fp16 parts with a per-vector power-of-two prescale.
+ */
+qd_status qgemv_mirai_m_rht(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                            const uint32_t* signs, const uint16_t* gamma, float eps,
+                            const uint16_t* x, qd_dtype x_dtype, float* y,
+                            int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                            qd_stream stream);
+qd_status qgemv_mirai_l_rht(const uint32_t* wq, const uint16_t* scales,
+                            const uint32_t* signs, const uint16_t* gamma, float eps,
+                            const uint16_t* x, qd_dtype x_dtype, float* y,
+                            int32_t N, int32_t K, int32_t batch, int32_t group_size,
+                            qd_stream stream);
+
+/*
  * Top-k routing ([TF] top and internals sections: each token uses only the
  * router's top-8 experts). For each token t: idx[t][0..k) are the experts
  * with the k largest logits in descending order, equal logits going to the

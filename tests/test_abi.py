@@ -156,3 +156,29 @@ def test_chunk_argument_errors():
     assert f(g=128) == qd.QD_ERR_UNSUPPORTED
     assert f(wq=None) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(x=MIS) == qd.QD_ERR_MISALIGNED
+
+
+def test_mirai_rht_argument_errors():
+    E = qd
+    L = qd.lib()
+
+    def m(wq=A, s=A, z=A, sg=A, g=A, eps=1e-6, x=A, dt=0, y=A, N=16, K=128, batch=1, gs=64):
+        return L.qgemv_mirai_m_rht(wq, s, z, sg, g, eps, x, dt, y, N, K, batch, gs, None)
+
+    def l(wq=A, s=A, sg=A, g=A, eps=1e-6, x=A, dt=1, y=A, N=16, K=128, batch=1, gs=64):
+        return L.qgemv_mirai_l_rht(wq, s, sg, g, eps, x, dt, y, N, K, batch, gs, None)
+
+    assert m(eps=-1.0) == E.QD_ERR_INVALID_ARGUMENT
+    assert "eps" in qd.last_error()
+    assert m(eps=float("nan")) == E.QD_ERR_INVALID_ARGUMENT
+    assert m(eps=float("inf")) == E.QD_ERR_INVALID_ARGUMENT
+    assert m(sg=MIS) == E.QD_ERR_MISALIGNED
+    assert m(g=MIS) == E.QD_ERR_MISALIGNED
+    assert m(z=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert m(batch=9) == E.QD_ERR_INVALID_ARGUMENT
+    assert m(K=32) == E.QD_ERR_INVALID_ARGUMENT
+    assert m(gs=32) == E.QD_ERR_UNSUPPORTED
+    assert l(eps=-0.5) == E.QD_ERR_INVALID_ARGUMENT
+    assert l(g=MIS) == E.QD_ERR_MISALIGNED
+    assert l(dt=3) == E.QD_ERR_UNSUPPORTED
+    assert l(y=None) == E.QD_ERR_INVALID_ARGUMENT
