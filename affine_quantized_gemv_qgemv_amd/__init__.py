@@ -31,6 +31,7 @@ QD_GELU_ERF, QD_GELU_TANH = 0, 1
 EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
+           "qgemm_affine4_verify",
            "qd_status_string", "qd_last_error")
 
 
@@ -79,13 +80,14 @@ def lib() -> ctypes.CDLL:
     L.qmoe_expert_gemv.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _I32, _I32, _P, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
     L.qd_status_string.argtypes = [ctypes.c_int]
     L.qd_status_string.restype = ctypes.c_char_p
     L.qd_last_error.argtypes = []
     L.qd_last_error.restype = ctypes.c_char_p
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
                "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
-               "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk"):
+               "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -346,4 +348,27 @@ def qgemm_affine4_chunk(wq, scales, biases, x, out=None):
     _need(out, "out", (torch.float32,), 2)
     _check(lib().qgemm_affine4_chunk(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), M, N,
                                      K, 64, _stream()))
+    return out
+
+
+def qgemm_affine4_verify(wq, scales, biases, x, out=None):
+    """Verification GEMM Y[m][n] = sum_k w[n][k] X[m][k] over drafted tokens, fp16 or bf16
+    X [M][K], M <= 128 (built for 9..64 tokens)."""
+    _need(wq, "wq", _CODES, 2)
+    _need(scales, "scales", _HALF, 2)
+    _need(biases, "biases", _HALF, 2)
+    _need(x, "x", (torch.float16, torch.bfloat16), 2)
+    N, K = wq.shape[0], wq.shape[1] * 8
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales/biases must be [N][K/64]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M][N]")
+    _check(lib().qgemm_affine4_verify(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _x_dtype(x),
+                                      _ptr(out), M, N, K, 64, _stream()))
     return out

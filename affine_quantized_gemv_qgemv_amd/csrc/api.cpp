@@ -318,6 +318,32 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
                     fn);
 }
 
+qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                               const uint16_t* x, qd_dtype x_dtype, float* y, int32_t M, int32_t N,
+                               int32_t K, int32_t group_size, qd_stream stream) {
+    const char* fn = "qgemm_affine4_verify";
+    qd_status st = check_matrix(fn, N, K, group_size);
+    if (st != QD_OK) return st;
+    if (M < 1 || M > 128)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: M = %d must be in [1, 128]", fn, M);
+    if (x_dtype != QD_F16 && x_dtype != QD_BF16)
+        return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
+    CHECK_PTR(wq);
+    CHECK_PTR(scales);
+    CHECK_PTR(biases);
+    CHECK_PTR(x);
+    CHECK_PTR(y);
+    // bf16 activations take the staged chunk kernel (its row tiles follow M);
+    // fp16 ones the token kernel, which reads them directly
+    if (x_dtype == QD_BF16)
+        return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, y, M, N, K,
+                                              (hipStream_t)stream),
+                        fn);
+    return from_hip(qd::launch_gemm4_tokens(wq, scales, biases, x, 0, y, N, K, M,
+                                            (hipStream_t)stream),
+                    fn);
+}
+
 const char* qd_status_string(qd_status s) {
     switch (s) {
         case QD_OK: return "QD_OK";

@@ -73,19 +73,23 @@ __device__ __forceinline__ int rot_group(int g, int G, int rot) {
     return g >= G ? g - G : g;
 }
 
-// One stage = SG groups of X (MT rows x 64 k each), staged by NT threads:
-// TPR = NT / MT threads share a row; thread part p holds k in
-// [64 p / TPR, 64 (p + 1) / TPR) of every group: XPT = 8 / TPR uint4 per group.
+// One stage = SG groups of X (MT rows x 64 k each), staged by the first NTS
+// of the NT threads (at most 8 per row; a multiple of 64, so whole waves
+// stage or skip): TPR = NTS / MT threads share a row; thread part p holds k
+// in [64 p / TPR, 64 (p + 1) / TPR) of every group: XPT = 8 / TPR uint4 per
+// group.
 template <int SG, int MT_, int NT>
 struct StageIO {
     static constexpr int MT = MT_;
-    static constexpr int TPR = NT / MT;
+    static constexpr int NTS = NT < 8 * MT ? NT : 8 * MT;
+    static constexpr int TPR = NTS / MT;
     static constexpr int XPT = 8 / TPR;
-    static_assert(TPR >= 1 && XPT >= 1, "staging split");
+    static_assert(TPR >= 1 && XPT >= 1 && NTS % 64 == 0, "staging split");
 
     __device__ static __forceinline__ void load(const ChunkArgs& a, int m0, int g0, int G, int rot,
                                                 uint4 (&xr)[SG][XPT]) {
         const int t = threadIdx.x;
+        if (NTS < NT && t >= NTS) return;
         const int m = m0 + t / TPR, part = t % TPR;
 #pragma unroll
         for (int gi = 0; gi < SG; ++gi) {
@@ -101,6 +105,7 @@ struct StageIO {
         // rows past M hold copies of row M - 1 (the loads clamp); they only
         // feed output rows that are never stored
         const int t = threadIdx.x;
+        if (NTS < NT && t >= NTS) return;
         const int r = t / TPR, part = t % TPR;
 #pragma unroll
         for (int gi = 0; gi < SG; ++gi) {
@@ -153,10 +158,15 @@ __device__ __forceinline__ int opaque(int v) {
 // Workgroup b takes column tile 8 (b / (8 RT)) + b % 8 and row tile
 // (b / 8) % RT, so the RT row tiles of a column tile run on one XCD and share
 // its L2 copy of the codes.
-template <int SG, int D, int MB, int WM, int NKS>
+//
+// XD = stages of X held in registers ahead of LDS: with 1, the next stage is
+// read while the current one is consumed; with 2 (small row tiles, whose
+// stages hold little matrix work) the stage after that is also in flight.
+template <int SG, int D, int MB, int WM, int NKS, int XD = 1>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
     constexpr int SPR = D / SG;     // stages per round
+    static_assert(XD == 1 || (XD == 2 && SPR % 2 == 0), "X prefetch depth");
     constexpr int JS = SG / NKS;    // groups per stage per wave
     constexpr int DW = D / NKS;     // ring slots per wave
     constexpr int WS = 2 * WM;      // waves per K-set
@@ -206,9 +216,12 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         bs[e] = srow[g];
         bb[e] = brow[g];
     }
-    uint4 xr[SG][IO::XPT];
-    IO::load(a, m0, 0, G, rot, xr);
-    IO::store(xs_raw, xsum_raw, xr);
+    // xr[i]: X of stage st + 1 + i while stage st runs (a ring when XD = 2;
+    // stage parity picks the slot, and rounds hold an even number of stages)
+    uint4 xr[XD][SG][IO::XPT];
+    IO::load(a, m0, 0, G, rot, xr[0]);
+    IO::store(xs_raw, xsum_raw, xr[0]);
+    if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
     __syncthreads();
 
     // one group (step g, slot e): MFMAs into P, then acc += s P, then the
@@ -316,7 +329,10 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     auto stage = [&](const int st, auto sjc, auto checked) __attribute__((always_inline)) {
         constexpr int sj = decltype(sjc)::value;
         const int buf = st & 1;
-        IO::load(a, m0, (st + 1) * SG, G, rot, xr);
+        // XD = 1: slot 0 receives stage st + 1; XD = 2: slot st % 2 receives
+        // stage st + 2 while slot (st + 1) % 2 holds stage st + 1
+        constexpr int ld = XD == 1 ? 0 : sj % 2, sv = XD == 1 ? 0 : (sj + 1) % 2;
+        IO::load(a, m0, (st + XD) * SG, G, rot, xr[ld]);
         bias_mfma(st, sjc, checked, xsum_raw + opaque(buf * SG * MT + ks));
         // group j of this wave is stage group NKS j + ks
         const uint4* xs = xs_raw + opaque(buf * L::XS + ks * MT * XS_STRIDE +
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
                 group(g, ec, xsj);
             }
         });
-        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr);
+        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr[sv]);
         __syncthreads();
     };
 
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     }
 }
 
-template <int SG, int D, int MB, int WM, int NKS>
+template <int SG, int D, int MB, int WM, int NKS, int XD = 1>
 static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st) {
     constexpr int MT = 32 * MB * WM;
     const int RT = (a.M + MT - 1) / MT;
@@ -389,7 +405,7 @@ static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st) {
     const size_t lds = ChunkLds<SG, MT>::bytes;
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     constexpr int threads = 128 * WM * NKS;
-    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS>;
+    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, XD>;
     (void)occupancy((const void*)kern, threads, lds);  // sets the dynamic-LDS limit once
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
     return hipGetLastError();
@@ -411,8 +427,13 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
     a.ncol_tiles = (N + CH_NT - 1) / CH_NT;
     a.x_row_stride = K;
     a.y_row_stride = N;
-// 4 groups per stage, ring depth 8 groups, each wave 4 row blocks (128 rows)
-// x 32 columns, 2 column waves x 4 K-sets = 8 waves (2 per SIMD).
+// Row tiles follow M (measured on K = 4096 -> N = 14336): up to 32 rows, one
+// row block per wave and two K-sets (4 waves); up to 64 rows, two row blocks
+// and four K-sets; beyond, the whole chunk as four row blocks per wave, 2
+// column waves x 4 K-sets = 8 waves (2 per SIMD). All use 4 groups per stage
+// and a ring of 8 groups.
+    if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2>(a, st);
+    if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4>(a, st);
     return launch_chunk_cfg<4, 8, 4, 1, 4>(a, st);
 }
 

@@ -69,6 +69,12 @@ hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,
                                hipStream_t st);
 
+// 4-bit weights over a few dozen tokens (f16 or bf16 activations) on the
+// matrix core: 32 tokens x 32 outputs per workgroup, K split over 8 waves.
+hipError_t launch_gemm4_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                               const uint16_t* x, int xkind, float* y, int N, int K, int T,
+                               hipStream_t st);
+
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x_bf16, float* y, int M, int N, int K,
                              hipStream_t st);

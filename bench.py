@@ -15,7 +15,8 @@ over time), the roofline of the dominant kernel, and the fp64 CPU oracle
 timed on a bounded sample of the same workload.
 
 Other workloads (``--config``): c1 (4096x4096 GEMV), c3 (MoE decode layer),
-c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8).
+c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8), verify
+(the verification GEMM over 16 and 32 drafted tokens on the c4 matrix).
 ``--format mirai-m`` / ``mirai-l`` runs c1, c2 and c5 on the Mirai weight
 formats of the uzu engine (4-bit codes with bf16 scale and 4-bit zero point
 per group of 64; signed 8-bit codes with bf16 scale per group of 64).
@@ -45,7 +46,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--config", default="c2",
-                   choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "stream"])
+                   choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "verify", "stream"])
     p.add_argument("--sets", type=int, default=0, help="weight sets cycled (0 = workload default)")
     p.add_argument("--format", default="affine", choices=["affine", "mirai-m", "mirai-l"],
                    help="weight format of the dense GEMV workloads (c1, c2, c5)")
@@ -325,6 +326,49 @@ def bench_chunk(args, torch, qd):
             "cpu_baseline": None}
 
 
+def bench_verify(args, torch, qd):
+    """Verification GEMM: M = 16 and 32 drafted tokens x K=4096 -> N=14336, int4
+    g64 weights, fp16 activations (the decode side's dtype; bf16 reported too),
+    fp32 output; 16 weight sets cycled (528 MB). Weight-stream bound at these M."""
+    import synth
+    K, N = 4096, 14336
+    nsets = args.sets or 16
+    sets = make_sets(torch, [(K, N)], nsets, 4)
+    rows = []
+    for M in (16, 32):
+        for dt in ("f16", "bf16"):
+            xb = synth.x_f16(M, K, cfg=4, set_id=2000 + M) if dt == "f16" else \
+                synth.x_bf16(M, K, cfg=4, set_id=2000 + M)
+            x = to_dev_half(torch, xb) if dt == "f16" else to_dev_bf16(torch, xb)
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+            def step(s, x=x, y=y):
+                def f():
+                    wq, sc, bi = sets[s][0][:3]
+                    qd.qgemm_affine4_verify(wq, sc, bi, x, out=y)
+                return f
+
+            secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)
+            t = secs / args.steps
+            nbytes = matrix_bytes(N, K) + M * K * 2 + M * N * 4
+            rows.append(dict(M=M, dtype=dt, us=round(t * 1e6, 2), GBps=round(nbytes / t / 1e9, 1),
+                             TFLOPs=round(2.0 * M * N * K / t / 1e12, 1), bytes=nbytes))
+    main_row = [r for r in rows if r["M"] == 32 and r["dtype"] == "f16"][0]
+    gbs = main_row["GBps"]
+    return {"metric": "verification GEMM achieved HBM GB/s (32 drafted tokens, int4 g64 weights)",
+            "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(main_row["us"] / 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": f"verify: M drafted tokens x K={K} -> N={N}, int4 g64, "
+                                   f"{nsets} weight sets cycled", "runs": rows},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "qgemm_affine4_verify M=32, fp16 activations",
+                         "bytes_per_launch": main_row["bytes"], "avg_launch_us": main_row["us"]},
+            "cpu_baseline": None}
+
+
 def device_affine(torch, gen, bits, shape_nk, extra=()):
     """Weights with the synth distributions, drawn on the device (fast enough to
     fill 30 MoE layers): uniform code words, scales U[0.002, 0.02] (x 15/255 for
@@ -550,6 +594,9 @@ def main():
         return
     if args.config == "c4":
         print(json.dumps(bench_chunk(args, torch, qd)), flush=True)
+        return
+    if args.config == "verify":
+        print(json.dumps(bench_verify(args, torch, qd)), flush=True)
         return
     if args.config in ("c3", "c4moe"):
         print(json.dumps(bench_moe(args, torch, qd, prefill=args.config == "c4moe")), flush=True)

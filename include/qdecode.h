@@ -17,7 +17,9 @@
  *   [Mirai] discuss.pytorch.kr/t/uzu-mac-iphone-llm-apple-silicon-rust/12363
  *         (uzu), section "uzu의 모델 변환과 Mirai 양자화 형식" (model
  *         conversion and the Mirai quantization formats): Mirai-M and
- *         Mirai-L, the two weight formats its checkpoints ship in.
+ *         Mirai-L, the two weight formats its checkpoints ship in; section
+ *         "추측 디코딩 구조" (speculative decoding): drafted tokens verified
+ *         in one forward pass.
  *
  * Data layout (all row-major, rows along the output dimension N):
  *   codes   uint32_t wq[N][K*bits/32]; code k of a row sits in word
@@ -202,6 +204,22 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
                               const uint16_t* x, float* y,
                               int32_t M, int32_t N, int32_t K, int32_t group_size,
                               qd_stream stream);
+
+/*
+ * Verification GEMM ([Mirai] speculative-decoding section: the target model
+ * checks 16 to 32 drafted tokens in one forward pass, so its projections
+ * become GEMMs over a few dozen tokens):
+ *   Y[m][n] = sum_k w[n][k] * X[m][k],  X [M][K] fp16 (QD_F16) or bf16
+ *   (QD_BF16) bits, Y [M][N] fp32, 1 <= M <= 128; 4-bit codes, scales and
+ *   biases as qgemv_affine4. Runs on fp16 / bf16 MFMA with the exact integer
+ *   codes as the matrix operand and the scales and biases applied per group
+ *   in fp32; built for the 9..64-token range between the GEMV kernels and a
+ *   prefill chunk.
+ */
+qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                               const uint16_t* x, qd_dtype x_dtype, float* y,
+                               int32_t M, int32_t N, int32_t K, int32_t group_size,
+                               qd_stream stream);
 
 /* Human-readable name of a status. */
 const char* qd_status_string(qd_status status);

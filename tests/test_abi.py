@@ -182,3 +182,19 @@ def test_mirai_rht_argument_errors():
     assert l(g=MIS) == E.QD_ERR_MISALIGNED
     assert l(dt=3) == E.QD_ERR_UNSUPPORTED
     assert l(y=None) == E.QD_ERR_INVALID_ARGUMENT
+
+
+def test_verify_argument_errors():
+    E = qd
+    L = qd.lib()
+
+    def v(wq=A, s=A, b=A, x=A, dt=0, y=A, M=16, N=16, K=128, gs=64):
+        return L.qgemm_affine4_verify(wq, s, b, x, dt, y, M, N, K, gs, None)
+
+    assert v(M=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(M=129) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(K=100) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(gs=128) == E.QD_ERR_UNSUPPORTED
+    assert v(dt=2) == E.QD_ERR_UNSUPPORTED
+    assert v(b=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(x=MIS) == E.QD_ERR_MISALIGNED
