@@ -11,6 +11,8 @@ Definitions followed (jeff.news/article/5193, TurboFieldfare; sections
 부분" (internals)): affine 4-bit group-64 weights with an 8-bit router,
 w = s*q + b; top-8 routing with renormalized weights; shared and routed
 expert outputs combined; prefill in chunks of at most 128 tokens.
+Decode attention follows the same article's internals section (circular KV
+for sliding-window layers, linear KV for full attention, exact attention).
 Mirai-M and Mirai-L weights follow the uzu page on discuss.pytorch.kr
 (section on model conversion and the Mirai quantization formats): 4-bit
 asymmetric codes with a 4-bit zero point and a bf16 scale per group of 64,
@@ -59,6 +61,10 @@ def _load():
     lib.qo_mirai_gemv.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
     lib.qo_rht.argtypes = [_P, _I64, _P, _P]
     lib.qo_rmsnorm.argtypes = [_P, _I64, _P, ctypes.c_double, _P]
+    lib.qo_attn_slot.argtypes = [_I64, _I64]
+    lib.qo_attn_slot.restype = _I64
+    lib.qo_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                   ctypes.c_double, _P, _P]
     lib.qo_set_threads.argtypes = [ctypes.c_int]
     lib.qo_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -234,6 +240,31 @@ def mirai_gemv_rht(w, x_bits, x_dtype="f16", signs=None, gamma_bits=None, eps: f
     xr = rht(xd, signs)
     y, a = mirai_gemv(w, xr, rows)
     return y, a, xr
+
+
+def attn_slot(pos: int, window: int) -> int:
+    return int(_load().qo_attn_slot(pos, window))
+
+
+def attn_decode(q, k_new, v_new, kc, vc, window: int, pos: int, scale: float):
+    """Decode attention of one token (fp64 inputs): q [Hq][D], k_new/v_new
+    [Hkv][D], caches [Hkv][cap][D]. Returns (out [Hq][D], A [Hq][D])."""
+    q2, pq = _c(q, np.float64)
+    kn, pkn = _c(k_new, np.float64)
+    vn, pvn = _c(v_new, np.float64)
+    k3, pk = _c(kc, np.float64)
+    v3, pv = _c(vc, np.float64)
+    Hq, D = q2.shape
+    Hkv, cap, D2 = k3.shape
+    if D2 != D or kn.shape != (Hkv, D) or vn.shape != (Hkv, D) or v3.shape != k3.shape:
+        raise ValueError("attention shapes")
+    if Hq % Hkv or pos < 0 or (window > 0 and cap != window) or (window == 0 and pos >= cap):
+        raise ValueError("attention sizes")
+    out = np.empty((Hq, D))
+    a = np.empty((Hq, D))
+    _load().qo_attn_decode(pq, pkn, pvn, pk, pv, Hq, Hkv, D, cap, window, pos, float(scale),
+                           out.ctypes.data_as(_P), a.ctypes.data_as(_P))
+    return out, a
 
 
 def route_topk(logits, k: int):

@@ -129,3 +129,25 @@ def moe_experts(mw, x, idx, p, act: int = 0):
         hs = ge(z[:mw.Is]) * z[mw.Is:]
         y[t] += dense(mw.sdn) @ hs
     return y
+
+
+def attn_decode(q, k_new, v_new, kc, vc, window: int, pos: int, scale: float):
+    """Decode attention by a second route: copy the caches, store the new
+    token at its slot, keep the occupied slots, and use scipy's softmax and
+    numpy matrix products per query head."""
+    from scipy.special import softmax
+    q = np.asarray(q, np.float64)
+    kc = np.array(kc, np.float64)
+    vc = np.array(vc, np.float64)
+    Hq, D = q.shape
+    Hkv, cap, _ = kc.shape
+    slot = pos - (pos // window) * window if window else pos
+    kc[:, slot] = k_new
+    vc[:, slot] = v_new
+    n = min(pos + 1, window) if window else pos + 1
+    out = np.zeros((Hq, D))
+    for h in range(Hq):
+        hk = h // (Hq // Hkv)
+        p = softmax(scale * (kc[hk, :n] @ q[h]))
+        out[h] = p @ vc[hk, :n]
+    return out

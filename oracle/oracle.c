@@ -10,6 +10,9 @@
  *   [uzu]  discuss.pytorch.kr/t/uzu-mac-iphone-llm-apple-silicon-rust/12363
  *          (uzu, an on-device engine), section "uzu의 모델 변환과 Mirai 양자화
  *          형식" (model conversion and the Mirai quantization formats).
+ *   [TF] internals section also fixes the KV storage of the decode step:
+ *          sliding-window layers keep a bounded circular KV store, full-
+ *          attention layers a linear one, and decode attention is exact.
  * Plain loops, fp64 throughout; OpenMP only splits independent output rows
  * (each row's sum is still taken in ascending k).
  */
@@ -349,4 +352,59 @@ void qo_rmsnorm(const double* x, int64_t K, const double* gamma, double eps, dou
     for (int64_t k = 0; k < K; ++k) ss += x[k] * x[k];
     const double r = 1.0 / sqrt(ss / (double)K + eps);
     for (int64_t k = 0; k < K; ++k) out[k] = x[k] * r * (gamma ? gamma[k] : 1.0);
+}
+
+/*
+ * Decode attention for one new token ([TF] internals section: sliding-window
+ * layers keep their keys and values in bounded circular storage, full-
+ * attention layers in linear storage, and decode attention is computed
+ * exactly). Readings where the page is silent: the token at position pos is
+ * stored at slot pos mod window (circular, cap == window) or at slot pos
+ * (linear, window == 0); the step first stores the new key and value there,
+ * then attends over the occupied slots [0, n) with n = min(pos + 1, window)
+ * or pos + 1, which are exactly the positions inside the window. Query head
+ * h reads key/value head h / (Hq / Hkv). Plain definition, in fp64:
+ *   s_j = scale * sum_d q[h][d] k[hk][j][d],  p = softmax_j(s),
+ *   out[h][d] = sum_j p_j v[hk][j][d],  a[h][d] = sum_j p_j |v[hk][j][d]|.
+ * kc / vc are [Hkv][cap][D]; they are read, never written (slot_of returns
+ * the slot the new token occupies, where k_new / v_new are used instead).
+ */
+int64_t qo_attn_slot(int64_t pos, int64_t window) { return window > 0 ? pos % window : pos; }
+
+void qo_attn_decode(const double* q, const double* k_new, const double* v_new,
+                    const double* kc, const double* vc, int64_t Hq, int64_t Hkv, int64_t D,
+                    int64_t cap, int64_t window, int64_t pos, double scale,
+                    double* out, double* a) {
+    const int64_t n = window > 0 ? (pos + 1 < window ? pos + 1 : window) : pos + 1;
+    const int64_t slot = qo_attn_slot(pos, window);
+    const int64_t grp = Hq / Hkv;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t hk = h / grp;
+        const double* qh = q + h * D;
+        double smax = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {
+            const double* kj = j == slot ? k_new + hk * D : kc + (hk * cap + j) * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += qh[d] * kj[d];
+            sc[j] = scale * acc;
+            if (sc[j] > smax) smax = sc[j];
+        }
+        double z = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            sc[j] = exp(sc[j] - smax);
+            z += sc[j];
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double* vj = j == slot ? v_new + hk * D : vc + (hk * cap + j) * D;
+                acc += sc[j] / z * vj[d];
+                aacc += sc[j] / z * fabs(vj[d]);
+            }
+            out[h * D + d] = acc;
+            if (a) a[h * D + d] = aacc;
+        }
+    }
+    free(sc);
 }

@@ -108,6 +108,20 @@ void qo_rht(const double* x, int64_t K, const uint32_t* signs, double* out);
 /* RMSNorm: out = x / sqrt(mean(x^2) + eps) * gamma (gamma NULL = 1). */
 void qo_rmsnorm(const double* x, int64_t K, const double* gamma, double eps, double* out);
 
+/*
+ * Decode attention for one token (TurboFieldfare article, internals section:
+ * circular KV storage for sliding-window layers, linear for full attention,
+ * exact decode attention). q [Hq][D]; k_new, v_new [Hkv][D]; kc, vc
+ * [Hkv][cap][D] (read only: slot qo_attn_slot(pos, window) takes k_new /
+ * v_new); window 0 = full attention (linear, pos < cap), else circular with
+ * cap == window. out, a [Hq][D]: the attention output and sum_j p_j |v_j|.
+ */
+int64_t qo_attn_slot(int64_t pos, int64_t window);
+void qo_attn_decode(const double* q, const double* k_new, const double* v_new,
+                    const double* kc, const double* vc, int64_t Hq, int64_t Hkv, int64_t D,
+                    int64_t cap, int64_t window, int64_t pos, double scale,
+                    double* out, double* a);
+
 /* Number of OpenMP threads the oracle uses (0 = runtime default). */
 void qo_set_threads(int n);
 int qo_get_threads(void);

@@ -196,6 +196,16 @@ def rmsnorm_gamma(K: int, cfg: int, set_id: int, dtype: str = "f16") -> np.ndarr
     return f32_to_bf16_bits(g.astype(np.float32))
 
 
+def attn_inputs(Hq: int, Hkv: int, D: int, cap: int, cfg: int, set_id: int,
+                scale_q: float = 1.0) -> dict:
+    """Decode-attention inputs as fp16 bits, all N(0, 1) (queries times scale_q):
+    q [Hq][D], k_new / v_new [Hkv][D], k_cache / v_cache [Hkv][cap][D]."""
+    r = rng(cfg, set_id, T_X)
+    f = lambda shape, sc=1.0: (r.standard_normal(shape) * sc).astype(np.float16).view(np.uint16)
+    return dict(q=f((Hq, D), scale_q), k_new=f((Hkv, D)), v_new=f((Hkv, D)),
+                k_cache=f((Hkv, cap, D)), v_cache=f((Hkv, cap, D)))
+
+
 def x_f16(T: int, K: int, cfg: int, set_id: int, tensor: int = T_X) -> np.ndarray:
     """Decode activations: fp16 N(0,1), returned as uint16 bits [T][K]."""
     return rng(cfg, set_id, tensor).standard_normal((T, K)).astype(np.float16).view(np.uint16)

@@ -558,3 +558,85 @@ def test_rht_generators():
     assert 0.4 < bits.mean() < 0.6
     g = brute.f16(synth.rmsnorm_gamma(1024, cfg=3, set_id=0))
     assert g.min() >= 0.5 and g.max() <= 1.5
+
+
+# ---------------------------------------------------------------- decode attention
+# jeff.news/article/5193 (TurboFieldfare), internals section: circular KV for
+# sliding-window layers, linear KV for full attention, exact decode attention.
+
+def _attn_case(Hq, Hkv, D, cap, seed, scale_q=1.0):
+    t = synth.attn_inputs(Hq, Hkv, D, cap, cfg=140, set_id=seed, scale_q=scale_q)
+    return {k: brute.f16(v) for k, v in t.items()}
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,cap,window,pos", [
+    (4, 2, 64, 40, 0, 0), (4, 2, 64, 40, 0, 17), (4, 2, 64, 40, 0, 39),
+    (6, 3, 32, 16, 16, 5), (6, 3, 32, 16, 16, 15), (6, 3, 32, 16, 16, 16), (6, 3, 32, 16, 16, 37),
+    (2, 2, 128, 8, 0, 7), (8, 1, 64, 24, 24, 100)])
+def test_attn_matches_bruteforce(Hq, Hkv, D, cap, window, pos):
+    t = _attn_case(Hq, Hkv, D, cap, seed=Hq * 100 + pos)
+    sc = 1.0 / math.sqrt(D)
+    out, a = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], window, pos, sc)
+    ob = brute.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], window, pos, sc)
+    assert np.allclose(out, ob, rtol=0, atol=1e-13)
+    assert np.all(a >= np.abs(out) - 1e-15)
+
+
+def test_attn_first_token_returns_its_value():
+    t = _attn_case(4, 2, 64, 10, seed=1)
+    out, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], 0, 0, 0.125)
+    assert np.array_equal(out, np.repeat(t["v_new"], 2, axis=0))
+
+
+def test_attn_equal_keys_give_the_mean_value():
+    Hq, Hkv, D, cap, pos = 4, 2, 32, 12, 9
+    t = _attn_case(Hq, Hkv, D, cap, seed=2)
+    kc = np.repeat(t["k_new"][:, None, :], cap, axis=1)
+    out, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], kc, t["v_cache"], 0, pos, 0.2)
+    vals = t["v_cache"].copy()
+    vals[:, pos] = t["v_new"]
+    expect = np.repeat(vals[:, :pos + 1].mean(axis=1), 2, axis=0)
+    assert np.allclose(out, expect, rtol=0, atol=1e-14)
+
+
+def test_attn_circular_equals_linear_over_the_window():
+    # a window of W: the circular store after position pos holds positions
+    # pos-W+1 .. pos at slots p mod W; laid out in order they form a linear
+    # store, and attention over either gives the same result
+    Hq, Hkv, D, W, pos = 4, 2, 32, 8, 21
+    t = _attn_case(Hq, Hkv, D, W, seed=3)
+    circ, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], W, pos, 0.3)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    kc[:, pos % W], vc[:, pos % W] = t["k_new"], t["v_new"]
+    order = [p % W for p in range(pos - W + 1, pos + 1)]
+    kl, vl = kc[:, order], vc[:, order]          # positions in order; the last is the new token
+    lin, _ = oracle.attn_decode(t["q"], kl[:, -1], vl[:, -1], kl, vl, 0, W - 1, 0.3)
+    assert np.allclose(circ, lin, rtol=0, atol=1e-14)
+
+
+def test_attn_overwritten_position_has_no_effect():
+    Hq, Hkv, D, W, pos = 2, 1, 16, 6, 14       # slot 2 held position 8, now position 14
+    t = _attn_case(Hq, Hkv, D, W, seed=4)
+    o1, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], W, pos, 0.25)
+    kc, vc = t["k_cache"].copy(), t["v_cache"].copy()
+    kc[:, pos % W] += 100.0
+    vc[:, pos % W] -= 50.0
+    o2, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], kc, vc, W, pos, 0.25)
+    assert np.array_equal(o1, o2)
+    # and a slot still inside the window does matter
+    kc2 = t["k_cache"].copy()
+    kc2[:, (pos + 1) % W] += 3.0
+    o3, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], kc2, t["v_cache"], W, pos, 0.25)
+    assert not np.array_equal(o1, o3)
+
+
+def test_attn_large_scores_are_stable():
+    t = _attn_case(2, 1, 64, 20, seed=5, scale_q=400.0)
+    out, _ = oracle.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], 0, 19, 1.0)
+    ob = brute.attn_decode(t["q"], t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], 0, 19, 1.0)
+    assert np.all(np.isfinite(out)) and np.allclose(out, ob, rtol=0, atol=1e-12)
+
+
+def test_attn_slot_rule():
+    assert [oracle.attn_slot(p, 4) for p in range(9)] == [0, 1, 2, 3, 0, 1, 2, 3, 0]
+    assert [oracle.attn_slot(p, 0) for p in (0, 5, 4095)] == [0, 5, 4095]

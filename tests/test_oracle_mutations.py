@@ -59,6 +59,14 @@ MUTATIONS = {
     "rmsnorm mean over K-1": ("const double r = 1.0 / sqrt(ss / (double)K + eps);",
                               "const double r = 1.0 / sqrt(ss / (double)(K - 1) + eps);"),
     "rmsnorm gamma ignored": ("out[k] = x[k] * r * (gamma ? gamma[k] : 1.0);", "out[k] = x[k] * r;"),
+    "attention head group": ("const int64_t hk = h / grp;", "const int64_t hk = h % Hkv;"),
+    "attention slot shifted": ("int64_t qo_attn_slot(int64_t pos, int64_t window) { return window > 0 ? pos % window : pos; }",
+                               "int64_t qo_attn_slot(int64_t pos, int64_t window) { return window > 0 ? (pos + 1) % window : pos; }"),
+    "attention window short": ("const int64_t n = window > 0 ? (pos + 1 < window ? pos + 1 : window) : pos + 1;",
+                               "const int64_t n = window > 0 ? (pos + 1 < window ? pos + 1 : window - 1) : pos + 1;"),
+    "attention scale dropped": ("sc[j] = scale * acc;", "sc[j] = acc + 0.0 * scale;"),
+    "attention unnormalized": ("acc += sc[j] / z * vj[d];", "acc += sc[j] * vj[d] + 0.0 * z;"),
+    "attention no max shift": ("sc[j] = exp(sc[j] - smax);", "sc[j] = exp(sc[j]) + 0.0 * smax;"),
     "shared expert halved": ("yt[n] += o[n];\n            if (at) at[n] += oa[n];\n        }\n    }",
                              "yt[n] += 0.5 * o[n];\n            if (at) at[n] += oa[n];\n        }\n    }"),
 }
@@ -92,6 +100,13 @@ PIN_CALLS = [
     (pins.test_rht_is_orthogonal_and_self_inverse_without_signs, {}),
     (pins.test_rmsnorm_closed_forms, {}),
     (pins.test_mirai_gemv_with_rotation_prologue_matches_bruteforce, {"fmt": "M"}),
+    (pins.test_attn_matches_bruteforce, {"Hq": 6, "Hkv": 3, "D": 32, "cap": 16, "window": 16, "pos": 37}),
+    (pins.test_attn_matches_bruteforce, {"Hq": 4, "Hkv": 2, "D": 64, "cap": 40, "window": 0, "pos": 17}),
+    (pins.test_attn_first_token_returns_its_value, {}),
+    (pins.test_attn_equal_keys_give_the_mean_value, {}),
+    (pins.test_attn_circular_equals_linear_over_the_window, {}),
+    (pins.test_attn_large_scores_are_stable, {}),
+    (pins.test_attn_slot_rule, {}),
 ]
 
 
