@@ -31,7 +31,7 @@ QD_GELU_ERF, QD_GELU_TANH = 0, 1
 EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
-           "qgemm_affine4_verify",
+           "qgemm_affine4_verify", "qattn_decode_workspace_bytes", "qattn_decode",
            "qd_status_string", "qd_last_error")
 
 
@@ -81,13 +81,18 @@ def lib() -> ctypes.CDLL:
                                    _P, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
     L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qattn_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
+    L.qattn_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.qattn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                               _P, _P, ctypes.c_size_t, _P]
     L.qd_status_string.argtypes = [ctypes.c_int]
     L.qd_status_string.restype = ctypes.c_char_p
     L.qd_last_error.argtypes = []
     L.qd_last_error.restype = ctypes.c_char_p
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
                "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
-               "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify"):
+               "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify",
+               "qattn_decode"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -371,4 +376,37 @@ def qgemm_affine4_verify(wq, scales, biases, x, out=None):
         raise ValueError("out must be [M][N]")
     _check(lib().qgemm_affine4_verify(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _x_dtype(x),
                                       _ptr(out), M, N, K, 64, _stream()))
+    return out
+
+
+def qattn_workspace_bytes(Hq: int, Hkv: int, D: int, cap: int) -> int:
+    return int(lib().qattn_decode_workspace_bytes(Hq, Hkv, D, cap))
+
+
+def qattn_decode(q, k_new, v_new, k_cache, v_cache, pos: int, window: int = 0, scale=None,
+                 out=None, workspace=None):
+    """Decode attention of one token: stores k_new / v_new at the token's slot of the
+    fp16 caches [Hkv][cap][D] (circular when window > 0), then attends over the
+    occupied slots. q [Hq][D], k_new / v_new [Hkv][D] fp16; returns out [Hq][D] fp32."""
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, (torch.float16,), 2)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, (torch.float16,), 3)
+    Hq, D = q.shape
+    Hkv, cap, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(k_new.shape) != (Hkv, D) \
+            or tuple(v_new.shape) != (Hkv, D):
+        raise ValueError("attention shapes do not match")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 2)
+    need = qattn_workspace_bytes(Hq, Hkv, D, cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().qattn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              Hq, Hkv, D, cap, window, pos, float(scale), _ptr(out),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream()))
     return out

@@ -344,6 +344,52 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
                     fn);
 }
 
+size_t qattn_decode_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t cap) {
+    if (Hq < 1 || Hkv < 1 || D < 1 || cap < 1) return 0;
+    return qd::attn_workspace_bytes(Hq, Hkv, D, cap);
+}
+
+qd_status qattn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                       uint16_t* k_cache, uint16_t* v_cache, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t cap, int32_t window, int32_t pos, float scale, float* out,
+                       void* workspace, size_t ws_bytes, qd_stream stream) {
+    const char* fn = "qattn_decode";
+    if (D != 64 && D != 128 && D != 256)
+        return fail(QD_ERR_UNSUPPORTED, "%s: head dim %d (64, 128 or 256)", fn, D);
+    if (Hkv < 1 || Hq < 1 || Hq % Hkv)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: Hq = %d must be a positive multiple of Hkv = %d",
+                    fn, Hq, Hkv);
+    const int g = Hq / Hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(QD_ERR_UNSUPPORTED, "%s: %d query heads per key/value head (1, 2, 4 or 8)", fn, g);
+    if (cap < 1 || cap > (1 << 24))
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: cap = %d must be in [1, 2^24]", fn, cap);
+    if (window < 0 || (window > 0 && window != cap))
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: window = %d must be 0 or equal cap = %d", fn,
+                    window, cap);
+    if (pos < 0 || (window == 0 && pos >= cap))
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: pos = %d out of range for cap = %d", fn, pos, cap);
+    if (!(scale == scale) || scale > 3e38f || scale < -3e38f)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: scale must be finite", fn);
+    CHECK_PTR(q);
+    CHECK_PTR(k_new);
+    CHECK_PTR(v_new);
+    CHECK_PTR(k_cache);
+    CHECK_PTR(v_cache);
+    CHECK_PTR(out);
+    const size_t need = qd::attn_workspace_bytes(Hq, Hkv, D, cap);
+    if (!workspace)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned16(workspace))
+        return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (ws_bytes < need)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    return from_hip(qd::launch_attn_decode(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, cap,
+                                           window, pos, scale, out, workspace,
+                                           (hipStream_t)stream),
+                    fn);
+}
+
 const char* qd_status_string(qd_status s) {
     switch (s) {
         case QD_OK: return "QD_OK";

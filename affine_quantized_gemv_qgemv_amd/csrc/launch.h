@@ -75,6 +75,13 @@ hipError_t launch_gemm4_tokens(const uint32_t* wq, const uint16_t* s, const uint
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,
                                hipStream_t st);
 
+// Decode attention of one token over fp16 KV caches (circular when window > 0).
+size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap);
+hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              uint16_t* kc, uint16_t* vc, int Hq, int Hkv, int D, int cap,
+                              int window, int pos, float scale, float* out, void* ws,
+                              hipStream_t st);
+
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x_bf16, float* y, int M, int N, int K,
                              hipStream_t st);

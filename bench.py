@@ -16,7 +16,9 @@ timed on a bounded sample of the same workload.
 
 Other workloads (``--config``): c1 (4096x4096 GEMV), c3 (MoE decode layer),
 c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8), verify
-(the verification GEMM over 16 and 32 drafted tokens on the c4 matrix).
+(the verification GEMM over 16 and 32 drafted tokens on the c4 matrix),
+attn (decode attention of one token through 25 sliding-window and 5
+full-attention layers).
 ``--format mirai-m`` / ``mirai-l`` runs c1, c2 and c5 on the Mirai weight
 formats of the uzu engine (4-bit codes with bf16 scale and 4-bit zero point
 per group of 64; signed 8-bit codes with bf16 scale per group of 64).
@@ -46,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--config", default="c2",
-                   choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "verify", "stream"])
+                   choices=["c1", "c2", "c3", "c4", "c4moe", "c5", "verify", "attn", "stream"])
     p.add_argument("--sets", type=int, default=0, help="weight sets cycled (0 = workload default)")
     p.add_argument("--format", default="affine", choices=["affine", "mirai-m", "mirai-l"],
                    help="weight format of the dense GEMV workloads (c1, c2, c5)")
@@ -369,6 +371,71 @@ def bench_verify(args, torch, qd):
             "cpu_baseline": None}
 
 
+def bench_attn(args, torch, qd):
+    """Decode attention of one token through a 30-layer stack: 25 sliding-window
+    layers (circular KV, window 1024) and 5 full-attention layers (linear KV of
+    4096 positions, the cache full), 16 query heads over 8 key/value heads of
+    dim 128, fp16 KV. Four such stacks (different sequences) are cycled so the
+    756 MB of KV stream from HBM. A step = one token through the 30 layers."""
+    Hq, Hkv, D, W, C = 16, 8, 128, 1024, 4096
+    nstack = args.sets or 4
+    layers = [("sliding", W, W)] * 25 + [("full", C, 0)] * 5
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(97)
+    stacks = []
+    for _ in range(nstack):
+        st = []
+        for kind, cap, window in layers:
+            kc = torch.randn((Hkv, cap, D), device="cuda", generator=gen).half()
+            vc = torch.randn((Hkv, cap, D), device="cuda", generator=gen).half()
+            st.append((kc, vc, cap, window))
+        stacks.append(st)
+    q = torch.randn((Hq, D), device="cuda", generator=gen).half()
+    kn = torch.randn((Hkv, D), device="cuda", generator=gen).half()
+    vn = torch.randn((Hkv, D), device="cuda", generator=gen).half()
+    out = torch.empty((Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qd.qattn_workspace_bytes(Hq, Hkv, D, C), dtype=torch.uint8, device="cuda")
+    pos = C - 1
+
+    def step(si, only=None):
+        def f():
+            for li, (kc, vc, cap, window) in enumerate(stacks[si]):
+                if only is not None and layers[li][0] != only:
+                    continue
+                qd.qattn_decode(q, kn, vn, kc, vc, pos, window, out=out, workspace=ws)
+        return f
+
+    def kv_bytes(cap_n):
+        return 2 * Hkv * cap_n * D * 2 + (Hq * D * 2 + 2 * Hkv * D * 2 + Hq * D * 4)
+
+    step_bytes = sum(kv_bytes(cap) for _, cap, _ in layers)
+    timer = Timer(torch)
+    secs, _ = timer.run([step(i) for i in range(nstack)], args.steps, args.warmup)
+    t = secs / args.steps
+    per = {}
+    for kind, cap in (("sliding", W), ("full", C)):
+        nl = sum(1 for l in layers if l[0] == kind)
+        sk, _ = timer.run([step(i, kind) for i in range(nstack)], args.steps, min(args.warmup, 8))
+        us = sk / args.steps / nl * 1e6
+        per[kind] = dict(layers=nl, positions=cap, us_per_layer=round(us, 2),
+                         GBps=round(kv_bytes(cap) / us / 1e3, 1))
+    gbs = step_bytes / t / 1e9
+    dom = per["full"]
+    return {"metric": "decode attention achieved HBM GB/s (30-layer step, fp16 KV)",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(t * 1e3, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "attn: one decode token through 25 sliding-window (window 1024, "
+                                   "circular KV) + 5 full-attention (4096 positions, linear KV) layers, "
+                                   f"Hq=16, Hkv=8, D=128, fp16 KV; {nstack} stacks cycled",
+                       "step_bytes": step_bytes, "us_per_step": round(t * 1e6, 2), "per_kind": per},
+            "roofline": {"bound": "hbm", "achieved": dom["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "qattn_decode, full-attention layer (4096 positions)",
+                         "bytes_per_launch": kv_bytes(C), "avg_launch_us": dom["us_per_layer"]},
+            "cpu_baseline": None}
+
+
 def device_affine(torch, gen, bits, shape_nk, extra=()):
     """Weights with the synth distributions, drawn on the device (fast enough to
     fill 30 MoE layers): uniform code words, scales U[0.002, 0.02] (x 15/255 for
@@ -597,6 +664,9 @@ def main():
         return
     if args.config == "verify":
         print(json.dumps(bench_verify(args, torch, qd)), flush=True)
+        return
+    if args.config == "attn":
+        print(json.dumps(bench_attn(args, torch, qd)), flush=True)
         return
     if args.config in ("c3", "c4moe"):
         print(json.dumps(bench_moe(args, torch, qd, prefill=args.config == "c4moe")), flush=True)

@@ -221,6 +221,32 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
                                int32_t M, int32_t N, int32_t K, int32_t group_size,
                                qd_stream stream);
 
+/*
+ * Decode attention for one new token ([TF] internals section: sliding-window
+ * layers keep keys and values in bounded circular storage, full-attention
+ * layers in linear storage, and decode attention is exact).
+ *   q [Hq][D], k_new / v_new [Hkv][D]: fp16 bits of the token's query, key
+ *   and value (already normed and rotated as the model requires);
+ *   k_cache / v_cache [Hkv][cap][D] fp16 bits, read and updated in place:
+ *   the token at position pos is stored at slot pos mod window when
+ *   window > 0 (circular storage, window == cap) or at slot pos when
+ *   window == 0 (linear storage, pos < cap);
+ *   out [Hq][D] fp32: for query head h and its key/value head
+ *   hk = h / (Hq / Hkv),  out[h] = sum_j softmax_j(scale q_h . k_j) v_j over
+ *   the occupied slots j < min(pos + 1, window) (or pos + 1): exactly the
+ *   positions inside the window.
+ *   D in {64, 128, 256}; Hq / Hkv in {1, 2, 4, 8}; scale finite.
+ *   workspace: device scratch of at least qattn_decode_workspace_bytes().
+ * The call first stores k_new / v_new at the token's slot, so the caches
+ * must not be read or written by other work until the stream reaches it.
+ */
+size_t qattn_decode_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t cap);
+qd_status qattn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                       uint16_t* k_cache, uint16_t* v_cache,
+                       int32_t Hq, int32_t Hkv, int32_t D, int32_t cap, int32_t window,
+                       int32_t pos, float scale, float* out,
+                       void* workspace, size_t ws_bytes, qd_stream stream);
+
 /* Human-readable name of a status. */
 const char* qd_status_string(qd_status status);
 

@@ -198,3 +198,29 @@ def test_verify_argument_errors():
     assert v(dt=2) == E.QD_ERR_UNSUPPORTED
     assert v(b=None) == E.QD_ERR_INVALID_ARGUMENT
     assert v(x=MIS) == E.QD_ERR_MISALIGNED
+
+
+def test_attention_argument_errors():
+    E = qd
+    L = qd.lib()
+    ws = qd.qattn_workspace_bytes(16, 8, 128, 4096)
+    assert ws > 0
+
+    def at(q=A, kn=A, vn=A, kc=A, vc=A, Hq=16, Hkv=8, D=128, cap=4096, window=0, pos=10,
+           scale=0.088, out=A, w=A, wsb=ws):
+        return L.qattn_decode(q, kn, vn, kc, vc, Hq, Hkv, D, cap, window, pos, scale, out, w, wsb, None)
+
+    assert at(D=96) == E.QD_ERR_UNSUPPORTED
+    assert at(Hq=12) == E.QD_ERR_INVALID_ARGUMENT     # 12 is not a multiple of 8
+    assert "multiple" in qd.last_error()
+    assert at(Hq=24, Hkv=8) == E.QD_ERR_UNSUPPORTED   # groups of 3
+    assert at(pos=4096) == E.QD_ERR_INVALID_ARGUMENT
+    assert at(pos=-1) == E.QD_ERR_INVALID_ARGUMENT
+    assert at(window=1024) == E.QD_ERR_INVALID_ARGUMENT   # circular storage needs cap == window
+    assert at(scale=float("nan")) == E.QD_ERR_INVALID_ARGUMENT
+    assert at(kc=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert at(q=MIS) == E.QD_ERR_MISALIGNED
+    assert at(w=None) == E.QD_ERR_WORKSPACE
+    assert at(wsb=ws - 1) == E.QD_ERR_WORKSPACE
+    # circular storage accepts any position
+    assert qd.qattn_workspace_bytes(16, 8, 128, 1024) <= ws
