@@ -201,17 +201,17 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
         for (int s = 0; s < a.nsplit; ++s) L = fmaf(ls[s], cs[s], L);
         Ls = L;
     }
-    // o over the splits in order, eight independent loads at a time
+    // o over the splits in order; each batch of 32 loads is issued before
+    // any is used (clamped indices, weight 0 past the end), so a combine
+    // costs about one memory latency per 32 splits
     float O = 0.f;
-    int s = 0;
-    for (; s + 8 <= a.nsplit; s += 8) {
-        float v[8];
+    for (int s0 = 0; s0 < a.nsplit; s0 += 32) {
+        float v[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = p[(s + i) * stride + d];
+        for (int i = 0; i < 32; ++i) v[i] = p[min(s0 + i, a.nsplit - 1) * stride + d];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) O = fmaf(v[i], cs[s + i], O);
+        for (int i = 0; i < 32; ++i) O = fmaf(v[i], s0 + i < a.nsplit ? cs[s0 + i] : 0.f, O);
     }
-    for (; s < a.nsplit; ++s) O = fmaf(p[s * stride + d], cs[s], O);
     __syncthreads();
     a.out[(int64_t)h * D + d] = O / Ls;
 }
