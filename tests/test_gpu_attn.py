@@ -113,3 +113,19 @@ def test_deterministic_and_in_bounds():
         outs.append(out.clone())
     assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + Hq * D:]).all()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_one_workspace_across_calls_with_different_split_counts():
+    # one workspace (sized for the full cache, left holding the previous
+    # call's partial sums) serves calls whose split counts differ
+    Hq, Hkv, D, cap = 16, 8, 128, 4096
+    t = synth.attn_inputs(Hq, Hkv, D, cap, cfg=603, set_id=0)
+    ws = torch.full((qd.qattn_workspace_bytes(Hq, Hkv, D, cap),), 255, dtype=torch.uint8, device="cuda")
+    for pos in (4095, 0, 37, 1000, 15, 4095, 2048):
+        dev = {k: dev_half(v) for k, v in t.items()}
+        y = qd.qattn_decode(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"], pos, 0,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        ref, a = oracle.attn_decode(f64(t["q"]), f64(t["k_new"]), f64(t["v_new"]), f64(t["k_cache"]),
+                                    f64(t["v_cache"]), 0, pos, D ** -0.5)
+        assert_within(y.cpu().numpy(), ref, a, f"pos {pos}")
