@@ -25,47 +25,46 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 
 constexpr int ROUTE_MAX_E = 1024;
 
+// Top-k of the E logits l[0..E) (global or LDS) of one token into idx[0..k)
+// and w[0..k). Threads 0..255 (four waves) rank; every thread of the
+// workgroup must call (it holds barriers). keys: ROUTE_MAX_E words of LDS.
 template <int PER>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int32_t* __restrict__ idx,
-                                                         float* __restrict__ wout) {
-    __shared__ __align__(16) uint32_t keys[ROUTE_MAX_E];
-    __shared__ int part[4][ROUTE_MAX_E];
-    __shared__ float sel[32];
-    const int t = blockIdx.x;
+__device__ __forceinline__ void rank_topk(const float* l, int E, int k, int32_t* idx, float* wout,
+                                          uint32_t* keys, int (*part)[ROUTE_MAX_E], float* sel) {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    const float* l = logits + (int64_t)t * E;
     const int E64 = (E + 63) & ~63;   // padded: each wave's quarter is a multiple of 16
-    for (int e = threadIdx.x; e < E64; e += 256) keys[e] = e < E ? order_key(l[e]) : 0u;
+    for (int e = threadIdx.x; e < E64; e += blockDim.x) keys[e] = e < E ? order_key(l[e]) : 0u;
     __syncthreads();
-    uint32_t mine[PER];
-    int rank[PER];
+    if (wv < 4) {
+        uint32_t mine[PER];
+        int rank[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        mine[i] = keys[lane + 64 * i < E64 ? lane + 64 * i : 0];
-        rank[i] = 0;
-    }
-    const int q = E64 / 4;
-    for (int e0 = wv * q; e0 < (wv + 1) * q; e0 += 16) {
-        uint4 kv[4];
+        for (int i = 0; i < PER; ++i) {
+            mine[i] = keys[lane + 64 * i < E64 ? lane + 64 * i : 0];
+            rank[i] = 0;
+        }
+        const int q = E64 / 4;
+        for (int e0 = wv * q; e0 < (wv + 1) * q; e0 += 16) {
+            uint4 kv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kv[j] = *(const uint4*)&keys[e0 + 4 * j];  // broadcast
+            for (int j = 0; j < 4; ++j) kv[j] = *(const uint4*)&keys[e0 + 4 * j];  // broadcast
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t kk[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int e2 = e0 + 4 * j + c;
+                for (int c = 0; c < 4; ++c) {
+                    const int e2 = e0 + 4 * j + c;
 #pragma unroll
-                for (int i = 0; i < PER; ++i)
-                    rank[i] += (kk[c] > mine[i]) || (kk[c] == mine[i] && e2 < lane + 64 * i);
+                    for (int i = 0; i < PER; ++i)
+                        rank[i] += (kk[c] > mine[i]) || (kk[c] == mine[i] && e2 < lane + 64 * i);
+                }
             }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-        if (lane + 64 * i < E64) part[wv][lane + 64 * i] = rank[i];
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i < E64) part[wv][lane + 64 * i] = rank[i];
+    }
     __syncthreads();
     if (wv == 0) {
 #pragma unroll
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                 const int r = part[0][e] + part[1][e] + part[2][e] + part[3][e];
                 if (r < k) {
                     sel[r] = l[e];
-                    idx[(int64_t)t * k + r] = e;
+                    idx[r] = e;
                 }
             }
         }
@@ -85,8 +84,21 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         const float lmax = sel[0];
         float tot = 0.f;
         for (int j = 0; j < k; ++j) tot += expf(sel[j] - lmax);
-        wout[(int64_t)t * k + lane] = expf(sel[lane] - lmax) / tot;
+        wout[lane] = expf(sel[lane] - lmax) / tot;
     }
+}
+
+template <int PER>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int32_t* __restrict__ idx,
+                                                         float* __restrict__ wout) {
+    __shared__ __align__(16) uint32_t keys[ROUTE_MAX_E];
+    __shared__ int part[4][ROUTE_MAX_E];
+    __shared__ float sel[32];
+    const int t = blockIdx.x;
+    (void)T;
+    rank_topk<PER>(logits + (int64_t)t * E, E, k, idx + (int64_t)t * k, wout + (int64_t)t * k, keys,
+                   part, sel);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
