@@ -32,6 +32,7 @@ EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
            "qgemm_affine4_verify", "qattn_decode_workspace_bytes", "qattn_decode",
+           "qmoe_layer_decode",
            "qd_status_string", "qd_last_error")
 
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
                                    _P, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
     L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qmoe_layer_decode.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P, ctypes.c_int, _P,
+                                    _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.qattn_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
     L.qattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.qattn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
@@ -92,7 +95,7 @@ def lib() -> ctypes.CDLL:
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
                "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
                "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify",
-               "qattn_decode"):
+               "qattn_decode", "qmoe_layer_decode"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -329,10 +332,30 @@ def qmoe_expert_gemv(w: MoeWeights, idx, weights, x, out=None, workspace=None):
 
 def qmoe_layer(w: MoeWeights, x, k: int = 8, workspace=None, logits=None, idx=None, weights=None,
                out=None):
-    """One MoE FFN layer: int8 router GEMV -> top-k routing -> expert block."""
+    """One MoE FFN layer: int8 router GEMV -> top-k routing -> expert block.
+
+    One token (decode) takes qmoe_layer_decode (the ranking inside the gate+up
+    kernel, identical results); several take the three separate calls."""
     T = x.shape[0]
     if logits is None:
         logits = torch.empty((T, w.E), dtype=torch.float32, device=x.device)
+    if T == 1 and w.E <= 256:
+        _need(x, "x", (torch.float16, torch.bfloat16), 2)
+        if idx is None:
+            idx = torch.empty((1, k), dtype=torch.int32, device=x.device)
+        if weights is None:
+            weights = torch.empty((1, k), dtype=torch.float32, device=x.device)
+        if out is None:
+            out = torch.empty((1, w.H), dtype=torch.float32, device=x.device)
+        st = w.cstruct()
+        need = int(lib().qmoe_expert_workspace_bytes(ctypes.byref(st), 1, k))
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        _check(lib().qmoe_layer_decode(ctypes.byref(st), _ptr(w.router_q), _ptr(w.router_s),
+                                       _ptr(w.router_b), k, _ptr(x), _x_dtype(x), _ptr(logits),
+                                       _ptr(idx), _ptr(weights), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream()))
+        return out
     qgemv_affine8(w.router_q, w.router_s, w.router_b, x, out=logits)
     idx, weights = qmoe_route_topk(logits, k, idx, weights)
     return qmoe_expert_gemv(w, idx, weights, x, out=out, workspace=workspace)

@@ -300,6 +300,44 @@ qd_status qmoe_expert_gemv(const qd_moe_weights* w, const int32_t* idx, const fl
                     fn);
 }
 
+qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
+                            const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                            const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                            float* weights, float* y, void* workspace, size_t ws_bytes,
+                            qd_stream stream) {
+    const char* fn = "qmoe_layer_decode";
+    qd_status st = check_moe(fn, w);
+    if (st != QD_OK) return st;
+    if (w->E > 256) return fail(QD_ERR_UNSUPPORTED, "%s: E = %d (at most 256)", fn, w->E);
+    if (k < 1 || k > w->E || k > 32)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: k = %d must be in [1, min(E, 32)]", fn, k);
+    if (x_dtype != QD_F16 && x_dtype != QD_BF16)
+        return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
+    CHECK_PTR(router_q);
+    CHECK_PTR(router_s);
+    CHECK_PTR(router_b);
+    CHECK_PTR(x);
+    CHECK_PTR(logits);
+    CHECK_PTR(idx);
+    CHECK_PTR(weights);
+    CHECK_PTR(y);
+    const qd::MoeArgs m = moe_args(w);
+    const size_t need = qd::moe_workspace_bytes(m, 1, k);
+    if (!workspace)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned16(workspace))
+        return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (ws_bytes < need)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    const int xkind = x_dtype == QD_F16 ? 0 : 1;
+    hipError_t e = qd::launch_gemv(8, 0, router_q, router_s, router_b, nullptr, x, xkind, logits,
+                                   w->E, w->H, 1, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e, fn);
+    return from_hip(qd::launch_moe_decode_routed(m, logits, k, x, xkind, idx, weights, y, workspace,
+                                                 (hipStream_t)stream),
+                    fn);
+}
+
 qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y, int32_t M, int32_t N, int32_t K,
                               int32_t group_size, qd_stream stream) {

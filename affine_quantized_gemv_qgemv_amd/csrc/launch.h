@@ -60,6 +60,12 @@ hipError_t launch_moe_decode(const MoeArgs& m, const int32_t* idx, const float* 
 hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
                               const void* x, int xkind, float* y, void* ws, hipStream_t st);
 
+// One decode token from its router logits: top-k ranked inside the gate+up
+// kernel (ids and weights written to idx / w), then down + combine.
+hipError_t launch_moe_decode_routed(const MoeArgs& m, const float* logits, int k, const void* x,
+                                    int xkind, int32_t* idx, float* w, float* y, void* ws,
+                                    hipStream_t st);
+
 hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
                               const void* x, int xkind, float* y, void* ws, size_t ws_bytes,
                               hipStream_t st);

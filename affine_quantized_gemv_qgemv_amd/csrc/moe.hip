@@ -25,8 +25,16 @@
 //      second pass and no atomics.
 // Prefill chunks (T > 1) group (token, slot) pairs by expert and run the
 // grouped MFMA kernels of chunk.hip.
+//
+// The routed decode entry (launch_moe_decode_routed) takes the router
+// logits instead of the routing: one wave of every gate+up workgroup that
+// has routed rows ranks them from LDS (wave_topk: the same exact top-k and
+// weights as the routing kernel, so all workgroups agree), and workgroup 0
+// writes the ids and weights for the down pass and the caller. A decode
+// layer is then three launches (router, gate+up, down) instead of four.
 #include "common.h"
 #include "launch.h"
+#include "route.h"
 
 namespace qd {
 
@@ -41,7 +49,10 @@ __device__ __forceinline__ float gelu_f(float u, int act) {
 struct MoeAArgs {
     const uint32_t *gu_q, *sgu_q;
     const uint16_t *gu_s, *gu_b, *sgu_s, *sgu_b;
-    const int32_t* idx;   // [k] expert ids of this token
+    const int32_t* idx;   // [k] expert ids of this token (when logits is NULL)
+    const float* logits;  // [E] router logits to rank here, or NULL
+    int32_t* idx_out;     // [k] ids written by workgroup 0 when ranking here
+    float* w_out;         // [k] weights written by workgroup 0 when ranking here
     const void* x;        // [H] activations of this token
     int xkind;
     float* h;             // [k*I + Is]
@@ -51,6 +62,8 @@ struct MoeAArgs {
 // ---------------------------------------------------------------------------
 // A. gathered gate+up rows with the GELU gate.
 // ---------------------------------------------------------------------------
+constexpr int MOE_RANK_E = 256;   // experts the in-kernel ranking handles
+
 template <int XF, int LPR, int U, int CPL>
 __global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
     extern __shared__ uint4 lds[];
@@ -69,7 +82,37 @@ __global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
     const int t0 = (int)((int64_t)ntiles * gw / W);
     const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
 
+    // The routing: given, or ranked here from the logits. One logit per
+    // thread is loaded before the activations are staged, so the two loads
+    // overlap, and the ranking then reads only LDS.
+    float lv = 0.f;
+    if (a.logits && (int)threadIdx.x < a.E) lv = a.logits[threadIdx.x];
     stage_x<4, XF, CPL>(a.x, a.xkind, a.H, 1, 0, C16, lds);
+    __shared__ int32_t sidx[32];
+    __shared__ float sw[32];
+    const int32_t* idx = a.idx;
+    // Workgroups whose tiles are all shared-expert rows need no routing;
+    // workgroup 0 always ranks, as it writes the ids and weights.
+    const int wg_t0 = (int)((int64_t)ntiles * (blockIdx.x * nwaves) / W);
+    if (a.logits && (blockIdx.x == 0 || wg_t0 * RPI < a.k * a.I)) {
+        __shared__ float lsh[MOE_RANK_E];
+        if ((int)threadIdx.x < a.E) lsh[threadIdx.x] = lv;
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            switch ((a.E + 63) >> 6) {   // candidates per lane
+                case 1: wave_topk<1>(lsh, a.E, a.k, sidx, sw); break;
+                case 2: wave_topk<2>(lsh, a.E, a.k, sidx, sw); break;
+                case 3: wave_topk<3>(lsh, a.E, a.k, sidx, sw); break;
+                default: wave_topk<4>(lsh, a.E, a.k, sidx, sw); break;
+            }
+        }
+        __syncthreads();
+        if (blockIdx.x == 0 && threadIdx.x < a.k) {
+            a.idx_out[threadIdx.x] = sidx[threadIdx.x];
+            a.w_out[threadIdx.x] = sw[threadIdx.x];
+        }
+        idx = sidx;
+    }
     __syncthreads();
     const uint32_t magic = in_vgpr(kMagic16);
 
@@ -84,7 +127,7 @@ __global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
         bool ok = pv;
         if (pc < a.k * a.I) {
             const int j = pc / a.I, i = pc - j * a.I;
-            int e = a.idx[j];
+            int e = idx[j];
             if (e < 0 || e >= a.E) {
                 ok = false;
                 e = 0;
@@ -413,6 +456,52 @@ hipError_t launch_moe_decode(const MoeArgs& m, const int32_t* idx, const float* 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_moe_decode_routed(const MoeArgs& m, const float* logits, int k, const void* x,
+                                    int xkind, int32_t* idx, float* w, float* y, void* ws,
+                                    hipStream_t st) {
+    // one logit per thread of a gate+up workgroup
+    if (m.E > MOE_RANK_E || m.E > 64 * moe_cfg().gu_nw || k > 32) return hipErrorInvalidValue;
+    float* h = (float*)ws;
+    MoeAArgs a{};
+    a.gu_q = m.gu_q;
+    a.sgu_q = m.sgu_q;
+    a.gu_s = m.gu_s;
+    a.gu_b = m.gu_b;
+    a.sgu_s = m.sgu_s;
+    a.sgu_b = m.sgu_b;
+    a.logits = logits;
+    a.idx_out = idx;
+    a.w_out = w;
+    a.x = x;
+    a.xkind = xkind;
+    a.h = h;
+    a.E = m.E;
+    a.H = m.H;
+    a.I = m.I;
+    a.Is = m.Is;
+    a.k = k;
+    a.act = m.act;
+    hipError_t e = xkind == X_F16 ? launch_gateup<0>(a, st) : launch_gateup<1>(a, st);
+    if (e != hipSuccess) return e;
+    MoeBArgs b{};
+    b.dn_q = m.dn_q;
+    b.sdn_q = m.sdn_q;
+    b.dn_s = m.dn_s;
+    b.dn_b = m.dn_b;
+    b.sdn_s = m.sdn_s;
+    b.sdn_b = m.sdn_b;
+    b.idx = idx;
+    b.p = w;
+    b.h = h;
+    b.y = y;
+    b.E = m.E;
+    b.H = m.H;
+    b.I = m.I;
+    b.Is = m.Is;
+    b.k = k;
+    return launch_down(b, st);
 }
 
 size_t moe_workspace_bytes(const MoeArgs& m, int T, int k) {

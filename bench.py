@@ -512,7 +512,7 @@ def bench_moe(args, torch, qd, prefill: bool):
                                    f"{H}->2x{Is}->{H}, {len(layers)} layers cycled, T={T}",
                        "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                        "mean_distinct_experts": mean_uniq, "step_bytes": int(step_bytes),
-                       "launches_per_layer": 4 if not prefill else 6},
+                       "launches_per_layer": 3 if not prefill else 6},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "cpu_baseline": None}

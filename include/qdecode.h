@@ -193,6 +193,27 @@ qd_status qmoe_expert_gemv(const qd_moe_weights* w, const int32_t* idx, const fl
                            void* workspace, size_t ws_bytes, qd_stream stream);
 
 /*
+ * A whole decode MoE layer for one token ([TF] internals section: router on
+ * the GPU, top-8 experts, routed plus shared experts combined):
+ * logits = router GEMV (8-bit, as qgemv_affine8), idx / weights = top-k of
+ * the logits (as qmoe_route_topk), y = the expert block (as
+ * qmoe_expert_gemv with T = 1). Results are bit-identical to those three
+ * calls; the ranking runs inside the gate+up kernel, so the layer takes
+ * three launches instead of four.
+ *   router_q [E][H/4] uint32, router_s / router_b [E][H/64] fp16 bits;
+ *   x [H] fp16 or bf16 bits; outputs logits [E], idx [k], weights [k], y [H];
+ *   E <= 256, 1 <= k <= min(E, 32); workspace as qmoe_expert_gemv with T = 1
+ *   (qmoe_expert_workspace_bytes(w, 1, k) bytes, 16-byte aligned).
+ * All buffers are device memory owned by the caller; every output is
+ * overwritten. Errors as qmoe_expert_gemv; E > 256 gives QD_ERR_UNSUPPORTED.
+ */
+qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
+                            const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                            const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                            float* weights, float* y, void* workspace, size_t ws_bytes,
+                            qd_stream stream);
+
+/*
  * Prefill chunk ([TF] internals: prompts run in chunks of at most 128 tokens
  * so one fetch of a weight serves many rows):
  *   Y[m][n] = sum_k w[n][k] * X[m][k],  X [M][K] bf16 bits, Y [M][N] fp32.

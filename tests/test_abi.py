@@ -137,6 +137,28 @@ def test_moe_argument_errors():
     assert moe_call(moe_struct(), dt=3) == qd.QD_ERR_UNSUPPORTED
 
 
+def layer_call(st, k=8, ws=A, ws_bytes=1 << 30, x=A, dt=0, rq=A, logits=A):
+    return qd.lib().qmoe_layer_decode(ctypes.byref(st), rq, A, A, k, x, dt, logits, A, A, A, ws,
+                                      ws_bytes, None)
+
+
+def test_moe_layer_decode_argument_errors():
+    L = qd.lib()
+    assert L.qmoe_layer_decode(None, A, A, A, 8, A, 0, A, A, A, A, A, 1 << 30,
+                               None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert layer_call(moe_struct(group_size=128)) == qd.QD_ERR_UNSUPPORTED
+    assert layer_call(moe_struct(E=257)) == qd.QD_ERR_UNSUPPORTED
+    assert layer_call(moe_struct(), k=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert layer_call(moe_struct(), k=33) == qd.QD_ERR_INVALID_ARGUMENT
+    assert layer_call(moe_struct(E=4), k=8) == qd.QD_ERR_INVALID_ARGUMENT
+    assert layer_call(moe_struct(), dt=2) == qd.QD_ERR_UNSUPPORTED
+    assert layer_call(moe_struct(), rq=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert layer_call(moe_struct(), logits=MIS) == qd.QD_ERR_MISALIGNED
+    assert layer_call(moe_struct(), ws=None) == qd.QD_ERR_WORKSPACE
+    assert layer_call(moe_struct(), ws_bytes=16) == qd.QD_ERR_WORKSPACE
+    assert layer_call(moe_struct(), ws=MIS) == qd.QD_ERR_MISALIGNED
+
+
 def test_moe_workspace_size_grows_with_tokens():
     st = moe_struct()
     L = qd.lib()

@@ -5,6 +5,8 @@ Expert ids and their order must match bit for bit; outputs must satisfy
 |y_gpu - y_ref| <= 1e-4 * A + 1e-6 with
 A = sum_j p_j sum_k |W_dn[e_j] h_j| + sum_k |W_sdn h_s| (oracle values).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -30,18 +32,24 @@ def run_layer(w, xb, k, xdt="f16"):
     x = x_dev(xb, xdt)
     T = x.shape[0]
     logits = torch.empty((T, w.E), dtype=torch.float32, device="cuda")
-    y = qd.qmoe_layer(w, x, k=k, logits=logits)
+    idx = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    p = torch.full((T, k), -7.0, dtype=torch.float32, device="cuda")
+    y = qd.qmoe_layer(w, x, k=k, logits=logits, idx=idx, weights=p)
     torch.cuda.synchronize()
-    return logits, y
+    return logits, idx, p, y
 
 
 def check_layer(mw, xb, k, act=0, xdt="f16", tokens=None, what=""):
     w = dev_moe(mw, act)
-    logits, _ = run_layer(w, xb, k, xdt)
+    logits, il, pl, yl = run_layer(w, xb, k, xdt)
     # routing on the GPU's own logits: ids bit-exact
     idx, p = qd.qmoe_route_topk(logits, k)
     y = qd.qmoe_expert_gemv(w, idx, p, x_dev(xb, xdt))
     torch.cuda.synchronize()
+    # the one-call layer (decode: ranking inside gate+up) equals the separate calls
+    assert torch.equal(il, idx), f"{what}: layer ids differ from qmoe_route_topk"
+    assert torch.equal(pl, p), f"{what}: layer weights differ from qmoe_route_topk"
+    assert torch.equal(yl, y), f"{what}: layer output differs from qmoe_expert_gemv"
     L = logits.cpu().numpy()
     ir, pr = oracle.route_topk(L.astype(np.float64), k)
     ig, pg = idx.cpu().numpy(), p.cpu().numpy()
@@ -96,6 +104,42 @@ def test_identical_experts_ignore_routing():
     yr, a = oracle.moe_experts(mw, oracle.f16_to_f64(xb), np.array([[2]]), np.array([[1.0]]))
     assert_within(ya, yr, a, "identical a")
     assert_within(yb, yr, a, "identical b")
+
+
+@pytest.mark.parametrize("E,k,flat", [(1, 1, False), (64, 8, False), (200, 32, False),
+                                      (256, 8, False), (128, 8, True), (96, 32, True)])
+def test_decode_layer_ranking_in_gateup(E, k, flat):
+    """qmoe_layer_decode against router GEMV + qmoe_route_topk + qmoe_expert_gemv
+    (flat: every logit ties, so the ids are 0..k-1 and the weights 1/k)."""
+    mw = synth.moe_weights(E=E, H=256, I=64, Is=128, cfg=406, layer=E, flat_router=flat)
+    w = dev_moe(mw)
+    L = qd.lib()
+    for s in range(3):
+        xb = synth.x_f16(1, 256, cfg=406, set_id=s)
+        x = dev_half(xb)
+        logits = torch.empty((1, E), dtype=torch.float32, device="cuda")
+        idx = torch.full((1, k), -7, dtype=torch.int32, device="cuda")
+        p = torch.full((1, k), -7.0, dtype=torch.float32, device="cuda")
+        y = torch.full((1, 256), float("nan"), dtype=torch.float32, device="cuda")
+        st = w.cstruct()
+        need = int(L.qmoe_expert_workspace_bytes(ctypes.byref(st), 1, k))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        rc = L.qmoe_layer_decode(ctypes.byref(st), w.router_q.data_ptr(), w.router_s.data_ptr(),
+                                 w.router_b.data_ptr(), k, x.data_ptr(), 0, logits.data_ptr(),
+                                 idx.data_ptr(), p.data_ptr(), y.data_ptr(), ws.data_ptr(), need,
+                                 None)
+        assert rc == qd.QD_OK, qd.last_error()
+        lr = qd.qgemv_affine8(w.router_q, w.router_s, w.router_b, x)
+        ir, pr = qd.qmoe_route_topk(lr, k)
+        yr = qd.qmoe_expert_gemv(w, ir, pr, x)
+        torch.cuda.synchronize()
+        assert torch.equal(logits, lr)
+        assert torch.equal(idx, ir), (idx, ir)
+        assert torch.equal(p, pr)
+        assert torch.equal(y, yr)
+        if flat:
+            assert np.array_equal(idx.cpu().numpy()[0], np.arange(k))
+            assert np.allclose(p.cpu().numpy(), 1.0 / k, rtol=1e-6)
 
 
 def test_flat_router_routes_first_k_evenly():
