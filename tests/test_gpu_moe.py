@@ -90,6 +90,13 @@ def test_odd_shapes():
     check_layer(mw, xb, 1, what="k=1")
 
 
+def test_down_row_over_several_rounds():
+    # k*I/32 + Is/32 = 260 chunks: more than one round of the down kernel
+    mw = synth.moe_weights(E=16, H=128, I=1024, Is=128, cfg=407, layer=0)
+    xb = synth.x_f16(1, 128, cfg=407, set_id=0)
+    check_layer(mw, xb, 8, what="two rounds")
+
+
 def test_identical_experts_ignore_routing():
     mw = synth.moe_weights(**TINY, cfg=402, layer=0, identical_experts=True)
     w = dev_moe(mw)
