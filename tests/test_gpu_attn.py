@@ -49,6 +49,8 @@ CASES = [
     (16, 8, 128, 1024, 1024, 1024), (16, 8, 128, 1024, 1024, 3000), (8, 8, 64, 300, 0, 299),
     (32, 4, 64, 777, 777, 2000), (4, 1, 256, 200, 0, 150), (8, 2, 256, 513, 513, 513),
     (16, 2, 128, 48, 0, 17), (2, 1, 128, 1, 1, 9),
+    # ragged split counts with one query head per key/value head
+    (4, 4, 256, 2049, 0, 2047), (4, 4, 256, 2049, 0, 2048), (8, 4, 64, 2048, 2048, 5000),
 ]
 
 
