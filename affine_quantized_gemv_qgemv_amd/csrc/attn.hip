@@ -217,13 +217,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 }
 
 // Splits for n occupied slots: about two workgroups per CU over all heads,
-// each at least one workgroup step of rows (a multiple of 16).
+// each at least one load round of rows (a multiple of 32: two row steps of
+// 16), which also keeps a short cache's combine to one batch of 32 splits.
 static void attn_split(int n, int Hkv, int& nsplit, int& chunk) {
     const int cus = device_info().cus;
     int want = std::max(1, (2 * cus + Hkv - 1) / Hkv);
-    want = std::min(std::min(want, AT_MAXSPLIT), (n + 15) / 16);
+    want = std::min(std::min(want, AT_MAXSPLIT), (n + 31) / 32);
     chunk = (n + want - 1) / want;
-    chunk = (chunk + 15) & ~15;
+    chunk = (chunk + 31) & ~31;
     nsplit = (n + chunk - 1) / chunk;
 }
 
