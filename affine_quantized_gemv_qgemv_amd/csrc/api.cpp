@@ -351,7 +351,7 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
     CHECK_PTR(biases);
     CHECK_PTR(x);
     CHECK_PTR(y);
-    return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, y, M, N, K,
+    return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, 1 /* bf16 */, y, M, N, K,
                                           (hipStream_t)stream),
                     fn);
 }
@@ -371,14 +371,9 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
     CHECK_PTR(biases);
     CHECK_PTR(x);
     CHECK_PTR(y);
-    // bf16 activations take the staged chunk kernel (its row tiles follow M);
-    // fp16 ones the token kernel, which reads them directly
-    if (x_dtype == QD_BF16)
-        return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, y, M, N, K,
-                                              (hipStream_t)stream),
-                        fn);
-    return from_hip(qd::launch_gemm4_tokens(wq, scales, biases, x, 0, y, N, K, M,
-                                            (hipStream_t)stream),
+    // the staged chunk kernel, whose row tiles follow M (x kinds: 0 fp16, 1 bf16)
+    return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, x_dtype == QD_F16 ? 0 : 1, y, M,
+                                          N, K, (hipStream_t)stream),
                     fn);
 }
 

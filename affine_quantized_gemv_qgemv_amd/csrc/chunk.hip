@@ -39,6 +39,8 @@
 
 namespace qd {
 
+typedef _Float16 halfx8_c __attribute__((ext_vector_type(8)));
+
 constexpr int CH_NT = 64;    // output columns per workgroup
 constexpr int CH_MMAX = 128; // rows per call (the whole chunk)
 
@@ -56,12 +58,13 @@ struct ChunkArgs {
 
 // A workgroup owns MT = 32 MB WM rows (one row tile) and 64 columns. LDS
 // layout (dynamic): xs[2 buffers][SG groups][MT rows][XS_STRIDE] uint4, then
-// xsum[2][MT rows][SG groups] fp32.
-template <int SG, int MT_>
+// xsum[2][MT rows][SG groups] fp32, then (fp16 activations only) the same
+// sums transposed, xsumT[2][SG groups][MT rows].
+template <int SG, int MT_, bool F16 = false>
 struct ChunkLds {
     static constexpr int MT = MT_;
     static constexpr int XS = SG * MT * XS_STRIDE;   // uint4 per buffer
-    static constexpr size_t bytes = 2 * (size_t)XS * 16 + 2 * SG * MT * 4;
+    static constexpr size_t bytes = 2 * (size_t)XS * 16 + (F16 ? 4 : 2) * SG * MT * 4;
 };
 
 // Group visited at step g (clamped to the last step) when a workgroup starts
@@ -78,7 +81,7 @@ __device__ __forceinline__ int rot_group(int g, int G, int rot) {
 // stage or skip): TPR = NTS / MT threads share a row; thread part p holds k
 // in [64 p / TPR, 64 (p + 1) / TPR) of every group: XPT = 8 / TPR uint4 per
 // group.
-template <int SG, int MT_, int NT>
+template <int SG, int MT_, int NT, bool F16 = false>
 struct StageIO {
     static constexpr int MT = MT_;
     static constexpr int NTS = NT < 8 * MT ? NT : 8 * MT;
@@ -101,7 +104,8 @@ struct StageIO {
         }
     }
 
-    __device__ static __forceinline__ void store(uint4* xs, float* xsum, const uint4 (&xr)[SG][XPT]) {
+    __device__ static __forceinline__ void store(uint4* xs, float* xsum, const uint4 (&xr)[SG][XPT],
+                                                 float* xsumT = nullptr) {
         // rows past M hold copies of row M - 1 (the loads clamp); they only
         // feed output rows that are never stored
         const int t = threadIdx.x;
@@ -114,14 +118,22 @@ struct StageIO {
             for (int i = 0; i < XPT; ++i) {
                 const uint4 v = xr[gi][i];
                 xs[(gi * MT + r) * XS_STRIDE + XPT * part + i] = v;
-                acc = bf16_pair_sum(v.x, acc);
-                acc = bf16_pair_sum(v.y, acc);
-                acc = bf16_pair_sum(v.z, acc);
-                acc = bf16_pair_sum(v.w, acc);
+                if constexpr (F16) {
+                    acc = dot2(v.x, 0x3C003C00u, acc);
+                    acc = dot2(v.y, 0x3C003C00u, acc);
+                    acc = dot2(v.z, 0x3C003C00u, acc);
+                    acc = dot2(v.w, 0x3C003C00u, acc);
+                } else {
+                    acc = bf16_pair_sum(v.x, acc);
+                    acc = bf16_pair_sum(v.y, acc);
+                    acc = bf16_pair_sum(v.z, acc);
+                    acc = bf16_pair_sum(v.w, acc);
+                }
             }
 #pragma unroll
             for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
             xsum[r * SG + gi] = acc;   // every lane of the row stores the same sum
+            if constexpr (F16) xsumT[gi * MT + r] = acc;
         }
     }
 };
@@ -162,7 +174,11 @@ __device__ __forceinline__ int opaque(int v) {
 // XD = stages of X held in registers ahead of LDS: with 1, the next stage is
 // read while the current one is consumed; with 2 (small row tiles, whose
 // stages hold little matrix work) the stage after that is also in flight.
-template <int SG, int D, int MB, int WM, int NKS, int XD = 1>
+// F16: fp16 activations; the codes enter an fp16 MFMA as 1024 + q and the
+// offset part -1024 s Xsum is added in fp32 per group (in the bias MFMA's
+// 16-bit split it would lose too much next to the result); bf16 activations
+// fold -128 s into the bias MFMA.
+template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
     constexpr int SPR = D / SG;     // stages per round
@@ -171,11 +187,12 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     constexpr int DW = D / NKS;     // ring slots per wave
     constexpr int WS = 2 * WM;      // waves per K-set
     constexpr int MT = 32 * MB * WM;
-    using L = ChunkLds<SG, MT>;
-    using IO = StageIO<SG, MT, 64 * WS * NKS>;
+    using L = ChunkLds<SG, MT, F16>;
+    using IO = StageIO<SG, MT, 64 * WS * NKS, F16>;
     extern __shared__ uint4 smem[];
     uint4* xs_raw = smem;                                    // [2][XS]
     float* xsum_raw = (float*)(smem + 2 * L::XS);            // [2][MT][SG]
+    float* xsumT_raw = xsum_raw + 2 * SG * MT;               // [2][SG][MT] (F16)
     const int RT = (a.M + MT - 1) / MT;                      // row tiles
     const int b = blockIdx.x;
     const int ct = (b / (8 * RT)) * 8 + b % 8;
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     // stage parity picks the slot, and rounds hold an even number of stages)
     uint4 xr[XD][SG][IO::XPT];
     IO::load(a, m0, 0, G, rot, xr[0]);
-    IO::store(xs_raw, xsum_raw, xr[0]);
+    IO::store(xs_raw, xsum_raw, xr[0], xsumT_raw);
     if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
     __syncthreads();
 
@@ -228,7 +245,8 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     // slot is refilled with step g + D. xs: this lane's A-operand row (row
     // 32 MB wm + l32, k-half h) of the group. The bias part, (b - 128 s) Xsum,
     // is added per stage on the matrix core (bias_mfma below).
-    auto group = [&](const int g, auto ec, const uint4* xs) __attribute__((always_inline)) {
+    auto group = [&](const int g, auto ec, const uint4* xs, const float* xt)
+                     __attribute__((always_inline)) {
         constexpr int e = decltype(ec)::value;
         // the 4 steps' B operands, then the row blocks PH at a time (fewer
         // live accumulators than all MB at once)
@@ -236,7 +254,8 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         const uint32_t wv[4] = {bq[e].x, bq[e].y, bq[e].z, bq[e].w};
         bf16x8_t bfrag[4];
 #pragma unroll
-        for (int stp = 0; stp < 4; ++stp) bfrag[stp] = codes_to_bf16(wv[stp]);
+        for (int stp = 0; stp < 4; ++stp)
+            bfrag[stp] = __builtin_bit_cast(bf16x8_t, codes_to_16n(wv[stp], F16 ? 0x64006400u : 0x43004300u));
         const float sf = h2f((uint16_t)bs[e]);
 #pragma unroll
         for (int m0b = 0; m0b < MB; m0b += PH) {
@@ -249,15 +268,36 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
             for (int stp = 0; stp < 4; ++stp) {
 #pragma unroll
                 for (int pb = 0; pb < PH; ++pb) {
-                    const bf16x8_t afrag =
-                        __builtin_bit_cast(bf16x8_t, xs[32 * (m0b + pb) * XS_STRIDE + stp]);
-                    P[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag[stp], P[pb], 0, 0, 0);
+                    const uint4 av = xs[32 * (m0b + pb) * XS_STRIDE + stp];
+                    if constexpr (F16)
+                        P[pb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(halfx8_c, av), __builtin_bit_cast(halfx8_c, bfrag[stp]),
+                            P[pb], 0, 0, 0);
+                    else
+                        P[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, av), bfrag[stp], P[pb], 0, 0, 0);
                 }
             }
+            if constexpr (F16) {
+                // rows 8 (i / 4) + 4 h + i % 4 of the block: quarter i / 4
+                const float mo = -1024.f * sf;
 #pragma unroll
-            for (int pb = 0; pb < PH; ++pb)
+                for (int pb = 0; pb < PH; ++pb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[m0b + pb][i] = fmaf(sf, P[pb][i], acc[m0b + pb][i]);
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const float4 xq = *(const float4*)(xt + 32 * (m0b + pb) + 8 * qq);
+                        const float xv[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[m0b + pb][4 * qq + j] = fmaf(sf, P[pb][4 * qq + j],
+                                                             fmaf(mo, xv[j], acc[m0b + pb][4 * qq + j]));
+                    }
+            } else {
+#pragma unroll
+                for (int pb = 0; pb < PH; ++pb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[m0b + pb][i] = fmaf(sf, P[pb][i], acc[m0b + pb][i]);
+            }
             __builtin_amdgcn_sched_barrier(0);   // keep the passes apart (registers)
         }
         // finish this group's epilogue here: left alone, the compiler sinks it
@@ -291,7 +331,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         for (int j = 0; j < JS; ++j) {
             const int e = sj * JS + j;
             const float sf = h2f((uint16_t)bs[e]);
-            bv[j] = h2f((uint16_t)bb[e]) - 128.f * sf;
+            bv[j] = h2f((uint16_t)bb[e]) - (F16 ? 0.f : 128.f * sf);
             if constexpr (decltype(checked)::value)
                 if (st * SG + NKS * j + ks >= G) bv[j] = 0.f;
         }
@@ -337,18 +377,23 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         // group j of this wave is stage group NKS j + ks
         const uint4* xs = xs_raw + opaque(buf * L::XS + ks * MT * XS_STRIDE +
                                           (32 * MB * wm + l32) * XS_STRIDE + 4 * h);
+        // fp16 only: this lane's accumulator rows of the row sums, group ks
+        const float* xt = F16 ? xsumT_raw + opaque(buf * SG * MT + ks * MT + 32 * MB * wm + 4 * h)
+                              : nullptr;
         static_for<0, JS>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
             const int g = st * SG + NKS * j + ks;
             constexpr std::integral_constant<int, sj * JS + j> ec{};
             const uint4* xsj = xs + NKS * j * MT * XS_STRIDE;
+            const float* xtj = F16 ? xt + NKS * j * MT : nullptr;
             if constexpr (decltype(checked)::value) {
-                if (g < G) group(g, ec, xsj);
+                if (g < G) group(g, ec, xsj, xtj);
             } else {
-                group(g, ec, xsj);
+                group(g, ec, xsj, xtj);
             }
         });
-        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr[sv]);
+        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr[sv],
+                  xsumT_raw + (buf ^ 1) * SG * MT);
         __syncthreads();
     };
 
@@ -397,29 +442,29 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     }
 }
 
-template <int SG, int D, int MB, int WM, int NKS, int XD = 1>
+template <int SG, int D, int MB, int WM, int NKS, bool F16>
 static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st) {
     constexpr int MT = 32 * MB * WM;
     const int RT = (a.M + MT - 1) / MT;
     const int grid = ((a.ncol_tiles + 7) / 8) * 8 * RT;
-    const size_t lds = ChunkLds<SG, MT>::bytes;
+    const size_t lds = ChunkLds<SG, MT, F16>::bytes;
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     constexpr int threads = 128 * WM * NKS;
-    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, XD>;
+    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16>;
     (void)occupancy((const void*)kern, threads, lds);  // sets the dynamic-LDS limit once
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                             const uint16_t* x_bf16, float* y, int M, int N, int K,
+                             const uint16_t* x, int xkind, float* y, int M, int N, int K,
                              hipStream_t st) {
-    if (bits != 4 || M > CH_MMAX) return hipErrorInvalidValue;
+    if (bits != 4 || M > CH_MMAX || (xkind != X_F16 && xkind != X_BF16)) return hipErrorInvalidValue;
     ChunkArgs a{};
     a.wq = wq;
     a.s = s;
     a.b = b;
-    a.x = x_bf16;
+    a.x = x;
     a.y = y;
     a.M = M;
     a.N = N;
@@ -432,9 +477,14 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
 // and four K-sets; beyond, the whole chunk as four row blocks per wave, 2
 // column waves x 4 K-sets = 8 waves (2 per SIMD). All use 4 groups per stage
 // and a ring of 8 groups.
-    if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2>(a, st);
-    if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4>(a, st);
-    return launch_chunk_cfg<4, 8, 4, 1, 4>(a, st);
+    if (xkind == X_F16) {
+        if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2, true>(a, st);
+        if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4, true>(a, st);
+        return launch_chunk_cfg<4, 8, 4, 1, 4, true>(a, st);
+    }
+    if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2, false>(a, st);
+    if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4, false>(a, st);
+    return launch_chunk_cfg<4, 8, 4, 1, 4, false>(a, st);
 }
 
 }  // namespace qd

@@ -75,12 +75,6 @@ hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,
                                hipStream_t st);
 
-// 4-bit weights over a few dozen tokens (f16 or bf16 activations) on the
-// matrix core: 32 tokens x 32 outputs per workgroup, K split over 8 waves.
-hipError_t launch_gemm4_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                               const uint16_t* x, int xkind, float* y, int N, int K, int T,
-                               hipStream_t st);
-
 // Decode attention of one token over fp16 KV caches (circular when window > 0).
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap);
 hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -88,8 +82,9 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const ui
                               int window, int pos, float scale, float* out, void* ws,
                               hipStream_t st);
 
+// x: fp16 or bf16 bits (xkind X_F16 / X_BF16), [M][K].
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                             const uint16_t* x_bf16, float* y, int M, int N, int K,
+                             const uint16_t* x, int xkind, float* y, int M, int N, int K,
                              hipStream_t st);
 
 }  // namespace qd

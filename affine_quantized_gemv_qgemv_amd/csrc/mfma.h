@@ -17,17 +17,17 @@ constexpr int XS_STRIDE = 9;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// 8 codes of one word -> bf16 (128 + q) in natural k order.
-__device__ __forceinline__ bf16x8_t codes_to_bf16(uint32_t w) {
+// 8 codes of one word -> 16-bit (off + q) in natural k order: the nibble in
+// the low mantissa of magic (per half: 0x4300 = bf16 128, 0x6400 = fp16 1024).
+__device__ __forceinline__ uint4 codes_to_16n(uint32_t w, uint32_t magic) {
     const uint32_t t = w & 0x0F0F0F0Fu;         // q0 q2 q4 q6 in bytes 0..3
     const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;  // q1 q3 q5 q7
     // v_perm_b32(u, t, sel): selector bytes 0..3 pick t's bytes, 4..7 u's, 0x0C gives 0
-    const uint32_t p01 = __builtin_amdgcn_perm(u, t, 0x0C040C00u) | 0x43004300u;
-    const uint32_t p23 = __builtin_amdgcn_perm(u, t, 0x0C050C01u) | 0x43004300u;
-    const uint32_t p45 = __builtin_amdgcn_perm(u, t, 0x0C060C02u) | 0x43004300u;
-    const uint32_t p67 = __builtin_amdgcn_perm(u, t, 0x0C070C03u) | 0x43004300u;
-    uint4 v = make_uint4(p01, p23, p45, p67);
-    return __builtin_bit_cast(bf16x8_t, v);
+    const uint32_t p01 = __builtin_amdgcn_perm(u, t, 0x0C040C00u) | magic;
+    const uint32_t p23 = __builtin_amdgcn_perm(u, t, 0x0C050C01u) | magic;
+    const uint32_t p45 = __builtin_amdgcn_perm(u, t, 0x0C060C02u) | magic;
+    const uint32_t p67 = __builtin_amdgcn_perm(u, t, 0x0C070C03u) | magic;
+    return make_uint4(p01, p23, p45, p67);
 }
 
 __device__ __forceinline__ float bf16_pair_sum(uint32_t v, float acc) {
