@@ -57,6 +57,9 @@ def parse():
                         "ahead of the GEMV (qgemv_mirai_*_rht)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--eager", action="store_true",
+                   help="launch every step from the host instead of replaying HIP graphs "
+                        "(shows the launch overhead the graphs remove)")
     return p.parse_args()
 
 
@@ -106,18 +109,35 @@ def stored_traffic(name: str, sources):
     return d.get("hbm_bytes_per_launch")
 
 
+EAGER = False   # set from --eager
+
+
 class Timer:
-    """Times a list of step callables replayed from HIP graphs on the current stream."""
+    """Times a list of step callables replayed from HIP graphs on the current
+    stream (or, with --eager, launched one by one from the host)."""
 
     def __init__(self, torch):
         self.torch = torch
 
     def run(self, step_fns, steps: int, warmup: int):
         torch = self.torch
+        # a graph of at least 32 steps, so one replay's launch cost is spread
+        # (a short cycle, e.g. one weight set, repeats its steps in order)
+        step_fns = list(step_fns) * max(1, -(-32 // len(step_fns)))
         n = len(step_fns)
         for i in range(warmup):
             step_fns[i % n]()
         torch.cuda.synchronize()
+        if EAGER:
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record()
+            for i in range(steps):
+                step_fns[i % n]()
+            end.record()
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / 1e3, time.perf_counter() - t0
         cyc = torch.cuda.CUDAGraph()
         with torch.cuda.graph(cyc):
             for f in step_fns:
@@ -153,11 +173,12 @@ def cpu_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline_gemv(mats, seconds: float):
+def cpu_baseline_gemv(mats, seconds: float, threads: int = 0):
     """The fp64 oracle on the same matrices (one step = every matrix once), repeated
-    until `seconds` of CPU time have passed; returns GB/s on the algorithmic bytes."""
+    until `seconds` of CPU time have passed; returns GB/s on the algorithmic bytes.
+    threads = 0: every core this process may use."""
     import oracle
-    oracle.set_threads(cpu_threads())
+    oracle.set_threads(threads or cpu_threads())
     done, nbytes = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -554,8 +575,17 @@ def bench_stream(args, torch):
             "reduce_us": round(red_s * 1e6, 2)}
 
 
+def emit(out):
+    """Prints the result line; records whether steps were graph-replayed."""
+    if isinstance(out.get("config"), dict):
+        out["config"]["launch"] = "eager" if EAGER else "graph"
+    print(json.dumps(out), flush=True)
+
+
 def main():
+    global EAGER
     args = parse()
+    EAGER = args.eager
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
@@ -569,7 +599,7 @@ def main():
     qd.lib()  # fail loudly if the HIP library is missing
 
     if args.config == "stream":
-        print(json.dumps(bench_stream(args, torch)), flush=True)
+        emit(bench_stream(args, torch))
         return
     if args.config in ("c1", "c2", "c5"):
         if args.config == "c1":
@@ -650,26 +680,29 @@ def main():
                  "us_per_step": round(rr["secs"] / args.steps * 1e6, 2)} for b, rr in results]
         if not args.no_cpu:
             v, done, el, thr = cpu_baseline_gemv(r["cpu_mats"], args.cpu_seconds)
+            v1, done1, el1, _ = cpu_baseline_gemv(r["cpu_mats"], args.cpu_seconds / 4, threads=1)
             out["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": thr,
                                    "kind": "oracle",
                                    "sample": f"{done} full step(s) of weight set 0 "
                                              f"({', '.join(f'{K}->{N}' for K, N in shapes)}, batch {batch}) "
-                                             f"in {el:.1f} s, fp64 C oracle"}
+                                             f"in {el:.1f} s, fp64 C oracle",
+                                   "value_1thread": round(v1, 4),
+                                   "sample_1thread": f"{done1} step(s) in {el1:.1f} s on one thread"}
         else:
             out["cpu_baseline"] = None
-        print(json.dumps(out), flush=True)
+        emit(out)
         return
     if args.config == "c4":
-        print(json.dumps(bench_chunk(args, torch, qd)), flush=True)
+        emit(bench_chunk(args, torch, qd))
         return
     if args.config == "verify":
-        print(json.dumps(bench_verify(args, torch, qd)), flush=True)
+        emit(bench_verify(args, torch, qd))
         return
     if args.config == "attn":
-        print(json.dumps(bench_attn(args, torch, qd)), flush=True)
+        emit(bench_attn(args, torch, qd))
         return
     if args.config in ("c3", "c4moe"):
-        print(json.dumps(bench_moe(args, torch, qd, prefill=args.config == "c4moe")), flush=True)
+        emit(bench_moe(args, torch, qd, prefill=args.config == "c4moe"))
         return
     raise SystemExit(f"config {args.config} is not wired into bench.py yet")
 
