@@ -397,6 +397,10 @@ Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
         c.u = S <= 4 ? 4 : 8;
         const int tiles = N / (64 / c.lpr);
         c.nw = std::max(1, std::min(16, pow2_floor(std::max(1, tiles / 256))));
+        // fewer tiles than CUs (a router): 8-wave workgroups share one staging
+        // of x instead of every wave staging it alone (measured 16 % faster
+        // on a 128-row router)
+        if (tiles < 256) c.nw = std::min(8, pow2_floor(std::max(1, tiles)));
         return c;
     }
     if (N >= 16384 && even) {
