@@ -129,6 +129,10 @@ struct Stage {
     static constexpr int QPC = XF == 1 ? CC / 4 : (XF == 2 ? 2 * QH : QH);  // uint4 per chunk
     static constexpr int CSZ = XF == 1 ? 4 : 8;                         // const bytes per chunk
     __host__ __device__ static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
+    // chunk-major layout for B > 1 vectors (fp16 path, see stage_x_cm)
+    __host__ __device__ static size_t bytes_cm(int B, int nc) {
+        return (size_t)nc * ((B * QPC + 1) * 16 + (B + 1) * 8);
+    }
 };
 
 // Slot of chunk c when each lane reads CPL consecutive chunks: chunk c goes
@@ -228,6 +232,62 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
             }
             float* cs = (float*)(xs + (size_t)nb * QPC * nc);
             cs[b * nc + c] = sum;
+        }
+    }
+}
+
+// Chunk-major staging of B > 1 fp16 vectors (the XF = 0 values and sums of
+// stage_x, rearranged):
+//   xs[c][b][q]  uint4, slot c at a stride of SC = B*QPC + 1 uint4 (the pad
+//                puts the 8 lanes of one LDS cycle in distinct banks);
+//   cs[c][b]     float2, slot c at a stride of B + 1 float2 (same reason).
+// Every (vector, quarter) of a chunk then sits at a compile-time offset from
+// the chunk's base, so the reads in group_rows take immediate offsets
+// instead of one address add each. Vectors b >= nb are not staged; their
+// results are never stored.
+template <int BITS, int B, int CPL = 1>
+__device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int nc, uint4* lds) {
+    using St = Stage<BITS, 0>;
+    constexpr int CC = St::CC;
+    constexpr int QPC = St::QPC;
+    constexpr int SC = B * QPC + 1;
+    uint4* xs = lds;
+    float2* cs = (float2*)(xs + (size_t)nc * SC);
+    for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
+        const int b = item / nc, cc = item - b * nc;
+        const int c = xslot<CPL>(cc, nc);
+        const uint16_t* xp = (const uint16_t*)x + (int64_t)b * xstride + (int64_t)(c0 + cc) * CC;
+        float s1 = 0.f, s16 = 0.f;
+        if constexpr (BITS == 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 raw = *(const uint4*)(xp + 8 * q);
+                uint16_t h[8];
+                h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
+                h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
+                h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
+                h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                xs[c * SC + b * QPC + q] = make_uint4(pack_h2(h[0], h[4]), pack_h2(h[1], h[5]),
+                                                      pack_h2(h[2], h[6]), pack_h2(h[3], h[7]));
+                s1 += (h2f(h[0]) + h2f(h[4])) + (h2f(h[2]) + h2f(h[6]));
+                s16 += (h2f(h[1]) + h2f(h[5])) + (h2f(h[3]) + h2f(h[7]));
+            }
+            cs[c * (B + 1) + b] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint4 raw = *(const uint4*)(xp + 8 * q);
+                uint16_t h[8];
+                h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
+                h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
+                h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
+                h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                xs[c * SC + b * QPC + q] = make_uint4(pack_h2(h[0], h[2]), pack_h2(h[1], h[3]),
+                                                      pack_h2(h[4], h[6]), pack_h2(h[5], h[7]));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s1 += h2f(h[i]);
+            }
+            cs[c * (B + 1) + b] = make_float2(1024.f * s1, s1);
         }
     }
 }
@@ -466,7 +526,7 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
 //   y[r][b] += s_r * (sum_k q_k x_k) + bias_r * (sum_k x_k).
 // The chunks' activations are read from LDS once and shared by the R rows;
 // slot[i] is the staged slot of chunk i.
-template <int BITS, int XF, int B, int R, int NCH>
+template <int BITS, int XF, int B, int R, int NCH, bool CM = false>
 __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const float (&sc)[R],
                                            const float (&bi)[R], const uint4* lds, int nb_staged,
                                            int nc, const int (&slot)[NCH], uint32_t magic,
@@ -475,8 +535,11 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
     constexpr int QPC = St::QPC;
     constexpr int NPL = XF == 2 ? 2 : 1;   // fp16 planes: value, or hi and lo
     const uint4* xs = lds;
+    static_assert(!CM || XF == 0, "chunk-major staging is for fp16 activations");
+    constexpr int SC = B * QPC + 1;   // chunk-major slot stride (uint4)
     if constexpr (XF == 0 || XF == 2) {
-        const float2* cs = (const float2*)(xs + (size_t)nb_staged * QPC * nc);
+        const float2* cs = CM ? (const float2*)(xs + (size_t)nc * SC)
+                              : (const float2*)(xs + (size_t)nb_staged * QPC * nc);
         float a1[R][B], a16[R][B];
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -492,7 +555,8 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-                        for (int b = 0; b < B; ++b) xq[pl][b] = xs[(b * QPC + pl * 4 + q) * nc + c];
+                        for (int b = 0; b < B; ++b)
+                            xq[pl][b] = CM ? xs[c * SC + b * QPC + q] : xs[(b * QPC + pl * 4 + q) * nc + c];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const uint4& w4 = cw[ch][r];
@@ -520,7 +584,8 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-                        for (int b = 0; b < B; ++b) xq[pl][b] = xs[(b * QPC + pl * 2 + q) * nc + c];
+                        for (int b = 0; b < B; ++b)
+                            xq[pl][b] = CM ? xs[c * SC + b * QPC + q] : xs[(b * QPC + pl * 2 + q) * nc + c];
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const uint4& w4 = cw[ch][r];
@@ -548,7 +613,7 @@ __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const floa
             float kx = 0.f, ky = 0.f;
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) {
-                const float2 k = cs[b * nc + slot[ch]];
+                const float2 k = CM ? cs[slot[ch] * (B + 1) + b] : cs[b * nc + slot[ch]];
                 kx += k.x;
                 ky += k.y;
             }

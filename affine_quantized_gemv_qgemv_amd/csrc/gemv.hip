@@ -78,6 +78,17 @@ struct Round {
     uint16_t sc[U][R], bi[U][R];   // raw scale / bias (or zero-point byte) bits; masked when consumed
 };
 
+// Staging for the kernel's activation layout: chunk-major for several fp16
+// vectors, the plain layout otherwise.
+template <int BITS, int XF, int B, int CPL>
+__device__ __forceinline__ void stage_x_any(const void* x, int kind, int64_t xstride, int nb, int c0,
+                                            int nc, uint4* lds) {
+    if constexpr (XF == 0 && B > 1)
+        stage_x_cm<BITS, B, CPL>(x, xstride, nb, c0, nc, lds);
+    else
+        stage_x<BITS, XF, CPL>(x, kind, xstride, nb, c0, nc, lds);
+}
+
 template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL, int FMT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
     GemvArgs a) {
@@ -86,6 +97,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     constexpr int CPG = 64 / CC;       // chunks per group of 64
     constexpr int RPI = 64 / LPR;      // rows per wave instruction
     constexpr int ROWS = RPI * R;      // rows per tile
+    constexpr bool CM = XF == 0 && B > 1;   // chunk-major staging (stage_x_cm)
     const int C16 = a.K / CC;
     const int c0 = blockIdx.y * a.chunks_split;
     const int nc = min(a.chunks_split, C16 - c0);
@@ -197,9 +209,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
                         cw[ch][r] = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u,
                                                v.z ^ 0x80808080u, v.w ^ 0x80808080u);
                     }
-                group_rows<BITS, XF, B, R, CPL>(cw, sc, bi, lds, a.nb, nc, slot, magic, y);
+                group_rows<BITS, XF, B, R, CPL, CM>(cw, sc, bi, lds, a.nb, nc, slot, magic, y);
             } else {
-                group_rows<BITS, XF, B, R, CPL>(buf.cw[u], sc, bi, lds, a.nb, nc, slot, magic, y);
+                group_rows<BITS, XF, B, R, CPL, CM>(buf.cw[u], sc, bi, lds, a.nb, nc, slot, magic, y);
             }
         }
         if (sg == RPT - 1) {
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
                                a.eps, rot, lds);
     else
-        stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+        stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; rd += 2) {
         issue(Bf, rd + 1);
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
                                a.eps, rot, lds);
     else
-        stage_x<BITS, XF, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+        stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; ++rd) {
         if (rd > 0) issue(A, rd);
@@ -293,10 +305,14 @@ hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     // chunks per split: a multiple of 4 so a lane's CPL chunks never straddle
     // a split
     auto per_of = [&](int sp) { return (((C16 + sp - 1) / sp) + 3) & ~3; };
-    while (St::bytes(base.nb, per_of(splits)) > budget && splits < C16) ++splits;
+    // the kernel's staging layout (chunk-major for several fp16 vectors)
+    auto bytes = [&](int nc) {
+        return (XF == 0 && B > 1) ? St::bytes_cm(B, nc) : St::bytes(base.nb, nc);
+    };
+    while (bytes(per_of(splits)) > budget && splits < C16) ++splits;
     const int per = std::min(per_of(splits), C16);
     splits = (C16 + per - 1) / per;
-    const size_t lds = St::bytes(base.nb, per);
+    const size_t lds = bytes(per);
     if (lds > dev.max_lds_per_block) return hipErrorInvalidValue;
 
     GemvArgs a = base;
