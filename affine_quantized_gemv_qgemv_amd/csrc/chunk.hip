@@ -130,8 +130,7 @@ struct StageIO {
                     acc = bf16_pair_sum(v.w, acc);
                 }
             }
-#pragma unroll
-            for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+            acc = seg_sum<TPR>(acc);   // the TPR adjacent lanes of the row
             xsum[r * SG + gi] = acc;   // every lane of the row stores the same sum
             if constexpr (F16) xsumT[gi * MT + r] = acc;
         }

@@ -100,11 +100,37 @@ __device__ __forceinline__ float word_i8_f32(uint32_t w, const float4& xa, float
     return acc;
 }
 
-// Sum over the `width` lanes of an aligned lane segment (width a power of two).
+// v from another lane through DPP (CTRL: quad_perm 0xB1 = lane ^ 1, 0x4E =
+// lane ^ 2; 0x141 = mirror within each 8 lanes; 0x140 = mirror within each
+// row of 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the `width` lanes of an aligned lane segment (width a power of two),
+// returned to every lane of the segment, without LDS traffic: pairs of lanes,
+// then quads, through DPP; 8- and 16-lane groups through the half-row and
+// row mirrors (after the previous steps every lane of a group holds the same
+// value, so a mirror pairs the groups as an xor would); rows of 16 and halves
+// of 32 through v_permlane16_swap / v_permlane32_swap.
 template <int WIDTH>
 __device__ __forceinline__ float seg_sum(float v) {
-#pragma unroll
-    for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    static_assert(WIDTH >= 1 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "segment width");
+    if constexpr (WIDTH >= 2) v += dpp_f<0xB1>(v);
+    if constexpr (WIDTH >= 4) v += dpp_f<0x4E>(v);
+    if constexpr (WIDTH >= 8) v += dpp_f<0x141>(v);
+    if constexpr (WIDTH >= 16) v += dpp_f<0x140>(v);
+    if constexpr (WIDTH >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (WIDTH >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     return v;
 }
 

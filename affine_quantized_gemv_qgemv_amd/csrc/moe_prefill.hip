@@ -272,8 +272,7 @@ struct XStage {
                     acc = F16 ? dot2(vv[j], 0x3C003C00u, acc) : bf16_pair_sum(vv[j], acc);
             }
         }
-#pragma unroll
-        for (int o = 1; o < TPG; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        acc = seg_sum<TPG>(acc);   // the TPG adjacent lanes of (row, group)
         // the TPG threads of (row, group) store the same sum
         xsum[rr * XSG + gi] = acc;
         xsum[SUMS + gi * 32 + rr] = acc;
