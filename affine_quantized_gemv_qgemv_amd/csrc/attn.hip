@@ -141,11 +141,13 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(AttnArgs a) {
     }
     // sum over the row groups of the wave (lanes dl, dl + LPR, ...)
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[h][i] += __shfl_xor(o[h][i], off, 64);
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (LPR <= 8) o[h][i] = xor_add<8>(o[h][i]);
+            if constexpr (LPR <= 16) o[h][i] = xor_add<16>(o[h][i]);
+            o[h][i] = xor_add<32>(o[h][i]);
+        }
     if (rg == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)

@@ -134,6 +134,36 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v;
 }
 
+// Maximum over the 64 lanes of a wave, in every lane (the same pairings as
+// seg_sum<64>).
+__device__ __forceinline__ float wave_max_f(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// v + (v of lane ^ OFF) for OFF = 8, 16 or 32: sums lanes that hold the same
+// position of different lane groups (row_ror:8 within each row of 16, then
+// the row and half swaps).
+template <int OFF>
+__device__ __forceinline__ float xor_add(float v) {
+    static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane offset");
+    if constexpr (OFF == 8) return v + dpp_f<0x128>(v);
+    if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Activation staging into LDS.
 //
@@ -470,8 +500,7 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
                 }
             }
             ss = seg_sum<64>(ss);
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+            mx = wave_max_f(mx);
             if (lane == 0) {
                 red[b * kRotWaves + wg] = ss;
                 red[(kRotMaxB + b) * kRotWaves + wg] = mx;
