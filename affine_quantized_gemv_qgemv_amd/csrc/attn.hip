@@ -184,25 +184,42 @@ __global__ __launch_bounds__(AT_THREADS) void attn_split_kernel(AttnArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+    constexpr int NW = D / 64;
     __shared__ float ms[AT_MAXSPLIT], ls[AT_MAXSPLIT], cs[AT_MAXSPLIT];
-    __shared__ float Ls;
+    __shared__ float wred[NW], wsum[NW];
     const int h = blockIdx.x, d = threadIdx.x;
+    const int lane = d & 63, wave = d >> 6;
     const float* p = a.part + (int64_t)h * (D + 2);
     const int64_t stride = (int64_t)a.Hq * (D + 2);
+    // m = max over the splits: strided loads, then a wave reduction and the
+    // NW wave maxima
+    float lm = -INFINITY;
     for (int s = d; s < a.nsplit; s += D) {
-        ms[s] = p[s * stride + D];
+        const float m = p[s * stride + D];
+        ms[s] = m;
         ls[s] = p[s * stride + D + 1];
+        lm = fmaxf(lm, m);
     }
+    lm = wave_max_f(lm);
+    if (lane == 0) wred[wave] = lm;
     __syncthreads();
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, ms[s]);
-    for (int s = d; s < a.nsplit; s += D) cs[s] = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
-    __syncthreads();
-    if (d == 0) {
-        float L = 0.f;
-        for (int s = 0; s < a.nsplit; ++s) L = fmaf(ls[s], cs[s], L);
-        Ls = L;
+    float M = wred[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, wred[w]);
+    // weights e^(m_s - m) and L = sum_s l_s e^(m_s - m), reduced in a fixed
+    // tree (each thread its own splits, then the wave, then the waves in order)
+    float lp = 0.f;
+    for (int s = d; s < a.nsplit; s += D) {
+        const float c = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
+        cs[s] = c;
+        lp = fmaf(ls[s], c, lp);
     }
+    lp = seg_sum<64>(lp);
+    if (lane == 0) wsum[wave] = lp;
+    __syncthreads();
+    float L = wsum[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) L += wsum[w];
     // o over the splits in order; each batch of 32 loads is issued before
     // any is used (clamped indices, weight 0 past the end), so a combine
     // costs about one memory latency per 32 splits
@@ -214,8 +231,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) O = fmaf(v[i], s0 + i < a.nsplit ? cs[s0 + i] : 0.f, O);
     }
-    __syncthreads();
-    a.out[(int64_t)h * D + d] = O / Ls;
+    a.out[(int64_t)h * D + d] = O / L;
 }
 
 // Splits for n occupied slots: about two workgroups per CU over all heads,
