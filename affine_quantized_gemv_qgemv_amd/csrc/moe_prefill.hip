@@ -113,17 +113,31 @@ __global__ __launch_bounds__(1024) void moe_prep_kernel(const int32_t* __restric
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0, rb = 0;
-        for (int e = 0; e < E; ++e) {
-            const int c = cnt[e];
-            cnt[e] = run;
-            rbl[e] = rb;
-            run += c;
-            rb += (c + 31) / 32;
+    // exclusive prefix sums of the counts and of their 32-row blocks: a
+    // double-buffered Hillis-Steele scan over the E + 1 entries (the last one
+    // 0, so entry E receives the totals), log2 steps instead of a serial walk
+    {
+        __shared__ int sc[2][PREP_MAX_E + 1], sb[2][PREP_MAX_E + 1];
+        for (int e = tid; e <= E; e += bs) {
+            const int c = e < E ? cnt[e] : 0;
+            sc[0][e] = c;
+            sb[0][e] = (c + 31) / 32;
         }
-        cnt[E] = run;
-        rbl[E] = rb;
+        __syncthreads();
+        int cur = 0;
+        for (int off = 1; off <= E; off <<= 1) {
+            for (int e = tid; e <= E; e += bs) {
+                sc[cur ^ 1][e] = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
+                sb[cur ^ 1][e] = sb[cur][e] + (e >= off ? sb[cur][e - off] : 0);
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+        // inclusive -> exclusive
+        for (int e = tid; e <= E; e += bs) {
+            cnt[e] = e ? sc[cur][e - 1] : 0;
+            rbl[e] = e ? sb[cur][e - 1] : 0;
+        }
     }
     __syncthreads();
     for (int e = tid; e <= E; e += bs) {
