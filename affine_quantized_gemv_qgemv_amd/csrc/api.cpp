@@ -57,6 +57,8 @@ qd_status check_matrix(const char* fn, int32_t N, int32_t K, int32_t group_size)
     if (N < 1) return fail(QD_ERR_INVALID_ARGUMENT, "%s: N = %d must be >= 1", fn, N);
     if (K < 64 || K % 64)
         return fail(QD_ERR_INVALID_ARGUMENT, "%s: K = %d must be a positive multiple of 64", fn, K);
+    if (K > (1 << 22))
+        return fail(QD_ERR_UNSUPPORTED, "%s: K = %d exceeds 4194304", fn, K);
     return QD_OK;
 }
 

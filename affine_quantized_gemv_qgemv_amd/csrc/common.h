@@ -47,6 +47,29 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   false);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (32-bit data format
+// word, no stride or swizzle). A load through it takes a 32-bit byte offset
+// from a VGPR and folds constant offsets into the instruction, so a tile's
+// loads need one 32-bit multiply-add per row instead of 64-bit address
+// arithmetic per load; a read at or past `bytes` returns zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFFll ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ uint8_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }

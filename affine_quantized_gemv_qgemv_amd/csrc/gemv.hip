@@ -135,11 +135,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     // Loads are unconditional inside a wave-uniform step test: rows past N and
     // chunks past the staged range read a clamped, valid address and get a
     // zero scale and bias, so they add nothing. (Branches around individual
-    // loads would make the compiler wait for every load in flight.)
-    auto issue = [&](Round<R, U, CPL>& buf, int rd) {
-        if (rd >= nrounds) return;
-        const int tile = t0 + (rd / RPT) * tstep;
-        const int sg = rd - (rd / RPT) * RPT;
+    // loads would make the compiler wait for every load in flight.) Each
+    // round's loads go through buffer resources based at the tile's first
+    // row, so per-lane offsets are 32-bit and the chunk and step offsets are
+    // instruction immediates.
+    const uint32_t rowb = (uint32_t)(wpr * 4);   // bytes of codes per row (< 2^24)
+    auto issue = [&](Round<R, U, CPL>& buf, int tile, int sg) {
+        const int64_t r0 = (int64_t)tile * ROWS;
+        const int rlast = a.N - 1 - (int)r0;     // last row of the matrix, tile-relative
+        const auto wr = buf_rsrc(a.wq + r0 * wpr, (a.N - r0) * (int64_t)rowb);
+        const auto sr = buf_rsrc(a.s + r0 * G, (a.N - r0) * (int64_t)G * 2);
+        __amdgpu_buffer_rsrc_t br;
+        if constexpr (FMT == W_AFFINE)
+            br = buf_rsrc(a.b + r0 * G, (a.N - r0) * (int64_t)G * 2);
+        else if constexpr (FMT == W_MIRAI_M)
+            br = buf_rsrc(a.zp + r0 * a.zstride, (a.N - r0) * (int64_t)a.zstride);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
@@ -147,18 +157,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             const int gc = c0 + min(c, nc - CPL);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = tile * ROWS + r * RPI + seg;
-                const int rc = min(row, a.N - 1);
+                const int lr = min(r * RPI + seg, rlast);
+                const uint32_t wo = (uint32_t)__umul24(lr, (int)rowb) + (uint32_t)gc * 16u;
 #pragma unroll
-                for (int ch = 0; ch < CPL; ++ch)
-                    buf.cw[u][ch][r] =
-                        *(const uint4*)(a.wq + (int64_t)rc * wpr + (int64_t)(gc + ch) * 4);
-                const int64_t gi = (int64_t)rc * G + gc / CPG;
-                buf.sc[u][r] = a.s[gi];
+                for (int ch = 0; ch < CPL; ++ch) buf.cw[u][ch][r] = buf_load16(wr, wo + 16u * ch);
+                const uint32_t go = (uint32_t)__umul24(lr, G) + (uint32_t)(gc / CPG);
+                buf.sc[u][r] = buf_load2(sr, 2u * go);
                 if constexpr (FMT == W_AFFINE)
-                    buf.bi[u][r] = a.b[gi];
+                    buf.bi[u][r] = buf_load2(br, 2u * go);
                 else if constexpr (FMT == W_MIRAI_M)   // byte holding groups 2j, 2j + 1
-                    buf.bi[u][r] = a.zp[(int64_t)rc * a.zstride + (gc / CPG) / 2];
+                    buf.bi[u][r] = buf_load1(br, (uint32_t)__umul24(lr, a.zstride) +
+                                                     (uint32_t)((gc / CPG) / 2));
             }
         }
     };
@@ -170,10 +179,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         for (int bb = 0; bb < B; ++bb) y[r][bb] = 0.f;
 
     const uint32_t magic = in_vgpr(kMagic16);
-    auto consume = [&](const Round<R, U, CPL>& buf, int rd) {
-        if (rd >= nrounds) return;
-        const int tile = t0 + (rd / RPT) * tstep;
-        const int sg = rd - (rd / RPT) * RPT;
+    auto consume = [&](const Round<R, U, CPL>& buf, int tile, int sg) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
@@ -235,31 +241,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         }
     };
 
-#ifdef QD_GEMV_DOUBLE_BUFFER
-    Round<R, U, CPL> A, Bf;
-    issue(A, 0);  // the first weights are in flight while the activations are staged
-    if constexpr (XF == 2)
-        stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
-                               a.eps, rot, lds);
-    else
-        stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
-    __syncthreads();
-    for (int rd = 0; rd < nrounds; rd += 2) {
-        issue(Bf, rd + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(A, rd);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(A, rd + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(Bf, rd + 1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#else
     // One buffer per wave: a round's loads are all issued before any is used;
     // other waves on the SIMD keep the memory system busy while this one
     // computes.
     Round<R, U, CPL> A;
-    issue(A, 0);  // the first weights are in flight while the activations are staged
+    if (nrounds > 0) issue(A, t0, 0);  // in flight while the activations are staged
     if constexpr (XF == 2)
         stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
                                a.eps, rot, lds);
@@ -267,10 +253,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
     __syncthreads();
     for (int rd = 0; rd < nrounds; ++rd) {
-        if (rd > 0) issue(A, rd);
-        consume(A, rd);
+        const int tile = t0 + (rd / RPT) * tstep;
+        const int sg = rd - (rd / RPT) * RPT;
+        if (rd > 0) issue(A, tile, sg);
+        consume(A, tile, sg);
     }
-#endif
 }
 
 __global__ void fill_zero_kernel(float* p, int64_t n) {

@@ -357,7 +357,7 @@ struct MoeCfg {
 };
 
 MoeCfg moe_cfg() {
-    MoeCfg c{4, 16, 1};
+    MoeCfg c{4, 0, 1};   // dn_nw 0: sized to the row count
 #ifdef QD_TUNING
     if (qd_tune_moe[0]) c = MoeCfg{qd_tune_moe[0], qd_tune_moe[1], qd_tune_moe[2]};
 #endif
@@ -394,7 +394,11 @@ hipError_t launch_down_r(const MoeBArgs& a, int nw, hipStream_t st) {
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     const int ntiles = (a.H + (64 / LPR) * R - 1) / ((64 / LPR) * R);
     auto kern = moe_down_kernel<LPR, R, U, CPL>;
-    // every workgroup stages all k*I + Is activations: at most one per CU
+    // Every workgroup stages all k*I + Is activations: at most one per CU,
+    // each with just enough waves (up to 16) that the rows spread over all
+    // CUs (2816 rows: 256 workgroups of 11 waves rather than 176 of 16).
+    const int cus = device_info().cus;
+    if (nw <= 0) nw = std::min(16, std::max(1, (ntiles + cus - 1) / cus));
     const int threads = 64 * nw;
     const int grid = std::min(grid_for(kern, threads, lds, ntiles), device_info().cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);

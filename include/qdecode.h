@@ -38,7 +38,8 @@
  *     nothing is written and the status says why; qd_last_error() gives a
  *     thread-local message. A launch failure returns QD_ERR_HIP.
  *   - Pointers must be 16-byte aligned; group_size must be 64; K must be a
- *     multiple of 64.
+ *     multiple of 64 and at most 4194304 (2^22; larger K returns
+ *     QD_ERR_UNSUPPORTED: the kernels address a row in 32 bits).
  *   - The calls are stateless and may be issued from several threads.
  */
 #ifndef QDECODE_H

@@ -65,6 +65,9 @@ def test_gemv_argument_errors(fn):
     assert gemv(fn, x=MIS) == E.QD_ERR_MISALIGNED
     assert gemv(fn, s=MIS) == E.QD_ERR_MISALIGNED
     assert gemv(fn, dt=7) == E.QD_ERR_UNSUPPORTED
+    # rows are addressed with 32-bit offsets: K is capped at 2^22
+    assert gemv(fn, K=(1 << 22) + 64) == E.QD_ERR_UNSUPPORTED
+    assert "4194304" in qd.last_error()
 
 
 def test_affine4_batch_limit_is_eight():
@@ -175,6 +178,7 @@ def test_chunk_argument_errors():
     assert f(M=0) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(M=129) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(K=96) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(K=(1 << 22) + 64) == qd.QD_ERR_UNSUPPORTED
     assert f(g=128) == qd.QD_ERR_UNSUPPORTED
     assert f(wq=None) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(x=MIS) == qd.QD_ERR_MISALIGNED
