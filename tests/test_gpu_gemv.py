@@ -112,6 +112,21 @@ def test_int8_token_chunk_deterministic_and_in_bounds():
 
 
 @pytest.mark.parametrize("bits", [4, 8])
+def test_largest_k(bits):
+    # K = 2^22, the largest the ABI accepts: rows are addressed with 32-bit
+    # offsets from a tile's first row, and x is split over many K ranges
+    # whose partial rows meet through atomics
+    K, N = 1 << 22, 3
+    w = synth.affine_weights(bits, N, K, cfg=209, set_id=bits)
+    for batch in (1, 2):
+        xb = draw_x(batch, K, "f16", 40 + batch)
+        print(f"bits={bits} N={N} K={K} batch={batch}", flush=True)
+        y = run_gemv(bits, w, xb).cpu().numpy()
+        yr, a = ref_gemv(w, xb)
+        assert_within(y, yr, a, f"bits={bits} K=2^22 batch={batch}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
 def test_one_hot_is_bit_exact(bits):
     N, K = 64, 2048
     w = synth.affine_weights(bits, N, K, cfg=203, set_id=bits)
