@@ -111,6 +111,21 @@ def test_int8_token_chunk_deterministic_and_in_bounds():
     assert_within(y1.cpu().numpy(), yr, a, "int8 chunk")
 
 
+@pytest.mark.parametrize("N", [16385, 16387, 16390])
+def test_ragged_last_tile_of_two_row_tiles(N):
+    # N >= 16384 with whole groups per lane takes two-row tiles: the last tile
+    # holds one valid row (or two of four) and its other rows are clamped
+    K = 4096
+    w = synth.affine_weights(4, N, K, cfg=210, set_id=N)
+    xb = draw_x(1, K, "f16", N)
+    print(f"N={N} K={K}", flush=True)
+    y = run_gemv(4, w, xb).cpu().numpy()
+    r = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([r.choice(N, 256, replace=False), np.arange(N - 8, N), [0]]))
+    yr, a = ref_gemv(w, xb, rows=rows)
+    assert_within(y[:, rows], yr, a, f"N={N}")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_largest_k(bits):
     # K = 2^22, the largest the ABI accepts: rows are addressed with 32-bit
