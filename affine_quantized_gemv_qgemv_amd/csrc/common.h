@@ -422,6 +422,16 @@ __device__ __forceinline__ void load8(const uint16_t* p, int kind, float (&o)[8]
     }
 }
 
+__device__ __forceinline__ void cvt8(uint4 raw, int kind, float (&o)[8]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t a = w[i] & 0xFFFF, b = w[i] >> 16;
+        o[2 * i] = kind == X_F16 ? h2f(a) : bf2f(a);
+        o[2 * i + 1] = kind == X_F16 ? h2f(b) : bf2f(b);
+    }
+}
+
 // hi/lo fp16 pairs of (a, b), and the fp32 sum of hi + lo added to s.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo, float& s) {
     typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
@@ -441,10 +451,15 @@ constexpr int kRotShared = 2 * kRotMaxB * kRotWaves + 2 * kRotMaxB;
 // Stage chunks [c0, c0 + nc) of the rotated x[b][K] (b < nb); gamma (K, x's
 // kind) and signs (K/32 words) may be NULL. rs is kRotShared floats of LDS;
 // on return rs[kRotMaxB + b] holds 2^-e of vector b. Every thread must call.
-template <int BITS, int CPL = 1>
+// after_loads() runs once per thread, right after the thread's first
+// activation loads are issued (or before the first barrier if it has none):
+// loads the caller issues there return after the activations (a wave's
+// loads return in order), so the transform overlaps their latency.
+template <int BITS, int CPL, typename F>
 __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, int nb, int c0,
                                             int nc, const uint16_t* gamma, const uint32_t* signs,
-                                            float eps, float* rs, uint4* lds) {
+                                            float eps, float* rs, uint4* lds, F&& after_loads) {
+    bool issued = false;
     using St = Stage<BITS, 2>;
     constexpr int CC = St::CC, QH = St::QH, QPC = St::QPC;
     constexpr int CPB = 32 / CC;   // chunks per block
@@ -481,12 +496,24 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
                 const int k0 = (c0 + bl * CPB) * CC + 16 * hh;
                 const uint32_t sg = signs ? signs[k0 / 32] >> (16 * hh) : 0u;
                 float v[16];
+                uint4 xr[2], gr[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    xr[q] = *(const uint4*)(xb + k0 + 8 * q);
+                    if (gamma) gr[q] = *(const uint4*)(gamma + k0 + 8 * q);
+                }
+                if (!issued) {   // the caller's loads go out behind these
+                    __builtin_amdgcn_sched_barrier(0);
+                    after_loads();
+                    __builtin_amdgcn_sched_barrier(0);
+                    issued = true;
+                }
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     float t[8], g[8];
-                    load8(xb + k0 + 8 * q, kind, t);
+                    cvt8(xr[q], kind, t);
                     if (gamma) {
-                        load8(gamma + k0 + 8 * q, kind, g);
+                        cvt8(gr[q], kind, g);
                     } else {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) g[i] = 1.f;
@@ -530,6 +557,7 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
             }
         }
     }
+    if (!issued) after_loads();
     __syncthreads();
     if (threadIdx.x < nb) {
         const int b = threadIdx.x;

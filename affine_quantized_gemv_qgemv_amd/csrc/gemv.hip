@@ -245,12 +245,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     // other waves on the SIMD keep the memory system busy while this one
     // computes.
     Round<R, U, CPL> A;
-    if (nrounds > 0) issue(A, t0, 0);  // in flight while the activations are staged
-    if constexpr (XF == 2)
+    if constexpr (XF == 2) {
+        // the first weight loads go out behind the activation loads, so the
+        // transform runs while they are in flight
         stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma, a.signs,
-                               a.eps, rot, lds);
-    else
+                               a.eps, rot, lds, [&]() { if (nrounds > 0) issue(A, t0, 0); });
+    } else {
+        if (nrounds > 0) issue(A, t0, 0);  // in flight while the activations are staged
         stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
+    }
     __syncthreads();
     for (int rd = 0; rd < nrounds; ++rd) {
         const int tile = t0 + (rd / RPT) * tstep;
