@@ -8,6 +8,7 @@
 // bad argument is reported identically on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -188,9 +189,17 @@ int occupancy(const void* func, int threads, size_t lds_bytes) {
         auto it = cache.find(key);
         if (it != cache.end()) return it->second;
     }
-    if (lds_bytes > 65536)
+    // allow launches up to the device's per-workgroup maximum less the
+    // kernel's static LDS (a kernel is launched with several dynamic sizes;
+    // the attribute must cover the largest)
+    if (lds_bytes > 65536) {
+        hipFuncAttributes fa{};
+        size_t stat = 0;
+        if (hipFuncGetAttributes(&fa, func) == hipSuccess) stat = fa.sharedSizeBytes;
+        const size_t maxdyn = device_info().max_lds_per_block - std::min(stat, device_info().max_lds_per_block);
         (void)hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds_bytes);
+                                  (int)std::max(maxdyn, lds_bytes));
+    }
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, func, threads, lds_bytes) != hipSuccess ||
         n < 1)
@@ -420,7 +429,7 @@ qd_status qattn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t*
     if (ws_bytes < need)
         return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
     return from_hip(qd::launch_attn_decode(q, k_new, v_new, k_cache, v_cache, Hq, Hkv, D, cap,
-                                           window, pos, scale, out, workspace,
+                                           window, pos, scale, out, workspace, ws_bytes,
                                            (hipStream_t)stream),
                     fn);
 }

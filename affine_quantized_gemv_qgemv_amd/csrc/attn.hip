@@ -237,19 +237,29 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
 // Splits for n occupied slots: about two workgroups per CU over all heads,
 // each at least one load round of rows (a multiple of 32: two row steps of
 // 16), which also keeps a short cache's combine to one batch of 32 splits.
-static void attn_split(int n, int Hkv, int& nsplit, int& chunk) {
+static int attn_split_want(int n, int Hkv) {
     const int cus = device_info().cus;
-    int want = std::max(1, (2 * cus + Hkv - 1) / Hkv);
-    want = std::min(std::min(want, AT_MAXSPLIT), (n + 31) / 32);
+    const int want = std::max(1, (2 * cus + Hkv - 1) / Hkv);
+    return std::max(1, std::min(std::min(want, AT_MAXSPLIT), (n + 31) / 32));
+}
+
+static void attn_split(int n, int Hkv, int& nsplit, int& chunk) {
+    const int want = attn_split_want(n, Hkv);
     chunk = (n + want - 1) / want;
     chunk = (chunk + 31) & ~31;
     nsplit = (n + chunk - 1) / chunk;
 }
 
-size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap) {
-    int nsplit, chunk;
-    attn_split(cap, Hkv, nsplit, chunk);
+// Workspace for every occupancy n <= cap. The split count of n is
+// ceil(n / chunk) with chunk >= ceil(n / want(n)), so it never exceeds
+// want(n) <= want(cap); it is not monotonic in n (the chunk is rounded up
+// to 32 rows), so the size comes from that bound, not from nsplit(cap).
+static size_t attn_part_bytes(int nsplit, int Hq, int D) {
     return (size_t)nsplit * Hq * (D + 2) * sizeof(float);
+}
+
+size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap) {
+    return attn_part_bytes(attn_split_want(cap, Hkv), Hq, D);
 }
 
 template <int D>
@@ -273,7 +283,7 @@ static hipError_t attn_launch_d(const AttnArgs& a, int G, hipStream_t st) {
 hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* kc, uint16_t* vc, int Hq, int Hkv, int D, int cap,
                               int window, int pos, float scale, float* out, void* ws,
-                              hipStream_t st) {
+                              size_t ws_bytes, hipStream_t st) {
     AttnArgs a{};
     a.q = q;
     a.k_new = k_new;
@@ -290,6 +300,9 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const ui
     a.slot = window > 0 ? pos % window : pos;
     a.scale = scale;
     attn_split(a.n, Hkv, a.nsplit, a.chunk);
+    // the split partials must fit the caller's workspace (they always do
+    // when it holds attn_workspace_bytes(cap); checked before any launch)
+    if (attn_part_bytes(a.nsplit, Hq, D) > ws_bytes) return hipErrorInvalidValue;
     const int G = Hq / Hkv;
     if (D == 64) return attn_launch_d<64>(a, G, st);
     if (D == 128) return attn_launch_d<128>(a, G, st);

@@ -6,20 +6,27 @@
 // inputs, w = s*q + b. Codes are packed LSB-first, eight (or four) per
 // uint32 along the input dimension.
 //
-// Arithmetic used on the fp16-activation path
-// -------------------------------------------
+// Arithmetic of the GEMV core
+// ---------------------------
 // OR-ing a 4-bit code into the low mantissa bits of fp16 1024.0 (0x6400)
 // gives exactly 1024 + q; OR-ing it one nibble higher gives 1024 + 16q.
 // One v_and_or_b32 therefore turns two codes of a word (the nibbles at
-// bits 0 and 16, or 4 and 20) into a packed half2, and v_dot2_f32_f16
-// multiplies such a pair with two activations and adds both products into
-// an fp32 accumulator. Each product is exact in fp32 (11-bit times 11-bit
-// significands). The 1024 offsets and the factor 16 are removed once per
-// 16-byte chunk with per-chunk activation sums computed while staging x:
-//     sum_k q_k x_k = acc_1 + acc_16 / 16 - (1024 * sum_1 x + 64 * sum_16 x)
+// bits 0 and 16, or 4 and 20) into a packed half2. One v_pk_add_f16 then
+// subtracts 1024 + c (or 1024 + 16c) from both halves, which is exact in
+// fp16 and leaves the centred codes q - c (or 16 (q - c)) with c the
+// centre of the format: 8 for affine 4-bit codes, 128 for 8-bit codes, the
+// group's zero point z for Mirai-M. v_dot2_f32_f16 multiplies such a pair
+// with two fp16 activations (both products exact in fp32) and adds them
+// into an fp32 accumulator; fp32 activations take v_fma_mix_f32 instead.
+// Because the offset is gone before anything is summed, the accumulators
+// hold sums of (q - c) x whose rounding follows |q - c| |x|, and a weight
+// that sits at the centre contributes exactly zero. Per group:
+//     sum_k (q_k - c) x_k = acc_1 + acc_16 / 16
 // where class "1" holds the codes at nibbles 0, 2, 4, 6 and class "16"
-// those at nibbles 1, 3, 5, 7. The affine epilogue then adds
-// s_g * (that sum) + b_g * (sum of the chunk's activations).
+// those at nibbles 1, 3, 5, 7, and the affine epilogue adds
+//     s_g * (that sum) + (b_g + c s_g) * (sum of the group's activations),
+// which is s_g q + b_g summed against x; the Mirai formats have no second
+// term (w = s (q - z), or s q for signed codes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +39,13 @@ namespace qd {
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kMagic16 = 0x64006400u;  // fp16 pair (1024, 1024)
+// fp16 pairs -(1024 + c) and -(1024 + 16 c): the centring subtrahends
+constexpr uint32_t kNeg1032 = 0xE408E408u;  // 4-bit codes, c = 8, class 1
+constexpr uint32_t kNeg1152 = 0xE480E480u;  // 4-bit class 16 (c = 8), and 8-bit codes (c = 128)
+
+// Subtrahend pairs for a per-group centre z in [0, 15] (Mirai-M zero point):
+// 0xE400 | z is fp16 -(1024 + z), 0xE400 | 16 z is -(1024 + 16 z).
+__device__ __forceinline__ uint32_t neg_pair(uint32_t h) { return h | (h << 16); }
 
 // A value the compiler must keep in a VGPR. Used for the fp16 magic so that
 // (w & mask) | magic is selected as one v_and_or_b32 (a VOP3 on gfx9 reads at
@@ -45,6 +59,19 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t c) {
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c,
                                   false);
+}
+
+// Packed fp16 add of two half2 (one v_pk_add_f16).
+__device__ __forceinline__ uint32_t pk_addh(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) + __builtin_bit_cast(half2v, b));
+}
+
+// fp32 accumulation of a packed fp16 pair against two fp32 activations
+// (two v_fma_mix_f32).
+__device__ __forceinline__ float fma_pair(uint32_t p, float x0, float x1, float acc) {
+    const half2v h = __builtin_bit_cast(half2v, p);
+    acc = fmaf((float)h.x, x0, acc);
+    return fmaf((float)h.y, x1, acc);
 }
 
 // Raw buffer resource over `bytes` bytes from `base` (32-bit data format
@@ -89,38 +116,6 @@ __device__ __forceinline__ float load_x(const void* x, int kind, int64_t i) {
     if (kind == X_F16) return h2f(((const uint16_t*)x)[i]);
     if (kind == X_BF16) return bf2f(((const uint16_t*)x)[i]);
     return ((const float*)x)[i];
-}
-
-// ---------------------------------------------------------------------------
-// Per-chunk partial dot products. A chunk is 16 bytes of codes (32 int4 or
-// 16 int8 codes = 4 words); the activations for it sit in LDS in the order
-// the unpacking produces the codes.
-// ---------------------------------------------------------------------------
-
-// int4 codes, fp32 activations: lo bytes are q0,q2,q4,q6 and hi bytes
-// q1,q3,q5,q7; xa = (x0,x2,x4,x6), xb = (x1,x3,x5,x7).
-__device__ __forceinline__ float word_i4_f32(uint32_t w, const float4& xa, const float4& xb,
-                                             float acc) {
-    const uint32_t lo = w & 0x0F0F0F0Fu;
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-    acc = fmaf((float)(lo & 0xFFu), xa.x, acc);
-    acc = fmaf((float)((lo >> 8) & 0xFFu), xa.y, acc);
-    acc = fmaf((float)((lo >> 16) & 0xFFu), xa.z, acc);
-    acc = fmaf((float)(lo >> 24), xa.w, acc);
-    acc = fmaf((float)(hi & 0xFFu), xb.x, acc);
-    acc = fmaf((float)((hi >> 8) & 0xFFu), xb.y, acc);
-    acc = fmaf((float)((hi >> 16) & 0xFFu), xb.z, acc);
-    acc = fmaf((float)(hi >> 24), xb.w, acc);
-    return acc;
-}
-
-// int8 codes, fp32 activations in natural order.
-__device__ __forceinline__ float word_i8_f32(uint32_t w, const float4& xa, float acc) {
-    acc = fmaf((float)(w & 0xFFu), xa.x, acc);
-    acc = fmaf((float)((w >> 8) & 0xFFu), xa.y, acc);
-    acc = fmaf((float)((w >> 16) & 0xFFu), xa.z, acc);
-    acc = fmaf((float)(w >> 24), xa.w, acc);
-    return acc;
 }
 
 // v from another lane through DPP (CTRL: quad_perm 0xB1 = lane ^ 1, 0x4E =
@@ -191,26 +186,29 @@ __device__ __forceinline__ float xor_add(float v) {
 // Activation staging into LDS.
 //
 // Layout for nc chunks and nb activation vectors:
-//   xs[b][q][c]  (uint4; q < QPC words-of-x per chunk), consecutive chunks
-//                at consecutive 16-byte slots so the lanes of a row segment
-//                read disjoint banks;
-//   cs[b][c]     float2 (1024*sum_1 + 64*sum_16 (or 1024*sum), sum) on the
-//                fp16 path, float sum on the fp32 path.
+//   xs[b][q][c]  (uint4; q < QPC per chunk), consecutive chunks at
+//                consecutive 16-byte slots so the lanes of a row segment
+//                read disjoint banks. Values sit in the order the unpacking
+//                produces the code pairs: per word of 4-bit codes the fp16
+//                pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), per two words of
+//                8-bit codes (x0,x2) (x1,x3) (x4,x6) (x5,x7); fp32 values
+//                (XF = 1) in the same order, one uint4 per four;
+//   cs[b][c]     float: the sum of the chunk's activations.
 // ---------------------------------------------------------------------------
 //
 // XF = 2 (rotated activations, see stage_x_rot) keeps the fp16 layout twice:
 // planes q < QH hold the fp16 rounding hi of each value, planes QH + q the
-// fp16 remainder lo = fp16(v - hi), and cs holds the class sums of hi + lo.
+// fp16 remainder lo = fp16(v - hi), and cs holds the sums of hi + lo.
 template <int BITS, int XF>
 struct Stage {
     static constexpr int CC = 128 / BITS;                               // codes per chunk
     static constexpr int QH = BITS == 4 ? 4 : 2;                        // fp16 uint4 per chunk
     static constexpr int QPC = XF == 1 ? CC / 4 : (XF == 2 ? 2 * QH : QH);  // uint4 per chunk
-    static constexpr int CSZ = XF == 1 ? 4 : 8;                         // const bytes per chunk
+    static constexpr int CSZ = 4;                                       // sum bytes per chunk
     __host__ __device__ static size_t bytes(int nb, int nc) { return (size_t)nb * nc * (QPC * 16 + CSZ); }
     // chunk-major layout for B > 1 vectors (fp16 path, see stage_x_cm)
     __host__ __device__ static size_t bytes_cm(int B, int nc) {
-        return (size_t)nc * ((B * QPC + 1) * 16 + (B + 1) * 8);
+        return (size_t)nc * ((B * QPC + 1) * 16 + (B + 1) * 4);
     }
 };
 
@@ -259,8 +257,8 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
                     s1 += (h2f(h[0]) + h2f(h[4])) + (h2f(h[2]) + h2f(h[6]));
                     s16 += (h2f(h[1]) + h2f(h[5])) + (h2f(h[3]) + h2f(h[7]));
                 }
-                float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
-                cs[b * nc + c] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+                float* cs = (float*)(xs + (size_t)nb * QPC * nc);
+                cs[b * nc + c] = s1 + s16;
             } else {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
@@ -279,8 +277,8 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
 #pragma unroll
                     for (int i = 0; i < 8; ++i) s1 += h2f(h[i]);
                 }
-                float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
-                cs[b * nc + c] = make_float2(1024.f * s1, s1);
+                float* cs = (float*)(xs + (size_t)nb * QPC * nc);
+                cs[b * nc + c] = s1;
             }
         } else {
             float v[CC];
@@ -294,19 +292,19 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
                 for (int w = 0; w < 4; ++w) {
                     const float* u = v + 8 * w;
                     xs[(b * QPC + 2 * w) * nc + c] =
-                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
-                                   __float_as_uint(u[4]), __float_as_uint(u[6]));
+                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[4]),
+                                   __float_as_uint(u[2]), __float_as_uint(u[6]));
                     xs[(b * QPC + 2 * w + 1) * nc + c] =
-                        make_uint4(__float_as_uint(u[1]), __float_as_uint(u[3]),
-                                   __float_as_uint(u[5]), __float_as_uint(u[7]));
+                        make_uint4(__float_as_uint(u[1]), __float_as_uint(u[5]),
+                                   __float_as_uint(u[3]), __float_as_uint(u[7]));
                 }
             } else {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const float* u = v + 4 * w;
                     xs[(b * QPC + w) * nc + c] =
-                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[1]),
-                                   __float_as_uint(u[2]), __float_as_uint(u[3]));
+                        make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
+                                   __float_as_uint(u[1]), __float_as_uint(u[3]));
                 }
             }
             float* cs = (float*)(xs + (size_t)nb * QPC * nc);
@@ -319,7 +317,7 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
 // stage_x, rearranged):
 //   xs[c][b][q]  uint4, slot c at a stride of SC = B*QPC + 1 uint4 (the pad
 //                puts the 8 lanes of one LDS cycle in distinct banks);
-//   cs[c][b]     float2, slot c at a stride of B + 1 float2 (same reason).
+//   cs[c][b]     float, slot c at a stride of B + 1 floats.
 // Every (vector, quarter) of a chunk then sits at a compile-time offset from
 // the chunk's base, so the reads in group_rows take immediate offsets
 // instead of one address add each. Vectors b >= nb are not staged; their
@@ -331,7 +329,7 @@ __device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int n
     constexpr int QPC = St::QPC;
     constexpr int SC = B * QPC + 1;
     uint4* xs = lds;
-    float2* cs = (float2*)(xs + (size_t)nc * SC);
+    float* cs = (float*)(xs + (size_t)nc * SC);
     for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
         const int b = item / nc, cc = item - b * nc;
         const int c = xslot<CPL>(cc, nc);
@@ -351,7 +349,7 @@ __device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int n
                 s1 += (h2f(h[0]) + h2f(h[4])) + (h2f(h[2]) + h2f(h[6]));
                 s16 += (h2f(h[1]) + h2f(h[5])) + (h2f(h[3]) + h2f(h[7]));
             }
-            cs[c * (B + 1) + b] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+            cs[c * (B + 1) + b] = s1 + s16;
         } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -366,7 +364,7 @@ __device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int n
 #pragma unroll
                 for (int i = 0; i < 8; ++i) s1 += h2f(h[i]);
             }
-            cs[c * (B + 1) + b] = make_float2(1024.f * s1, s1);
+            cs[c * (B + 1) + b] = s1;
         }
     }
 }
@@ -465,7 +463,7 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
     constexpr int CPB = 32 / CC;   // chunks per block
     const int nblk = nc / CPB;
     uint4* xs = lds;
-    float2* cs = (float2*)(xs + (size_t)nb * QPC * nc);
+    float* cs = (float*)(xs + (size_t)nb * QPC * nc);
     float* mulv = rs;                        // [kRotMaxB]
     float* unscale = rs + kRotMaxB;          // [kRotMaxB]
     float* red = rs + 2 * kRotMaxB;          // [2][kRotMaxB][kRotWaves]
@@ -619,177 +617,149 @@ __device__ __forceinline__ void stage_x_rot(const uint16_t* x, int kind, int K, 
         if constexpr (BITS == 4) {
             s1 += pair_swap(s1);   // the chunk's 32 inputs span both lanes
             s16 += pair_swap(s16);
-            if (hh == 0) cs[b * nc + xslot<CPL>(bl, nc)] = make_float2(1024.f * s1 + 64.f * s16, s1 + s16);
+            if (hh == 0) cs[b * nc + xslot<CPL>(bl, nc)] = s1 + s16;
         } else {
-            cs[b * nc + xslot<CPL>(bl * 2 + hh, nc)] = make_float2(1024.f * s1, s1);
+            cs[b * nc + xslot<CPL>(bl * 2 + hh, nc)] = s1;
         }
+    }
+}
+
+// Centred code pairs of one word: the four half2 that the dot products take.
+// 4-bit: (q0, q4), 16 (q1, q5), (q2, q6), 16 (q3, q7), each minus the
+// centre; 8-bit (two words w0, w1): (q0, q2), (q1, q3) of each word.
+template <int BITS>
+__device__ __forceinline__ void centred_pairs(uint32_t w0, uint32_t w1, uint32_t magic, uint32_t n1,
+                                              uint32_t n16, uint32_t (&p)[4]) {
+    if constexpr (BITS == 4) {
+        (void)w1;
+        const uint32_t w8 = w0 >> 8;
+        p[0] = pk_addh((w0 & 0x000F000Fu) | magic, n1);    // q0 - c, q4 - c
+        p[1] = pk_addh((w0 & 0x00F000F0u) | magic, n16);   // 16 (q1 - c), 16 (q5 - c)
+        p[2] = pk_addh((w8 & 0x000F000Fu) | magic, n1);    // q2 - c, q6 - c
+        p[3] = pk_addh((w8 & 0x00F000F0u) | magic, n16);   // 16 (q3 - c), 16 (q7 - c)
+    } else {
+        p[0] = pk_addh((w0 & 0x00FF00FFu) | magic, n1);            // q0 - c, q2 - c
+        p[1] = pk_addh(((w0 >> 8) & 0x00FF00FFu) | magic, n1);     // q1 - c, q3 - c
+        p[2] = pk_addh((w1 & 0x00FF00FFu) | magic, n1);
+        p[3] = pk_addh(((w1 >> 8) & 0x00FF00FFu) | magic, n1);
     }
 }
 
 // Partial dot products of NCH consecutive 16-byte code chunks (one lane's
 // share of a group) of each of R rows with every activation vector b < B,
-// followed by one affine epilogue into y[r][b]:
-//   y[r][b] += s_r * (sum_k q_k x_k) + bias_r * (sum_k x_k).
-// The chunks' activations are read from LDS once and shared by the R rows;
-// slot[i] is the staged slot of chunk i.
-template <int BITS, int XF, int B, int R, int NCH, bool CM = false>
+// followed by one epilogue into y[r][b]:
+//   y[r][b] += sc_r * (sum_k (q_k - c_r) x_k) + bi_r * (sum_k x_k),
+// with the centre c_r given by the subtrahend pairs n1_r (class 1) and
+// n16_r (class 16; 8-bit codes use n1_r only). The second term is left out
+// when XSUM is false. The chunks' activations are read from LDS once and
+// shared by the R rows; slot[i] is the staged slot of chunk i.
+template <int BITS, int XF, int B, int R, int NCH, bool CM = false, bool XSUM = true>
 __device__ __forceinline__ void group_rows(const uint4 (&cw)[NCH][R], const float (&sc)[R],
-                                           const float (&bi)[R], const uint4* lds, int nb_staged,
-                                           int nc, const int (&slot)[NCH], uint32_t magic,
-                                           float (&y)[R][B]) {
+                                           const float (&bi)[R], const uint32_t (&n1)[R],
+                                           const uint32_t (&n16)[R], const uint4* lds,
+                                           int nb_staged, int nc, const int (&slot)[NCH],
+                                           uint32_t magic, float (&y)[R][B]) {
     using St = Stage<BITS, XF>;
     constexpr int QPC = St::QPC;
+    constexpr int QH = St::QH;
     constexpr int NPL = XF == 2 ? 2 : 1;   // fp16 planes: value, or hi and lo
     const uint4* xs = lds;
     static_assert(!CM || XF == 0, "chunk-major staging is for fp16 activations");
     constexpr int SC = B * QPC + 1;   // chunk-major slot stride (uint4)
-    if constexpr (XF == 0 || XF == 2) {
-        const float2* cs = CM ? (const float2*)(xs + (size_t)nc * SC)
-                              : (const float2*)(xs + (size_t)nb_staged * QPC * nc);
-        float a1[R][B], a16[R][B];
+    const float* cs = CM ? (const float*)(xs + (size_t)nc * SC)
+                         : (const float*)(xs + (size_t)nb_staged * QPC * nc);
+    float a1[R][B], a16[R][B];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) a1[r][b] = a16[r][b] = 0.f;
+        for (int b = 0; b < B; ++b) a1[r][b] = a16[r][b] = 0.f;
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-            const int c = slot[ch];
-            if constexpr (BITS == 4) {
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int c = slot[ch];
+        // a 4-bit chunk is 4 steps of one word, an 8-bit chunk 2 steps of two
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint4 xq[NPL][B];   // plane 1 (if any): the fp16 remainders
+        for (int q = 0; q < QH; ++q) {
+            if constexpr (XF == 0 || XF == 2) {
+                uint4 xq[NPL][B];   // plane 1 (if any): the fp16 remainders
+#pragma unroll
+                for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+                        xq[pl][b] = CM ? xs[c * SC + b * QPC + q] : xs[(b * QPC + pl * QH + q) * nc + c];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint4& w4 = cw[ch][r];
+                    uint32_t p[4];
+                    if constexpr (BITS == 4)
+                        centred_pairs<4>(q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w, 0u,
+                                         magic, n1[r], n16[r], p);
+                    else
+                        centred_pairs<8>(q == 0 ? w4.x : w4.z, q == 0 ? w4.y : w4.w, magic, n1[r],
+                                         n1[r], p);
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-                        for (int b = 0; b < B; ++b)
-                            xq[pl][b] = CM ? xs[c * SC + b * QPC + q] : xs[(b * QPC + pl * 4 + q) * nc + c];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint4& w4 = cw[ch][r];
-                        const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
-                        const uint32_t p04 = (w & 0x000F000Fu) | magic;   // 1024+q0, 1024+q4
-                        const uint32_t p15 = (w & 0x00F000F0u) | magic;   // 1024+16q1, 1024+16q5
-                        const uint32_t w8 = w >> 8;
-                        const uint32_t p26 = (w8 & 0x000F000Fu) | magic;  // 1024+q2, 1024+q6
-                        const uint32_t p37 = (w8 & 0x00F000F0u) | magic;  // 1024+16q3, 1024+16q7
-#pragma unroll
-                        for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-                            for (int b = 0; b < B; ++b) {
-                                a1[r][b] = dot2(p04, xq[pl][b].x, a1[r][b]);
-                                a16[r][b] = dot2(p15, xq[pl][b].y, a16[r][b]);
-                                a1[r][b] = dot2(p26, xq[pl][b].z, a1[r][b]);
-                                a16[r][b] = dot2(p37, xq[pl][b].w, a16[r][b]);
-                            }
-                    }
+                        for (int b = 0; b < B; ++b) {
+                            a1[r][b] = dot2(p[0], xq[pl][b].x, a1[r][b]);
+                            a16[r][b] = dot2(p[1], xq[pl][b].y, a16[r][b]);
+                            a1[r][b] = dot2(p[2], xq[pl][b].z, a1[r][b]);
+                            a16[r][b] = dot2(p[3], xq[pl][b].w, a16[r][b]);
+                        }
                 }
             } else {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    uint4 xq[NPL][B];
-#pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-                        for (int b = 0; b < B; ++b)
-                            xq[pl][b] = CM ? xs[c * SC + b * QPC + q] : xs[(b * QPC + pl * 2 + q) * nc + c];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint4& w4 = cw[ch][r];
-                        const uint32_t w0 = q == 0 ? w4.x : w4.z;
-                        const uint32_t w1 = q == 0 ? w4.y : w4.w;
-                        const uint32_t p02 = (w0 & 0x00FF00FFu) | magic;          // 1024+q0, 1024+q2
-                        const uint32_t p13 = ((w0 >> 8) & 0x00FF00FFu) | magic;   // 1024+q1, 1024+q3
-                        const uint32_t r02 = (w1 & 0x00FF00FFu) | magic;
-                        const uint32_t r13 = ((w1 >> 8) & 0x00FF00FFu) | magic;
-#pragma unroll
-                        for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-                            for (int b = 0; b < B; ++b) {
-                                a1[r][b] = dot2(p02, xq[pl][b].x, a1[r][b]);
-                                a16[r][b] = dot2(p13, xq[pl][b].y, a16[r][b]);
-                                a1[r][b] = dot2(r02, xq[pl][b].z, a1[r][b]);
-                                a16[r][b] = dot2(r13, xq[pl][b].w, a16[r][b]);
-                            }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float kx = 0.f, ky = 0.f;
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const float2 k = CM ? cs[slot[ch] * (B + 1) + b] : cs[b * nc + slot[ch]];
-                kx += k.x;
-                ky += k.y;
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float p =
-                    (BITS == 4 ? fmaf(a16[r][b], 0.0625f, a1[r][b]) : a1[r][b] + a16[r][b]) - kx;
-                y[r][b] = fmaf(sc[r], p, y[r][b]);
-                y[r][b] = fmaf(bi[r], ky, y[r][b]);
-            }
-        }
-    } else {
-        const float* cs = (const float*)(xs + (size_t)nb_staged * QPC * nc);
-        float acc[R][B];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-            const int c = slot[ch];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
+                // fp32 activations: 4-bit word q as (x0,x4,x2,x6), (x1,x5,x3,x7);
+                // 8-bit words 2q, 2q + 1 as (x0,x2,x1,x3) each
+                uint4 xa[B], xb[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    if constexpr (BITS == 4) {
-                        const uint4 xa = xs[(b * QPC + 2 * q) * nc + c];
-                        const uint4 xb = xs[(b * QPC + 2 * q + 1) * nc + c];
+                    xa[b] = xs[(b * QPC + 2 * q) * nc + c];
+                    xb[b] = xs[(b * QPC + 2 * q + 1) * nc + c];
+                }
 #pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const uint4& w4 = cw[ch][r];
-                            const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
-                            acc[r][b] = word_i4_f32(w, *(const float4*)&xa, *(const float4*)&xb, acc[r][b]);
-                        }
-                    } else {
-                        const uint4 xa = xs[(b * QPC + q) * nc + c];
+                for (int r = 0; r < R; ++r) {
+                    const uint4& w4 = cw[ch][r];
+                    uint32_t p[4];
+                    if constexpr (BITS == 4)
+                        centred_pairs<4>(q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w, 0u,
+                                         magic, n1[r], n16[r], p);
+                    else
+                        centred_pairs<8>(q == 0 ? w4.x : w4.z, q == 0 ? w4.y : w4.w, magic, n1[r],
+                                         n1[r], p);
 #pragma unroll
-                        for (int r = 0; r < R; ++r) {
-                            const uint4& w4 = cw[ch][r];
-                            const uint32_t w = q == 0 ? w4.x : q == 1 ? w4.y : q == 2 ? w4.z : w4.w;
-                            acc[r][b] = word_i8_f32(w, *(const float4*)&xa, acc[r][b]);
+                    for (int b = 0; b < B; ++b) {
+                        const float4 fa = *(const float4*)&xa[b];
+                        const float4 fb = *(const float4*)&xb[b];
+                        if constexpr (BITS == 4) {
+                            a1[r][b] = fma_pair(p[0], fa.x, fa.y, a1[r][b]);
+                            a1[r][b] = fma_pair(p[2], fa.z, fa.w, a1[r][b]);
+                            a16[r][b] = fma_pair(p[1], fb.x, fb.y, a16[r][b]);
+                            a16[r][b] = fma_pair(p[3], fb.z, fb.w, a16[r][b]);
+                        } else {
+                            a1[r][b] = fma_pair(p[0], fa.x, fa.y, a1[r][b]);
+                            a16[r][b] = fma_pair(p[1], fa.z, fa.w, a16[r][b]);
+                            a1[r][b] = fma_pair(p[2], fb.x, fb.y, a1[r][b]);
+                            a16[r][b] = fma_pair(p[3], fb.z, fb.w, a16[r][b]);
                         }
                     }
                 }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float xsum = 0.f;
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) xsum += cs[b * nc + slot[ch]];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                y[r][b] = fmaf(sc[r], acc[r][b], y[r][b]);
-                y[r][b] = fmaf(bi[r], xsum, y[r][b]);
             }
         }
     }
-}
-
-// One chunk per row (the gathered MoE kernels).
-template <int BITS, int XF, int B, int R>
-__device__ __forceinline__ void chunk_rows(const uint4 (&cw)[R], const float (&sc)[R],
-                                           const float (&bi)[R], const uint4* lds, int nb_staged,
-                                           int nc, int c, uint32_t magic, float (&y)[R][B]) {
-    uint4 cw1[1][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) cw1[0][r] = cw[r];
-    const int slot[1] = {c};
-    group_rows<BITS, XF, B, R, 1>(cw1, sc, bi, lds, nb_staged, nc, slot, magic, y);
+    for (int b = 0; b < B; ++b) {
+        float xsum = 0.f;
+        if constexpr (XSUM) {
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch)
+                xsum += CM ? cs[slot[ch] * (B + 1) + b] : cs[b * nc + slot[ch]];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float p = BITS == 4 ? fmaf(a16[r][b], 0.0625f, a1[r][b]) : a1[r][b] + a16[r][b];
+            y[r][b] = fmaf(sc[r], p, y[r][b]);
+            if constexpr (XSUM) y[r][b] = fmaf(bi[r], xsum, y[r][b]);
+        }
+    }
 }
 
 }  // namespace qd

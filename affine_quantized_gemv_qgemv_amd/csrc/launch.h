@@ -22,8 +22,6 @@ const DeviceInfo& device_info();
 // Resident workgroups per CU for a kernel at this block size and LDS use.
 int occupancy(const void* func, int threads, size_t lds_bytes);
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
-
 // Rotation prologue of the Mirai formats: x -> H D (RMSNorm(x) * gamma) per
 // block of 32 inputs before the contraction.
 struct GemvRot {
@@ -80,7 +78,7 @@ size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap);
 hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                               uint16_t* kc, uint16_t* vc, int Hq, int Hkv, int D, int cap,
                               int window, int pos, float scale, float* out, void* ws,
-                              hipStream_t st);
+                              size_t ws_bytes, hipStream_t st);
 
 // x: fp16 or bf16 bits (xkind X_F16 / X_BF16), [M][K].
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,

@@ -170,16 +170,17 @@ __global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
                 const int cu = ((s0 + u) * LPR + sl) * CPL;
                 const bool live = ok && cu < C16;
                 const int c = min(cu, C16 - CPL);
-                float sc[2], bi[2];
+                float sc[2], bi[2];   // scale and centred bias b + 8 s
+                const uint32_t n1[2] = {kNeg1032, kNeg1032}, n16[2] = {kNeg1152, kNeg1152};
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     sc[r] = live ? h2f(sr[u][r]) : 0.f;
-                    bi[r] = live ? h2f(br[u][r]) : 0.f;
+                    bi[r] = live ? fmaf(8.f, sc[r], h2f(br[u][r])) : 0.f;
                 }
                 int slot[CPL];
 #pragma unroll
                 for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, C16);
-                group_rows<4, XF, 1, 2, CPL>(cw[u], sc, bi, lds, 1, C16, slot, magic, y);
+                group_rows<4, XF, 1, 2, CPL>(cw[u], sc, bi, n1, n16, lds, 1, C16, slot, magic, y);
             }
         }
         const float zg = seg_sum<LPR>(y[0][0]);
@@ -263,12 +264,12 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
         constexpr int QPC = St::QPC;
         const int sl = xslot<CPL>(c, C);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < 4; ++w) {   // the pair order of the 4-bit unpack
             const float* u = v + 8 * w;
-            lds[(2 * w) * C + sl] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[2]),
-                                               __float_as_uint(u[4]), __float_as_uint(u[6]));
-            lds[(2 * w + 1) * C + sl] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[3]),
-                                                   __float_as_uint(u[5]), __float_as_uint(u[7]));
+            lds[(2 * w) * C + sl] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[4]),
+                                               __float_as_uint(u[2]), __float_as_uint(u[6]));
+            lds[(2 * w + 1) * C + sl] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[5]),
+                                                   __float_as_uint(u[3]), __float_as_uint(u[7]));
         }
         ((float*)(lds + (size_t)QPC * C))[sl] = sum;
     }
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
     const int ntiles = (a.H + ROWS - 1) / ROWS;
     const int t0 = (int)((int64_t)ntiles * gw / W);
     const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
-    const uint32_t magic = 0;  // unused on the fp32 path
+    const uint32_t magic = in_vgpr(kMagic16);
 
     for (int tile = t0; tile < t1; ++tile) {
         float y[R][1];
@@ -314,17 +315,20 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
                 const int cu = ((s0 + u) * LPR + sl) * CPL;
                 const int c = min(cu, C - CPL);
                 const bool live = cu < C && info[c].qstride > 0;
-                float sc[R], bi[R];
+                float sc[R], bi[R];   // scale and centred bias b + 8 s
+                uint32_t n1[R], n16[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const bool ok = live && (tile * ROWS + r * RPI + seg < a.H);
                     sc[r] = ok ? h2f(sr[u][r]) : 0.f;
-                    bi[r] = ok ? h2f(br[u][r]) : 0.f;
+                    bi[r] = ok ? fmaf(8.f, sc[r], h2f(br[u][r])) : 0.f;
+                    n1[r] = kNeg1032;
+                    n16[r] = kNeg1152;
                 }
                 int slot[CPL];
 #pragma unroll
                 for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, C);
-                group_rows<4, 1, 1, R, CPL>(cw[u], sc, bi, lds, 1, C, slot, magic, y);
+                group_rows<4, 1, 1, R, CPL>(cw[u], sc, bi, n1, n16, lds, 1, C, slot, magic, y);
             }
         }
 #pragma unroll
@@ -343,12 +347,6 @@ size_t moe_decode_workspace_bytes(const MoeArgs& m, int k) {
     return ((size_t)k * m.I + m.Is) * sizeof(float);
 }
 
-#ifdef QD_TUNING
-// Tuning builds only: force the decode launch shapes (all zero = default).
-int qd_tune_moe[3] = {0, 0, 0};
-extern "C" int* qd_tune_moe_ptr() { return qd_tune_moe; }
-#endif
-
 namespace {
 
 // Launch shapes of the two decode kernels (workgroup waves, rows per tile).
@@ -358,9 +356,6 @@ struct MoeCfg {
 
 MoeCfg moe_cfg() {
     MoeCfg c{4, 0, 1};   // dn_nw 0: sized to the row count
-#ifdef QD_TUNING
-    if (qd_tune_moe[0]) c = MoeCfg{qd_tune_moe[0], qd_tune_moe[1], qd_tune_moe[2]};
-#endif
     return c;
 }
 
@@ -407,10 +402,6 @@ hipError_t launch_down_r(const MoeBArgs& a, int nw, hipStream_t st) {
 
 hipError_t launch_down(const MoeBArgs& a, hipStream_t st) {
     const MoeCfg c = moe_cfg();
-#ifdef QD_TUNING
-    if (c.dn_r == 4) return launch_down_r<4>(a, c.dn_nw, st);
-    if (c.dn_r == 2) return launch_down_r<2>(a, c.dn_nw, st);
-#endif
     return launch_down_r<1>(a, c.dn_nw, st);
 }
 

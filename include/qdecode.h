@@ -258,7 +258,10 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
  *   the occupied slots j < min(pos + 1, window) (or pos + 1): exactly the
  *   positions inside the window.
  *   D in {64, 128, 256}; Hq / Hkv in {1, 2, 4, 8}; scale finite.
- *   workspace: device scratch of at least qattn_decode_workspace_bytes().
+ *   workspace: device scratch of at least qattn_decode_workspace_bytes(Hq,
+ *   Hkv, D, cap); that size covers every pos the cache can hold. A call
+ *   whose split partials would not fit ws_bytes fails with
+ *   QD_ERR_WORKSPACE before any launch (nothing is written).
  * The call first stores k_new / v_new at the token's slot, so the caches
  * must not be read or written by other work until the stream reaches it.
  */

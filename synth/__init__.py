@@ -70,12 +70,26 @@ class AffineWeights:
         return self.wq.nbytes + self.scales.nbytes + self.biases.nbytes
 
 
+def _pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Pack integer codes [N][K] LSB-first into uint32 words (code i of a word at
+    bits [bits*i, bits*(i+1)))."""
+    per_word = 32 // bits
+    N, K = q.shape
+    qq = q.astype(np.uint64).reshape(N, K // per_word, per_word)
+    shifts = (np.arange(per_word, dtype=np.uint64) * np.uint64(bits))
+    return (qq << shifts).sum(axis=2).astype(np.uint32)
+
+
 def affine_weights(bits: int, N: int, K: int, cfg: int, set_id: int, tensor_base: int = 0,
-                   codes: str = "uniform", const_code: int = 0) -> AffineWeights:
+                   codes: str = "uniform", const_code: int = 0, code_set=None,
+                   bias_code: float | None = None) -> AffineWeights:
     """Draw one packed weight matrix.
 
-    codes: "uniform" (random words), "zero" (all codes 0) or "const" (every
-    code equal to ``const_code``).
+    codes: "uniform" (random words), "zero" (all codes 0), "const" (every
+    code equal to ``const_code``) or "set" (each code drawn uniformly from
+    ``code_set``). bias_code: the code c in b = fp16(-c*s + N(0, 1e-3));
+    default the middle code (8 or 128), so that a weight w = s*q + b sits near
+    zero when q = c.
     """
     if bits not in (4, 8):
         raise ValueError("bits must be 4 or 8")
@@ -96,13 +110,19 @@ def affine_weights(bits: int, N: int, K: int, cfg: int, set_id: int, tensor_base
         for i in range(per_word):
             word |= c << (bits * i)
         wq = np.full((N, K // per_word), word, dtype=np.uint32)
+    elif codes == "set":
+        vals = np.asarray(list(code_set), dtype=np.int64)
+        if vals.size == 0 or vals.min() < 0 or vals.max() >= (1 << bits):
+            raise ValueError("code_set out of range")
+        q = vals[rng(cfg, set_id, tensor_base + T_CODES).integers(0, vals.size, size=(N, K))]
+        wq = _pack_codes(q, bits)
     else:
         raise ValueError(codes)
     su = rng(cfg, set_id, tensor_base + T_SCALE).uniform(0.002, 0.02, size=(N, G))
     if bits == 8:
         su = su * (15.0 / 255.0)
     s16 = su.astype(np.float16)
-    mid = 8.0 if bits == 4 else 128.0
+    mid = (8.0 if bits == 4 else 128.0) if bias_code is None else float(bias_code)
     noise = rng(cfg, set_id, tensor_base + T_BIAS).normal(0.0, 1e-3, size=(N, G))
     b16 = (-mid * s16.astype(np.float64) + noise).astype(np.float16)
     return AffineWeights(bits, N, K, wq, s16.view(np.uint16), b16.view(np.uint16))
@@ -140,11 +160,13 @@ def _const_words(N: int, words: int, bits: int, value: int) -> np.ndarray:
 
 def mirai_weights(fmt: str, N: int, K: int, cfg: int, set_id: int, tensor_base: int = 0,
                   codes: str = "uniform", const_code: int = 0,
-                  zeros: str = "uniform", const_zero: int = 0) -> MiraiWeights:
+                  zeros: str = "uniform", const_zero: int = 0,
+                  code_set=None) -> MiraiWeights:
     """Draw one packed Mirai-M / Mirai-L matrix.
 
-    codes: "uniform" or "const" (every code ``const_code``: 0..15 for M,
-    -128..127 for L); zeros (M only): "uniform" or "const" (``const_zero``).
+    codes: "uniform", "const" (every code ``const_code``: 0..15 for M,
+    -128..127 for L) or "set" (each code drawn uniformly from ``code_set``,
+    same ranges); zeros (M only): "uniform" or "const" (``const_zero``).
     """
     if fmt not in ("M", "L"):
         raise ValueError("fmt must be 'M' or 'L'")
@@ -160,6 +182,13 @@ def mirai_weights(fmt: str, N: int, K: int, cfg: int, set_id: int, tensor_base: 
         if not lo <= const_code <= hi:
             raise ValueError("const_code out of range")
         wq = _const_words(N, words, bits, int(const_code))
+    elif codes == "set":
+        lo, hi = (0, 15) if fmt == "M" else (-128, 127)
+        vals = np.asarray(list(code_set), dtype=np.int64)
+        if vals.size == 0 or vals.min() < lo or vals.max() > hi:
+            raise ValueError("code_set out of range")
+        q = vals[rng(cfg, set_id, tensor_base + T_CODES).integers(0, vals.size, size=(N, K))]
+        wq = _pack_codes(q & ((1 << bits) - 1), bits)
     else:
         raise ValueError(codes)
     su = rng(cfg, set_id, tensor_base + T_SCALE).uniform(0.002, 0.02, size=(N, G))
@@ -255,11 +284,13 @@ def moe_weights(E: int, H: int, I: int, Is: int, cfg: int, layer: int,
     """Draw one MoE layer. Tensor ids are spaced by 8 per matrix.
 
     identical_experts: every routed expert gets expert 0's tensors.
-    flat_router: router codes all zero and biases all equal, so all logits tie.
+    flat_router: router codes all zero, and scales and biases all equal, so every
+    router row holds the same stored values and all logits tie exactly.
     """
     router = affine_weights(8, E, H, cfg, layer, 0)
     if flat_router:
-        router = AffineWeights(8, E, H, np.zeros_like(router.wq), router.scales,
+        router = AffineWeights(8, E, H, np.zeros_like(router.wq),
+                               np.full_like(router.scales, router.scales.flat[0]),
                                np.full_like(router.biases, router.biases.flat[0]))
     gus, dns = [], []
     for e in range(E):

@@ -1,6 +1,9 @@
 """Test helpers: move synthetic inputs to the device and compare with the oracle."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -41,14 +44,28 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def _log_margin(what: str, worst: float) -> None:
+    """Append the worst err/tol of one comparison to the JSON-lines file named by
+    QD_MARGIN_LOG (if set), keyed by the running test, so margins per test
+    family can be tabulated after a run."""
+    path = os.environ.get("QD_MARGIN_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(path, "a") as f:
+        f.write(json.dumps({"test": test, "what": what, "worst": worst}) + "\n")
+
+
 def assert_within(y_gpu, y_ref, a_ref, what=""):
     """|y_gpu - y_ref| <= 1e-4 * A + 1e-6 element by element."""
     y = np.asarray(y_gpu, dtype=np.float64)
     err = np.abs(y - y_ref)
     tol = 1e-4 * a_ref + 1e-6
     bad = err > tol
+    worst = float((err / tol).max()) if err.size else 0.0
+    _log_margin(what, worst)
     if bad.any():
         i = np.unravel_index(np.argmax(err / tol), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at {i}: "
                              f"gpu {y[i]!r} ref {y_ref[i]!r} err {err[i]:.3e} tol {tol[i]:.3e}")
-    return float((err / tol).max()) if err.size else 0.0
+    return worst

@@ -250,3 +250,35 @@ def test_attention_argument_errors():
     assert at(wsb=ws - 1) == E.QD_ERR_WORKSPACE
     # circular storage accepts any position
     assert qd.qattn_workspace_bytes(16, 8, 128, 1024) <= ws
+
+
+def _attn_splits(n, Hkv, cus=256, maxsplit=256):
+    """The split rule of the decode-attention launch, written out: about two
+    workgroups per CU over the key/value heads, at most 256 splits, splits of
+    a multiple of 32 rows."""
+    want = max(1, min((2 * cus + Hkv - 1) // Hkv, maxsplit, (n + 31) // 32))
+    chunk = -(-n // want)
+    chunk = (chunk + 31) // 32 * 32
+    return -(-n // chunk)
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 4, 8, 16])
+def test_attention_workspace_covers_every_position(Hkv):
+    # the split count is not monotonic in the occupancy n (the chunk is
+    # rounded up to 32 rows), so the workspace for a cache of `cap` slots
+    # must cover the largest split count of any n <= cap
+    Hq, D = 2 * Hkv, 128
+    per_split = Hq * (D + 2) * 4
+    caps = sorted(set(list(range(1, 4200, 7)) + [1025, 2049, 4097, 8193, 16385, 20000]))
+    worst = 0
+    for cap in caps:
+        ws = qd.qattn_workspace_bytes(Hq, Hkv, D, cap)
+        need = max(_attn_splits(n, Hkv) for n in range(max(1, cap - 1200), cap + 1))
+        worst = max(worst, need)
+        assert ws >= need * per_split, (cap, ws, need)
+        # a larger cache never needs less
+        assert ws >= qd.qattn_workspace_bytes(Hq, Hkv, D, max(1, cap - 1))
+    # the case that overran the old cap-based size (Hkv 8, cap 2049, n 2048)
+    if Hkv == 8:
+        assert _attn_splits(2048, 8) > _attn_splits(2049, 8)
+        assert qd.qattn_workspace_bytes(16, 8, 128, 2049) >= _attn_splits(2048, 8) * 16 * 130 * 4

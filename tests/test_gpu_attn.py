@@ -131,3 +131,24 @@ def test_one_workspace_across_calls_with_different_split_counts():
         ref, a = oracle.attn_decode(f64(t["q"]), f64(t["k_new"]), f64(t["v_new"]), f64(t["k_cache"]),
                                     f64(t["v_cache"]), 0, pos, D ** -0.5)
         assert_within(y.cpu().numpy(), ref, a, f"pos {pos}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,cap,pos", [(16, 8, 128, 2049, 2047), (32, 16, 64, 1025, 1023),
+                                             (8, 4, 128, 4097, 4095), (16, 8, 128, 2049, 2048)])
+def test_workspace_guard_band_at_ragged_split_counts(Hq, Hkv, D, cap, pos):
+    # occupancies just below a multiple of the split size take more splits
+    # than the full cache: the workspace (sized for the cache) must still
+    # hold them, and nothing past it may be written
+    print(f"attn guard Hq={Hq} Hkv={Hkv} D={D} cap={cap} pos={pos}", flush=True)
+    t = synth.attn_inputs(Hq, Hkv, D, cap, cfg=604, set_id=cap + pos)
+    need = qd.qattn_workspace_bytes(Hq, Hkv, D, cap)
+    guard = 1 << 16
+    buf = torch.full((need + guard,), 0x7F, dtype=torch.uint8, device="cuda")
+    dev = {k: dev_half(v) for k, v in t.items()}
+    y = qd.qattn_decode(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"], pos, 0,
+                        workspace=buf[:need])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0x7F).all()), "write past the workspace"
+    ref, a = oracle.attn_decode(f64(t["q"]), f64(t["k_new"]), f64(t["v_new"]), f64(t["k_cache"]),
+                                f64(t["v_cache"]), 0, pos, D ** -0.5)
+    assert_within(y.cpu().numpy(), ref, a, f"guard cap={cap} pos={pos}")

@@ -129,8 +129,8 @@ def test_ragged_last_tile_of_two_row_tiles(N):
 @pytest.mark.parametrize("bits", [4, 8])
 def test_largest_k(bits):
     # K = 2^22, the largest the ABI accepts: rows are addressed with 32-bit
-    # offsets from a tile's first row, and x is split over many K ranges
-    # whose partial rows meet through atomics
+    # offsets from a tile's first row, and x is streamed through LDS in
+    # about a hundred K slices
     K, N = 1 << 22, 3
     w = synth.affine_weights(bits, N, K, cfg=209, set_id=bits)
     for batch in (1, 2):
@@ -181,6 +181,64 @@ def test_constant_and_zero_codes(bits):
         y = run_gemv(bits, w, xb).cpu().numpy()
         yr, a = ref_gemv(w, xb)
         assert_within(y, yr, a, f"{kind} {c}")
+
+
+# Weights at and near zero (TurboFieldfare article, section "성능과 제약":
+# w = s*q + b; with b close to -c*s a code q = c gives a weight close to
+# zero, where real weights cluster). The bar is the same relative bar, so
+# the kernel's rounding must follow |w x|, not s*q or b separately.
+NEAR_ZERO = {
+    4: [("all 8, b ~ -8s", "const", 8, None, 8), ("codes 7..9, b ~ -8s", "set", 0, (7, 8, 9), 8),
+        ("all 0, b ~ 0", "const", 0, None, 0), ("all 15, b ~ -15s", "const", 15, None, 15),
+        ("all 3, b ~ -3s", "const", 3, None, 3), ("all 12, b ~ -12s", "const", 12, None, 12)],
+    8: [("all 128, b ~ -128s", "const", 128, None, 128),
+        ("codes 127..129, b ~ -128s", "set", 0, (127, 128, 129), 128),
+        ("all 0, b ~ 0", "const", 0, None, 0), ("all 255, b ~ -255s", "const", 255, None, 255),
+        ("all 40, b ~ -40s", "const", 40, None, 40)],
+}
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_near_zero_weights(bits, xdt):
+    N = 300
+    for name, kind, c, cset, bc in NEAR_ZERO[bits]:
+        for K in (64, 128, 704, 4096):
+            seed = K + c + bc
+            w = synth.affine_weights(bits, N, K, cfg=230, set_id=seed, codes=kind, const_code=c,
+                                     code_set=cset, bias_code=bc)
+            for batch in (1, 8):
+                xb = draw_x(batch, K, xdt, seed + batch)
+                print(f"near-zero bits={bits} {name} K={K} batch={batch} {xdt}", flush=True)
+                y = run_gemv(bits, w, xb, xdt).cpu().numpy()
+                yr, a = ref_gemv(w, xb, xdt)
+                assert_within(y, yr, a, f"near-zero bits={bits} {name} K={K} batch={batch} {xdt}")
+
+
+# Shapes whose activations are streamed through LDS in K slices (more than
+# half the CU's LDS): the partial rows are summed in a fixed order, so two
+# runs must agree bit for bit, and nothing outside y may be written.
+SLICED = [(28672, 1000, 2), (28672, 1000, 4), (28672, 1000, 8), (8192, 3000, 8), (1 << 22, 3, 1),
+          (1 << 22, 5, 2), (65536, 700, 1)]
+
+
+@pytest.mark.parametrize("K,N,batch", SLICED)
+def test_sliced_k_is_deterministic_and_in_bounds(K, N, batch):
+    print(f"sliced K={K} N={N} batch={batch}", flush=True)
+    w = synth.affine_weights(4, N, K, cfg=231, set_id=K + batch)
+    xb = synth.x_f16(batch, K, cfg=231, set_id=batch)
+    guard = 4096
+    buf = torch.full((guard + batch * N + guard,), float("nan"), device="cuda")
+    out = buf[guard:guard + batch * N].view(batch, N)
+    y1 = run_gemv(4, w, xb, out=out).clone()
+    y2 = run_gemv(4, w, xb).clone()
+    y3 = run_gemv(4, w, xb).clone()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + batch * N:]).all()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    rows = np.unique(np.concatenate([np.random.default_rng(K + N).choice(N, min(N, 64), replace=False),
+                                     [0, N - 1]]))
+    yr, a = ref_gemv(w, xb, rows=rows)
+    assert_within(y1.cpu().numpy()[:, rows], yr, a, f"sliced K={K} N={N} batch={batch}")
 
 
 def test_deterministic_and_no_out_of_bounds_writes():

@@ -91,25 +91,40 @@ def test_zero_activation_gives_zero(fmt):
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_mirai_m_extreme_codes_and_zero_points(xdt):
+    # code == zero point makes every weight exactly zero (w = s (q - z)), so
+    # the bar reduces to |y| <= 1e-6
     K = 1088   # 17 groups: the second zero-point word has 7 padding nibbles
-    for code, zero in ((15, 0), (0, 15), (15, 15), (0, 0), (7, 8)):
+    for code, zero in ((15, 0), (0, 15), (15, 15), (0, 0), (7, 8), (8, 8), (3, 3)):
         w = synth.mirai_weights("M", 50, K, cfg=224, set_id=code * 16 + zero, codes="const",
                                 const_code=code, zeros="const", const_zero=zero)
-        xb = draw_x(2, K, xdt, code)
-        y = run(w, xb, xdt).cpu().numpy()
-        yr, a = oracle.mirai_gemv_x(w, xb, xdt)
-        if code == zero:
-            # every weight is exactly zero, so the relative bar has nothing to
-            # scale with; the kernel's s*P - s*z*X cancels to within the fp32
-            # rounding of its per-chunk sums: at most ~40 roundings of partial
-            # sums bounded by (1024 + 15) * sum|x| per chunk, < 2^-18 of
-            # s * 1039 * sum|x| over the row
-            s = oracle.bf16_to_f64(w.scales)
-            xa = np.abs(oracle.f16_to_f64(xb) if xdt == "f16" else oracle.bf16_to_f64(xb))
-            bound = 2.0 ** -18 * s.max() * 1039 * xa.sum(1)
-            assert np.all(np.abs(y) <= bound[:, None]), f"code=zero={code}"
-        else:
-            assert_within(y, yr, a, f"code {code} zero {zero} {xdt}")
+        for batch in (1, 8):
+            xb = draw_x(batch, K, xdt, code + batch)
+            y = run(w, xb, xdt).cpu().numpy()
+            yr, a = oracle.mirai_gemv_x(w, xb, xdt)
+            assert_within(y, yr, a, f"code {code} zero {zero} batch {batch} {xdt}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_mirai_near_zero_weights(xdt):
+    # Mirai-M: codes at and next to the zero point (w = 0 or +-s); Mirai-L:
+    # signed codes -1, 0, 1; every K from one group to 4096, batch 1 and 8
+    for K in (64, 128, 704, 4096):
+        for z in (0, 8, 15):
+            cs = [v for v in (z - 1, z, z + 1) if 0 <= v <= 15]
+            for only_z in (True, False):
+                w = synth.mirai_weights("M", 130, K, cfg=229, set_id=K + z, codes="set",
+                                        code_set=[z] if only_z else cs, zeros="const", const_zero=z)
+                for batch in (1, 8):
+                    xb = draw_x(batch, K, xdt, K + z + batch)
+                    y = run(w, xb, xdt).cpu().numpy()
+                    yr, a = oracle.mirai_gemv_x(w, xb, xdt)
+                    assert_within(y, yr, a, f"mirai-M K={K} z={z} codes {cs if not only_z else [z]} b={batch} {xdt}")
+        w = synth.mirai_weights("L", 130, K, cfg=229, set_id=K, codes="set", code_set=(-1, 0, 1))
+        for batch in (1, 8):
+            xb = draw_x(batch, K, xdt, K + batch)
+            y = run(w, xb, xdt).cpu().numpy()
+            yr, a = oracle.mirai_gemv_x(w, xb, xdt)
+            assert_within(y, yr, a, f"mirai-L K={K} codes -1..1 b={batch} {xdt}")
 
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
