@@ -32,7 +32,7 @@ EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
            "qgemm_affine4_verify", "qattn_decode_workspace_bytes", "qattn_decode",
-           "qmoe_layer_decode",
+           "qmoe_layer_decode", "qmoe_layer_decode_noalloc",
            "qd_status_string", "qd_last_error")
 
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
     L.qmoe_layer_decode.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P, ctypes.c_int, _P,
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.qmoe_layer_decode_noalloc.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P,
+                                            ctypes.c_int, _P, _P, _P, _P, _P]
     L.qattn_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
     L.qattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.qattn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
                "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
                "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify",
-               "qattn_decode", "qmoe_layer_decode"):
+               "qattn_decode", "qmoe_layer_decode", "qmoe_layer_decode_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -359,6 +361,29 @@ def qmoe_layer(w: MoeWeights, x, k: int = 8, workspace=None, logits=None, idx=No
     qgemv_affine8(w.router_q, w.router_s, w.router_b, x, out=logits)
     idx, weights = qmoe_route_topk(logits, k, idx, weights)
     return qmoe_expert_gemv(w, idx, weights, x, out=out, workspace=workspace)
+
+
+def qmoe_layer_decode_noalloc(w: MoeWeights, x, k: int = 8, logits=None, idx=None, weights=None,
+                              out=None):
+    """One decode token through a MoE layer (as qmoe_layer with T = 1) with the
+    intermediate activations in the library's per-device scratch: no workspace
+    is allocated for the call. Calls on one device must not overlap."""
+    _need(x, "x", (torch.float16, torch.bfloat16), 2)
+    if x.shape[0] != 1 or x.shape[1] != w.H:
+        raise ValueError("x must be [1][H]")
+    if logits is None:
+        logits = torch.empty((1, w.E), dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty((1, k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((1, k), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((1, w.H), dtype=torch.float32, device=x.device)
+    st = w.cstruct()
+    _check(lib().qmoe_layer_decode_noalloc(ctypes.byref(st), _ptr(w.router_q), _ptr(w.router_s),
+                                           _ptr(w.router_b), k, _ptr(x), _x_dtype(x), _ptr(logits),
+                                           _ptr(idx), _ptr(weights), _ptr(out), _stream()))
+    return out
 
 
 def qgemm_affine4_chunk(wq, scales, biases, x, out=None):

@@ -311,12 +311,15 @@ qd_status qmoe_expert_gemv(const qd_moe_weights* w, const int32_t* idx, const fl
                     fn);
 }
 
-qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
-                            const uint16_t* router_s, const uint16_t* router_b, int32_t k,
-                            const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
-                            float* weights, float* y, void* workspace, size_t ws_bytes,
-                            qd_stream stream) {
-    const char* fn = "qmoe_layer_decode";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode-layer calls (everything but the workspace).
+qd_status check_layer_decode(const char* fn, const qd_moe_weights* w, const uint32_t* router_q,
+                             const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                             const void* x, qd_dtype x_dtype, const float* logits,
+                             const int32_t* idx, const float* weights, const float* y) {
     qd_status st = check_moe(fn, w);
     if (st != QD_OK) return st;
     if (w->E > 256) return fail(QD_ERR_UNSUPPORTED, "%s: E = %d (at most 256)", fn, w->E);
@@ -332,6 +335,22 @@ qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
     CHECK_PTR(idx);
     CHECK_PTR(weights);
     CHECK_PTR(y);
+    return QD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
+                            const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                            const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                            float* weights, float* y, void* workspace, size_t ws_bytes,
+                            qd_stream stream) {
+    const char* fn = "qmoe_layer_decode";
+    qd_status st = check_layer_decode(fn, w, router_q, router_s, router_b, k, x, x_dtype, logits,
+                                      idx, weights, y);
+    if (st != QD_OK) return st;
     const qd::MoeArgs m = moe_args(w);
     const size_t need = qd::moe_workspace_bytes(m, 1, k);
     if (!workspace)
@@ -346,6 +365,30 @@ qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
     if (e != hipSuccess) return from_hip(e, fn);
     return from_hip(qd::launch_moe_decode_routed(m, logits, k, x, xkind, idx, weights, y, workspace,
                                                  (hipStream_t)stream),
+                    fn);
+}
+
+qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* router_q,
+                                    const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                                    const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                                    float* weights, float* y, qd_stream stream) {
+    const char* fn = "qmoe_layer_decode_noalloc";
+    qd_status st = check_layer_decode(fn, w, router_q, router_s, router_b, k, x, x_dtype, logits,
+                                      idx, weights, y);
+    if (st != QD_OK) return st;
+    const qd::MoeArgs m = moe_args(w);
+    const size_t need = qd::moe_decode_workspace_bytes(m, k);
+    if (need > qd::kMoeNoAllocBytes)
+        return fail(QD_ERR_WORKSPACE,
+                    "%s: k * I + I_shared = %zu activations need %zu bytes of scratch; the "
+                    "allocation-free call holds at most %zu (use qmoe_layer_decode)",
+                    fn, need / sizeof(float), need, qd::kMoeNoAllocBytes);
+    const int xkind = x_dtype == QD_F16 ? 0 : 1;
+    hipError_t e = qd::launch_gemv(8, 0, router_q, router_s, router_b, nullptr, x, xkind, logits,
+                                   w->E, w->H, 1, (hipStream_t)stream);
+    if (e != hipSuccess) return from_hip(e, fn);
+    return from_hip(qd::launch_moe_decode_routed_noalloc(m, logits, k, x, xkind, idx, weights, y,
+                                                         (hipStream_t)stream),
                     fn);
 }
 

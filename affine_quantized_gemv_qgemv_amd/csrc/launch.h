@@ -64,6 +64,13 @@ hipError_t launch_moe_decode_routed(const MoeArgs& m, const float* logits, int k
                                     int xkind, int32_t* idx, float* w, float* y, void* ws,
                                     hipStream_t st);
 
+// The same layer with the gate+up activations in the library's per-device
+// scratch (kMoeNoAllocBytes) instead of a caller workspace.
+constexpr size_t kMoeNoAllocBytes = size_t(4) << 20;
+hipError_t launch_moe_decode_routed_noalloc(const MoeArgs& m, const float* logits, int k,
+                                            const void* x, int xkind, int32_t* idx, float* w,
+                                            float* y, hipStream_t st);
+
 hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float* w, int T, int k,
                               const void* x, int xkind, float* y, void* ws, size_t ws_bytes,
                               hipStream_t st);

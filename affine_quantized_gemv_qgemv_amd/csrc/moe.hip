@@ -36,6 +36,8 @@
 #include "launch.h"
 #include "route.h"
 
+#include <mutex>
+
 namespace qd {
 
 __device__ __forceinline__ float gelu_f(float u, int act) {
@@ -497,6 +499,44 @@ hipError_t launch_moe_decode_routed(const MoeArgs& m, const float* logits, int k
     b.Is = m.Is;
     b.k = k;
     return launch_down(b, st);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode layer: the gate+up activations h live in a scratch
+// array of this library, one per device, held until the process ends. Only
+// the host touches it, through its device address (looked up once per device;
+// the array's name in host code is not that address), which is passed to the
+// kernels as their workspace. Every call on a device shares the array, so
+// calls that overlap on one device race; h is fully written by gate+up before
+// down reads it, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kMoeNoAllocBytes];
+
+static hipError_t scratch_address(void** out) {
+    static void* addr[64];
+    static hipError_t err[64];
+    static std::once_flag once[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    // with this device current (hipGetDevice above): its copy of the array
+    std::call_once(once[dev], [dev] {
+        err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch));
+    });
+    if (err[dev] != hipSuccess) return err[dev];
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_moe_decode_routed_noalloc(const MoeArgs& m, const float* logits, int k,
+                                            const void* x, int xkind, int32_t* idx, float* w,
+                                            float* y, hipStream_t st) {
+    if (moe_decode_workspace_bytes(m, k) > kMoeNoAllocBytes) return hipErrorInvalidValue;
+    void* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_moe_decode_routed(m, logits, k, x, xkind, idx, w, y, ws, st);
 }
 
 size_t moe_workspace_bytes(const MoeArgs& m, int T, int k) {

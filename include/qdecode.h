@@ -215,6 +215,23 @@ qd_status qmoe_layer_decode(const qd_moe_weights* w, const uint32_t* router_q,
                             qd_stream stream);
 
 /*
+ * qmoe_layer_decode without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. The gate+up
+ * activations (k * I + I_shared floats) go to a scratch array inside the
+ * library instead, 4 MiB per device, held by every device the library runs
+ * on until the process ends; a layer needing more is rejected with
+ * QD_ERR_WORKSPACE before any launch. The call allocates nothing. All calls
+ * on one device share that scratch, so calls that may overlap on a device
+ * (other streams, other threads) race and must be serialized by the caller.
+ * Arguments, outputs and results are those of qmoe_layer_decode, bit for bit.
+ */
+qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* router_q,
+                                    const uint16_t* router_s, const uint16_t* router_b, int32_t k,
+                                    const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                                    float* weights, float* y, qd_stream stream);
+
+/*
  * Prefill chunk ([TF] internals: prompts run in chunks of at most 128 tokens
  * so one fetch of a weight serves many rows):
  *   Y[m][n] = sum_k w[n][k] * X[m][k],  X [M][K] bf16 bits, Y [M][N] fp32.

@@ -282,3 +282,24 @@ def test_attention_workspace_covers_every_position(Hkv):
     if Hkv == 8:
         assert _attn_splits(2048, 8) > _attn_splits(2049, 8)
         assert qd.qattn_workspace_bytes(16, 8, 128, 2049) >= _attn_splits(2048, 8) * 16 * 130 * 4
+
+
+def test_moe_layer_decode_noalloc_argument_errors():
+    # the allocation-free decode layer: same checks as qmoe_layer_decode, and
+    # a layer whose activations exceed the library's 4 MiB scratch is refused
+    # before any launch
+    L = qd.lib()
+
+    def call(st, k=8, dt=0, rq=A, logits=A):
+        return L.qmoe_layer_decode_noalloc(ctypes.byref(st), rq, A, A, k, A, dt, logits, A, A, A, None)
+
+    assert L.qmoe_layer_decode_noalloc(None, A, A, A, 8, A, 0, A, A, A, A, None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert call(moe_struct(group_size=128)) == qd.QD_ERR_UNSUPPORTED
+    assert call(moe_struct(E=257)) == qd.QD_ERR_UNSUPPORTED
+    assert call(moe_struct(), k=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert call(moe_struct(), dt=2) == qd.QD_ERR_UNSUPPORTED
+    assert call(moe_struct(), rq=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert call(moe_struct(), logits=MIS) == qd.QD_ERR_MISALIGNED
+    # 32 slots of I = 32768 plus the shared expert: 4 MiB + 4 KiB of activations
+    assert call(moe_struct(E=64, I=32768, I_shared=1024), k=32) == qd.QD_ERR_WORKSPACE
+    assert "scratch" in qd.last_error()
