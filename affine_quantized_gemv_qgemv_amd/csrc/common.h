@@ -313,7 +313,7 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
     }
 }
 
-// Chunk-major staging of B > 1 fp16 vectors (the XF = 0 values and sums of
+// Chunk-major staging of B fp16 vectors (the XF = 0 values and sums of
 // stage_x, rearranged):
 //   xs[c][b][q]  uint4, slot c at a stride of SC = B*QPC + 1 uint4 (the pad
 //                puts the 8 lanes of one LDS cycle in distinct banks);

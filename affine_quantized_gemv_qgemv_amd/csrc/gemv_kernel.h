@@ -22,10 +22,13 @@
 //    is used, so every wave keeps U*R 16-byte loads per lane in flight.
 //  * When the staged activations would not fit LDS, each workgroup streams
 //    K through LDS in slices: it stages slice 0, runs all of its tiles over
-//    it, stages slice 1, and so on. After each slice a tile's row segments
-//    are reduced and added to a per-row partial held in LDS by the one wave
-//    that owns the tile, so every output is summed in the same order on
-//    every run (no atomics, no cleared output, no second launch).
+//    it, stages slice 1, and so on. When a matrix has too few tiles to fill
+//    the chip, the F wave groups of a workgroup share each tile, group f
+//    taking the steps f, f + F, ... of every slice. A tile's row segments
+//    are reduced after each slice and added to a per-row partial that the
+//    group keeps in LDS; at the end the F partials are summed in group
+//    order. Every output is therefore summed in the same order on every run
+//    (no atomics, no cleared output, no second launch).
 //
 // Weight formats (template parameter FMT); all reduce to the per-group
 // epilogue y += s * sum(u x) + c * sum(x) with unsigned codes u:
@@ -60,9 +63,9 @@ struct GemvArgs {
     int N, K;
     int nb;              // activation vectors in this launch (<= B)
     int chunks_slice;    // chunks per K slice staged at a time (a multiple of 4)
-    int nslices;         // K slices; > 1 keeps per-row partials in LDS
+    int nslices;         // K slices staged one after another
     int slice_lds;       // bytes of LDS before the partials (the staged slice, aligned)
-    int part_tiles;      // tiles per wave the partials region holds
+    int part_tiles;      // tiles per tile-wave the partials region holds
     const uint8_t* zp;   // Mirai-M zero points, zstride bytes per row
     int zstride;
     const uint32_t* signs;   // XF == 2: rotation signs [K/32] (NULL = none)
@@ -92,14 +95,17 @@ struct Round {
 template <int BITS, int XF, int B, int CPL>
 __device__ __forceinline__ void stage_x_any(const void* x, int kind, int64_t xstride, int nb, int c0,
                                             int nc, uint4* lds) {
-    if constexpr (XF == 0 && B > 1)
+    if constexpr (XF == 0)
         stage_x_cm<BITS, B, CPL>(x, xstride, nb, c0, nc, lds);
     else
         stage_x<BITS, XF, CPL>(x, kind, xstride, nb, c0, nc, lds);
 }
 
 // SL: K is streamed in a.nslices slices (otherwise one slice holds all of K).
-template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL, int FMT, bool SL>
+// LF: log2 of F, the wave groups that share each tile (group f takes the
+// steps f, f + F, ... of every slice).
+template <int BITS, int XF, int B, int LPR, int R, int U, int WPE, int CPL, int FMT, bool SL,
+          int LF>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) void qgemv_kernel(
     GemvArgs a) {
     extern __shared__ uint4 lds[];
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     constexpr int CPG = 64 / CC;       // chunks per group of 64
     constexpr int RPI = 64 / LPR;      // rows per wave instruction
     constexpr int ROWS = RPI * R;      // rows per tile
-    constexpr bool CM = XF == 0 && B > 1;   // chunk-major staging (stage_x_cm)
+    constexpr bool CM = XF == 0;   // chunk-major staging of fp16 activations (stage_x_cm)
     const int C16 = a.K / CC;
     const int G = a.K / 64;
     const int64_t wpr = (int64_t)a.K * BITS / 32;  // words per row
@@ -115,25 +121,34 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     const int lane = threadIdx.x & 63;
     const int seg = lane / LPR, sl = lane % LPR;
     const int nwaves = blockDim.x >> 6;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // wave-uniform: keeps the tile bounds and loop control in scalar registers
-    const int gw = blockIdx.x * nwaves + wave;
-    const int W = gridDim.x * nwaves;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int F = 1 << LF;           // wave groups per tile
+    const int f = wave & (F - 1);        // this wave's group
+    const int TWG = nwaves >> LF;        // tile-waves per workgroup
+    const int tw = wave >> LF;
+    const int gw = blockIdx.x * TWG + tw;
+    const int W = gridDim.x * TWG;
     const int ntiles = (a.N + ROWS - 1) / ROWS;
-    // This wave's tiles, interleaved: wave w takes tiles w, w + W, ..., so
-    // all waves together sweep one window of the matrix, as a streaming read
-    // does.
+    // This tile-wave's tiles, interleaved: tile-wave w takes tiles w, w + W,
+    // ..., so all waves together sweep one window of the matrix, as a
+    // streaming read does.
     const int t0 = gw, tstep = W;
     const int ntl = gw < ntiles ? (ntiles - gw + W - 1) / W : 0;
-    // Per-row partials across K slices: [wave][tile of the wave][row][vector]
-    float* part = (float*)((char*)lds + a.slice_lds) + (size_t)wave * a.part_tiles * ROWS * B;
+    // Partials in LDS unless one pass over K finishes every row:
+    // [group][tile-wave][tile of the tile-wave][row][vector]
+    const bool direct = F == 1 && a.nslices == 1;
+    const int PT = a.part_tiles;
+    float* part_base = (float*)((char*)lds + a.slice_lds);
+    float* part = part_base + (size_t)(f * TWG + tw) * PT * ROWS * B;
 
     // Rotation prologue: LDS for the per-vector factors (only kernels with
     // XF == 2 reference it); rot[kRotMaxB + b] is 2^-e of vector b.
     float* rot = nullptr;
     if constexpr (XF == 2) rot = rot_shared();
 
-    // The slice being processed: chunks [c0, c0 + nc), S steps per row,
+    // The slice being processed: chunks [c0, c0 + nc); S steps per row for
+    // this wave's group (step i of the group is step i F + f of the row),
     // RPT rounds per tile.
     int c0 = 0, nc = 0, S = 0, RPT = 1;
 
@@ -158,7 +173,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
-            const int c = ((sg * U + u) * LPR + sl) * CPL;
+            const int c = (((sg * U + u) * F + f) * LPR + sl) * CPL;
             const int gc = c0 + min(c, nc - CPL);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -185,12 +200,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
 
     const uint32_t magic = in_vgpr(kMagic16);
     // ti: the tile's index among this wave's tiles (its partials slot)
-    auto consume = [&](const Round<R, U, CPL>& buf, int tile, int ti, int sg, bool first,
-                       bool last) {
+    auto consume = [&](const Round<R, U, CPL>& buf, int tile, int ti, int sg, bool last) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (sg * U + u >= S) break;  // uniform
-            const int cu = ((sg * U + u) * LPR + sl) * CPL;
+            const int cu = (((sg * U + u) * F + f) * LPR + sl) * CPL;
             const int c = min(cu, nc - CPL);
             // per row: scale, centred bias and the centring subtrahends
             float sc[R], bi[R];
@@ -223,7 +237,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             }
             int slot[CPL];
 #pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) slot[ch] = xslot<CPL>(c + ch, nc);
+            // c is a multiple of CPL: the lane's chunks sit nc / CPL slots apart
+            for (int ch = 0; ch < CPL; ++ch)
+                slot[ch] = (int)((unsigned)c / CPL + (unsigned)ch * ((unsigned)nc / CPL));
             constexpr bool XS = FMT == W_AFFINE;   // the Mirai formats have no sum term
             if constexpr (FMT == W_MIRAI_L) {
                 uint4 cw[CPL][R];   // signed bytes -> offset-128 unsigned codes
@@ -243,8 +259,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             }
         }
         if (sg == RPT - 1) {
-            // the tile's rows over this slice: add the earlier slices' partial
-            // (same wave, same order on every run) and keep or store the sum
+            // the tile's rows over this slice (this group's steps): stored, or
+            // added to the group's partial (same wave, same order on every
+            // run); a lone group stores the sum after the last slice
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int row = tile * ROWS + r * RPI + seg;
@@ -254,12 +271,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
                     if constexpr (XF == 2) v *= rot[kRotMaxB + bb];
                     y[r][bb] = 0.f;
                     if (sl == 0 && row < a.N && bb < a.nb) {
-                        float* pp = part + ((size_t)ti * ROWS + r * RPI + seg) * B + bb;
-                        if (!first) v = *pp + v;
-                        if (last)
-                            a.y[(int64_t)bb * a.N + row] = v;
-                        else
-                            *pp = v;
+                        float* dst = a.y + (int64_t)bb * a.N + row;
+                        if (direct) {
+                            *dst = v;
+                        } else {
+                            float* pp = part + ((size_t)ti * ROWS + r * RPI + seg) * B + bb;
+                            v = *pp + v;
+                            if (F == 1 && last)
+                                *dst = v;
+                            else
+                                *pp = v;
+                        }
                     }
                 }
             }
@@ -273,8 +295,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     auto set_slice = [&](int slc) {
         c0 = slc * a.chunks_slice;
         nc = min(a.chunks_slice, C16 - c0);
-        S = (nc + LPR * CPL - 1) / (LPR * CPL);   // steps per row
-        RPT = (S + U - 1) / U;                    // rounds per tile
+        const int srow = (nc + LPR * CPL - 1) / (LPR * CPL);   // steps per row
+        S = srow > f ? (srow - f + F - 1) >> LF : 0;           // this group's
+        RPT = (S + U - 1) / U;                                 // rounds per tile
     };
     // all of this wave's tiles over the staged slice
     auto run_slice = [&](bool first, bool last) {
@@ -284,9 +307,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             const int tile = t0 + ti * tstep;
             const int sg = rd - ti * RPT;
             if (rd > 0 || !first) issue(A, tile, sg);
-            consume(A, tile, ti, sg, first, last);
+            consume(A, tile, ti, sg, last);
         }
     };
+    // this group's partials start at zero (visible after the first barrier)
+    if (!direct)
+        for (int e = lane; e < PT * ROWS * B; e += 64) part[e] = 0.f;
     // Slice 0: the first weight loads are in flight while the activations
     // are staged (behind the activation loads when they are rotated, so the
     // transform runs while the weights arrive).
@@ -318,6 +344,25 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             __syncthreads();
         }
     }
+    if constexpr (F > 1) {
+        // the F groups' partials of each row, summed in group order
+        __syncthreads();
+        if (f == 0) {
+            for (int ti = 0; ti < ntl; ++ti) {
+                const int tile = t0 + ti * tstep;
+                for (int e = lane; e < ROWS * B; e += 64) {
+                    const int rl = e / B, bb = e - rl * B;
+                    const int row = tile * ROWS + rl;
+                    if (row < a.N && bb < a.nb) {
+                        float v = 0.f;
+                        for (int g = 0; g < F; ++g)
+                            v += part_base[((size_t)(g * TWG + tw) * PT + ti) * ROWS * B + e];
+                        a.y[(int64_t)bb * a.N + row] = v;
+                    }
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -344,7 +389,7 @@ hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     auto per_of = [&](int sp) { return (((C16 + sp - 1) / sp) + 3) & ~3; };
     // the kernel's staging layout (chunk-major for several fp16 vectors)
     auto bytes = [&](int nc) {
-        return (XF == 0 && B > 1) ? St::bytes_cm(B, nc) : St::bytes(base.nb, nc);
+        return XF == 0 ? St::bytes_cm(B, nc) : St::bytes(base.nb, nc);
     };
     int slices = 1;
     if (bytes(C16) > budget) {
@@ -363,24 +408,39 @@ hipError_t run_cfg(const GemvArgs& base, int nwaves, hipStream_t st) {
     const int threads = nwaves * 64;
     const int rows_per_tile = (64 / LPR) * R;
     const int ntiles = (a.N + rows_per_tile - 1) / rows_per_tile;
-    const int want = (ntiles + nwaves - 1) / nwaves;
+    auto kern = slices == 1 ? qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, false, 0>
+                            : qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, true, 0>;
+    // resident wave slots with the partials region reserved
+    const int occ = std::max(1, occupancy((const void*)kern, threads, xlds + kPartReserve));
+    const int slots = occ * dev.cus * nwaves;
+    // Sliced fp16 launches of several vectors (few rows over a long K) take
+    // F wave groups per tile while the tiles leave resident waves idle
+    // (never more groups than a slice has steps per row).
+    int F = 1;
+    if constexpr (XF == 0 && B > 1) {
+        const int steps = (per + LPR * CPL - 1) / (LPR * CPL);
+        if (slices > 1)
+            while (F < 4 && 2 * F <= nwaves && 2 * F <= steps && (int64_t)ntiles * 2 * F <= slots)
+                F *= 2;
+        if (F == 2) kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, true, 1>;
+        if (F == 4) kern = qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, true, 2>;
+    }
+    const int twg = nwaves / F;   // tile-waves per workgroup
+    const int want = (ntiles + twg - 1) / twg;
     size_t lds = xlds;
     int grid;
-    auto kern = slices == 1 ? qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, false>
-                            : qgemv_kernel<BITS, XF, B, LPR, R, U, WPE, CPL, FMT, true>;
-    if (slices == 1) {
-        const int occ = occupancy((const void*)kern, threads, lds);
-        grid = std::max(1, std::min(want, std::max(1, occ) * dev.cus));
+    if (slices == 1 && F == 1) {
+        const int occ1 = occupancy((const void*)kern, threads, lds);
+        grid = std::max(1, std::min(want, std::max(1, occ1) * dev.cus));
     } else {
         // partial slots of one tile for every wave of a workgroup
         const size_t per_tile = (size_t)nwaves * rows_per_tile * B * sizeof(float);
-        const int occ = occupancy((const void*)kern, threads, xlds + kPartReserve);
-        grid = std::max(1, std::min(want, std::max(1, occ) * dev.cus));
-        int pt = (ntiles + grid * nwaves - 1) / (grid * nwaves);
+        grid = std::max(1, std::min(want, occ * dev.cus));
+        int pt = (ntiles + grid * twg - 1) / (grid * twg);
         const int cap = std::max<int>(1, (int)(kPartReserve / per_tile));
         if (pt > cap) {   // more workgroups, each with fewer tiles per wave
-            grid = (ntiles + nwaves * cap - 1) / (nwaves * cap);
-            pt = (ntiles + grid * nwaves - 1) / (grid * nwaves);
+            grid = (ntiles + twg * cap - 1) / (twg * cap);
+            pt = (ntiles + grid * twg - 1) / (grid * twg);
         }
         a.part_tiles = pt;
         lds = xlds + (size_t)pt * per_tile;
