@@ -32,7 +32,7 @@ EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
            "qgemm_affine4_verify", "qattn_decode_workspace_bytes", "qattn_decode",
-           "qmoe_layer_decode", "qmoe_layer_decode_noalloc",
+           "qmoe_layer_decode", "qmoe_layer_decode_noalloc", "qd_stream_read",
            "qd_status_string", "qd_last_error")
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.qattn_decode_workspace_bytes.restype = ctypes.c_size_t
     L.qattn_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
                                _P, _P, ctypes.c_size_t, _P]
+    L.qd_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+    L.qd_stream_read.restype = ctypes.c_int
     L.qd_status_string.argtypes = [ctypes.c_int]
     L.qd_status_string.restype = ctypes.c_char_p
     L.qd_last_error.argtypes = []
@@ -384,6 +386,14 @@ def qmoe_layer_decode_noalloc(w: MoeWeights, x, k: int = 8, logits=None, idx=Non
                                            _ptr(w.router_b), k, _ptr(x), _x_dtype(x), _ptr(logits),
                                            _ptr(idx), _ptr(weights), _ptr(out), _stream()))
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Reads every byte of the device tensor buf once (the HBM read ceiling;
+    see qd_stream_read). sink: a device tensor of at least 4 bytes."""
+    if not buf.is_cuda or not sink.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf and sink must be contiguous device tensors")
+    _check(lib().qd_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()))
 
 
 def qgemm_affine4_chunk(wq, scales, biases, x, out=None):

@@ -477,6 +477,15 @@ qd_status qattn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t*
                     fn);
 }
 
+qd_status qd_stream_read(const void* buf, size_t bytes, uint32_t* sink, qd_stream stream) {
+    const char* fn = "qd_stream_read";
+    CHECK_PTR(buf);
+    CHECK_PTR(sink);
+    if (bytes == 0 || bytes > ((size_t)1 << 40))
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: bytes = %zu must be in [1, 2^40]", fn, bytes);
+    return from_hip(qd::launch_stream_read(buf, (int64_t)bytes, sink, (hipStream_t)stream), fn);
+}
+
 const char* qd_status_string(qd_status s) {
     switch (s) {
         case QD_OK: return "QD_OK";

@@ -87,6 +87,9 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const ui
                               int window, int pos, float scale, float* out, void* ws,
                               size_t ws_bytes, hipStream_t st);
 
+// Read-only stream over bytes of device memory (the HBM read ceiling).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st);
+
 // x: fp16 or bf16 bits (xkind X_F16 / X_BF16), [M][K].
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x, int xkind, float* y, int M, int N, int K,

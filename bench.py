@@ -10,9 +10,13 @@ HBM before timing starts. Steps are replayed from a HIP graph; the timed
 region is bracketed by device synchronizations and measured with HIP
 events on the launch stream.
 
-Printed: one JSON line with the achieved HBM bandwidth (algorithmic bytes
-over time), the roofline of the dominant kernel, and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+Printed: one JSON line with the achieved HBM bandwidth over the K timed
+steps (algorithmic bytes over time), each projection timed alone (median of
+5 trials of >= 200 launches) against both the 8 TB/s peak and the read-only
+stream kernel's rate at the same byte count (the practical ceiling), the
+roofline of the dominant kernel, µs per decode MoE layer (the c3 workload,
+median of 5 trials of 240 layer calls), and the fp64 CPU oracle timed on a
+bounded sample of the same workload, with the host CPU model.
 
 Other workloads (``--config``): c1 (4096x4096 GEMV), c3 (MoE decode layer),
 c4 (prefill chunk GEMM), c5 (70B-shaped sweep over batch 1/2/4/8), verify
@@ -56,6 +60,8 @@ def parse():
                    help="Mirai formats: fuse RMSNorm + the block-32 random Hadamard rotation "
                         "ahead of the GEMV (qgemv_mirai_*_rht)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-moe", action="store_true",
+                   help="c2: leave the decode MoE layer figure out of the line")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--eager", action="store_true",
                    help="launch every step from the host instead of replaying HIP graphs "
@@ -91,6 +97,8 @@ def source_hash(files) -> str:
 
 
 GEMV_SOURCES = ["affine_quantized_gemv_qgemv_amd/csrc/gemv.hip",
+                "affine_quantized_gemv_qgemv_amd/csrc/gemv_kernel.h",
+                "affine_quantized_gemv_qgemv_amd/csrc/gemv_affine4.hip",
                 "affine_quantized_gemv_qgemv_amd/csrc/common.h"]
 
 
@@ -150,6 +158,8 @@ class Timer:
                 for f in step_fns[:rem]:
                     f()
         cyc.replay()
+        if remg is not None:
+            remg.replay()   # every graph replayed once before the timed region
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -164,6 +174,47 @@ class Timer:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return start.elapsed_time(end) / 1e3, wall
+
+
+TRIALS = 5          # trials per figure (the median is reported)
+MIN_CALLS = 200     # calls per trial
+
+
+def median_time(step_fns, calls: int = MIN_CALLS, trials: int = TRIALS, warmup: int = 8):
+    """Median over `trials` timings of `calls` replayed calls (seconds per call),
+    each trial bracketed by device synchronizations; also returns every trial."""
+    import torch
+    timer = Timer(torch)
+    calls = max(calls, len(step_fns))
+    per = []
+    for t in range(trials):
+        secs, _ = timer.run(step_fns, calls, warmup if t == 0 else 0)
+        per.append(secs / calls)
+    return float(np.median(per)), per
+
+
+def cpu_model() -> str:
+    """The host CPU model (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stream_ceiling(torch, qd, nbytes: int, min_total: int = 1 << 30):
+    """The read-only stream kernel (qd_stream_read) over buffers of nbytes each,
+    cycled so that their total exceeds the 256 MB Infinity Cache: median GB/s of
+    5 trials of >= 200 reads."""
+    nbuf = max(2, -(-min_total // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fns = [(lambda b=b: qd.stream_read(b, sink)) for b in bufs]
+    t, _ = median_time(fns)
+    del bufs
+    return nbytes / t / 1e9, t
 
 
 def cpu_threads():
@@ -302,11 +353,11 @@ def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine", rht=Fa
     step_bytes = sum(gemv_bytes(N, K, batch, fmt=fmt, rht=rht) for K, N in shapes)
     per_shape = []
     for j, (K, N) in enumerate(shapes):
-        sj, _ = timer.run([step_fn(s, j) for s in range(nsets)], max(nsets, steps // 2),
-                          min(args.warmup, nsets))
-        n = max(nsets, steps // 2)
-        per_shape.append(dict(K=K, N=N, us=sj / n * 1e6,
-                              gbs=gemv_bytes(N, K, batch, fmt=fmt, rht=rht) * n / sj / 1e9))
+        # each projection alone: median of 5 trials of >= 200 launches
+        t, trials = median_time([step_fn(s, j) for s in range(nsets)])
+        nb = gemv_bytes(N, K, batch, fmt=fmt, rht=rht)
+        per_shape.append(dict(K=K, N=N, us=t * 1e6, gbs=nb / t / 1e9,
+                              trials_us=[round(x * 1e6, 3) for x in trials]))
     cpu = [(sets[0][j][3], xbits[j]) + ((rots[j][2], rots[j][3]) if rht else ())
            for j in range(len(shapes))]
     return dict(secs=secs, wall=wall, step_bytes=step_bytes, per_shape=per_shape,
@@ -474,16 +525,18 @@ def device_affine(torch, gen, bits, shape_nk, extra=()):
     return wq, s16, b16
 
 
-def bench_moe(args, torch, qd, prefill: bool):
-    """MoE layer (router int8 -> top-8 -> 8 routed + shared expert), 30 layers
-    cycled. Decode: batch 1, fp16 activations (16 distinct tokens per layer).
-    Prefill: one 128-token chunk of bf16 activations per step."""
-    E, H, I, Is, k, L = 128, 2816, 704, 2112, 8, 30
+MOE_SHAPE = dict(E=128, H=2816, I=704, Is=2112, k=8, layers=30)
+
+
+def build_moe(torch, qd, prefill: bool, nlayers: int):
+    """MoE layers with the synth distributions drawn on the device, and the
+    activations: decode 16 distinct fp16 tokens, prefill one bf16 chunk of 128."""
+    E, H, I, Is = MOE_SHAPE["E"], MOE_SHAPE["H"], MOE_SHAPE["I"], MOE_SHAPE["Is"]
     T = 128 if prefill else 1
     gen = torch.Generator(device="cuda")
     gen.manual_seed(3 if not prefill else 4)
     layers = []
-    for _ in range(args.sets or L):
+    for _ in range(nlayers):
         rq, rs, rb = device_affine(torch, gen, 8, (E, H))
         guq, gus, gub = device_affine(torch, gen, 4, (2 * I, H), (E,))
         dnq, dns, dnb = device_affine(torch, gen, 4, (H, I), (E,))
@@ -494,6 +547,15 @@ def bench_moe(args, torch, qd, prefill: bool):
     ntok = 16 if not prefill else 1
     xdt = torch.bfloat16 if prefill else torch.float16
     xs = [torch.randn((T, H), device="cuda", generator=gen).to(xdt) for _ in range(ntok)]
+    return layers, xs, T
+
+
+def moe_steps(torch, qd, layers, xs, T, prefill: bool):
+    """One step per (layer, token) pair (at most 240), and the step's algorithmic
+    bytes: router + each distinct selected expert once + shared expert +
+    activations in and out."""
+    E, H, I, Is, k = (MOE_SHAPE[n] for n in ("E", "H", "I", "Is", "k"))
+    ntok = len(xs)
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -502,25 +564,54 @@ def bench_moe(args, torch, qd, prefill: bool):
 
     def step(i):
         lw, x = layers[i % len(layers)], xs[i % ntok]
+
         def f():
             qd.qmoe_layer(lw, x, k=k, workspace=ws, logits=logits, idx=idx, weights=wts, out=y)
         return f
 
-    nsteps_cycle = len(layers) * ntok if not prefill else len(layers)
-    nsteps_cycle = min(nsteps_cycle, 240)
-    secs, _ = Timer(torch).run([step(i) for i in range(nsteps_cycle)], args.steps, args.warmup)
-    t = secs / args.steps
-    # algorithmic bytes: router + each distinct selected expert once + shared expert
+    ncyc = min(len(layers) * ntok if not prefill else len(layers), 240)
+    fns = [step(i) for i in range(ncyc)]
     expert_bytes = matrix_bytes(2 * I, H) + matrix_bytes(H, I)
     shared_bytes = matrix_bytes(2 * Is, H) + matrix_bytes(H, Is)
     router_bytes = matrix_bytes(E, H, 8)
     uniq = []
-    for i in range(min(nsteps_cycle, 32)):
-        step(i)()
+    for i in range(min(ncyc, 32)):
+        fns[i]()
         torch.cuda.synchronize()
         uniq.append(len(set(idx.cpu().numpy().ravel().tolist())))
     mean_uniq = float(np.mean(uniq))
     step_bytes = router_bytes + mean_uniq * expert_bytes + shared_bytes + T * H * (2 + 4)
+    return fns, step_bytes, mean_uniq
+
+
+def moe_decode_figure(torch, qd):
+    """µs per decode MoE layer (the c3 workload): median of 5 trials of 240
+    layer calls over 30 resident layers (13.2 GB) and 16 tokens."""
+    layers, xs, T = build_moe(torch, qd, False, MOE_SHAPE["layers"])
+    fns, step_bytes, mean_uniq = moe_steps(torch, qd, layers, xs, T, False)
+    t, trials = median_time(fns, calls=240)
+    gbs = step_bytes / t / 1e9
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": "c3: MoE decode layer, batch 1, hidden 2816, 128 experts (int4 g64 "
+                        "gate+up 2816->2x704, down 704->2816), int8 router, top-8, shared expert "
+                        "2816->2x2112->2816, 30 layers cycled",
+            "us_per_layer": round(t * 1e6, 2), "trials_us": [round(x * 1e6, 2) for x in trials],
+            "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "step_bytes": int(step_bytes), "mean_distinct_experts": mean_uniq,
+            "launches_per_layer": 3}
+
+
+def bench_moe(args, torch, qd, prefill: bool):
+    """MoE layer (router int8 -> top-8 -> 8 routed + shared expert), 30 layers
+    cycled. Decode: batch 1, fp16 activations (16 distinct tokens per layer).
+    Prefill: one 128-token chunk of bf16 activations per step."""
+    E, H, I, Is, k = (MOE_SHAPE[n] for n in ("E", "H", "I", "Is", "k"))
+    layers, xs, T = build_moe(torch, qd, prefill, args.sets or MOE_SHAPE["layers"])
+    fns, step_bytes, mean_uniq = moe_steps(torch, qd, layers, xs, T, prefill)
+    secs, _ = Timer(torch).run(fns, args.steps, args.warmup)
+    t = secs / args.steps
+    tm, trials = median_time(fns, calls=max(MIN_CALLS, len(fns)))
     gbs = step_bytes / t / 1e9
     name = "c4 MoE prefill chunk" if prefill else "c3 MoE decode layer"
     return {"metric": "µs per MoE layer" + (" (128-token prefill chunk)" if prefill else " (decode, batch 1)"),
@@ -532,6 +623,7 @@ def bench_moe(args, torch, qd, prefill: bool):
                                    f"down {I}->{H}), router int8, top-{k}, shared expert "
                                    f"{H}->2x{Is}->{H}, {len(layers)} layers cycled, T={T}",
                        "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                       "median5_us": round(tm * 1e6, 2), "trials_us": [round(x * 1e6, 2) for x in trials],
                        "mean_distinct_experts": mean_uniq, "step_bytes": int(step_bytes),
                        "launches_per_layer": 3 if not prefill else 6},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
@@ -539,10 +631,20 @@ def bench_moe(args, torch, qd, prefill: bool):
             "cpu_baseline": None}
 
 
-def bench_stream(args, torch):
-    """Plain device copy (torch's copy kernel) and a read-mostly reduction over
-    2 GiB buffers: the practical HBM ceiling, and the known-size reference used
-    to scale the FETCH_SIZE / WRITE_SIZE counters."""
+def bench_stream(args, torch, qd):
+    """The read-only stream kernel (qd_stream_read) at the workloads' matrix sizes
+    and beyond, each cycled over >= 1 GB of buffers: the practical HBM read
+    ceiling. Also torch's device copy and a reduction over 2 GiB buffers (the
+    known-size reference used to scale the FETCH_SIZE / WRITE_SIZE counters)."""
+    sizes = [("c1 4096x4096", matrix_bytes(4096, 4096)), ("c2 down", matrix_bytes(4096, 14336)),
+             ("c2 gate+up", matrix_bytes(28672, 4096)), ("c5 matrix", matrix_bytes(28672, 8192)),
+             ("512 MiB", 1 << 29), ("2 GiB", 1 << 31)]
+    ceiling = []
+    for name, nb in sizes:
+        g, t = stream_ceiling(torch, qd, nb)
+        ceiling.append({"size": name, "bytes": nb, "GBps": round(g, 1), "us": round(t * 1e6, 3),
+                        "frac_of_hbm_peak": round(g / HBM_PEAK_GBS, 4)})
+        torch.cuda.empty_cache()
     n = 1 << 29  # fp32 elements = 2 GiB
     src = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
     dst = torch.empty_like(src)
@@ -568,7 +670,7 @@ def bench_stream(args, torch):
     torch.cuda.synchronize()
     red_s = e0.elapsed_time(e1) / 1e3 / reps
     nbytes = n * 4
-    return {"config": "stream", "bytes_per_buffer": nbytes, "reps": reps,
+    return {"config": "stream", "read_stream_kernel": ceiling, "bytes_per_buffer": nbytes, "reps": reps,
             "copy_GBps_read_plus_write": round(2 * nbytes / copy_s / 1e9, 1),
             "copy_us": round(copy_s * 1e6, 2),
             "reduce_GBps_read": round(nbytes / red_s / 1e9, 1),
@@ -599,7 +701,7 @@ def main():
     qd.lib()  # fail loudly if the HIP library is missing
 
     if args.config == "stream":
-        emit(bench_stream(args, torch))
+        emit(bench_stream(args, torch, qd))
         return
     if args.config in ("c1", "c2", "c5"):
         if args.config == "c1":
@@ -674,6 +776,21 @@ def main():
                          "bytes_per_launch": bytes_per_launch,
                          "avg_launch_us": round(launch_s * 1e6, 3)},
         }
+        # the practical ceiling at each projection's size: the read-only stream
+        # kernel over buffers of the matrix's bytes, cycled like the weights
+        for j, (K, N) in enumerate(shapes):
+            cg, _ = stream_ceiling(torch, qd, matrix_bytes(N, K, fmt=fmt))
+            ps = out["config"]["per_shape"][j]
+            ps["stream_GBps"] = round(cg, 1)
+            ps["pct_of_stream"] = round(100 * ps["gbs"] / cg, 1)
+            ps["pct_of_hbm_peak"] = round(100 * ps["gbs"] / HBM_PEAK_GBS, 1)
+            if j == dom:
+                out["roofline"]["stream_ceiling_GBps"] = round(cg, 1)
+                out["roofline"]["frac_of_stream"] = round(achieved / cg, 4)
+        torch.cuda.empty_cache()
+        if args.config == "c2" and fmt == "affine" and not args.no_moe:
+            # the metric's second half: µs per decode MoE layer (c3), same run
+            out["config"]["moe_decode"] = moe_decode_figure(torch, qd)
         if len(results) > 1:
             out["config"]["batch_sweep"] = [
                 {"batch": b, "GBps": round(rr["step_bytes"] * args.steps / rr["secs"] / 1e9, 1),
@@ -682,7 +799,7 @@ def main():
             v, done, el, thr = cpu_baseline_gemv(r["cpu_mats"], args.cpu_seconds)
             v1, done1, el1, _ = cpu_baseline_gemv(r["cpu_mats"], args.cpu_seconds / 4, threads=1)
             out["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": thr,
-                                   "kind": "oracle",
+                                   "kind": "oracle", "cpu_model": cpu_model(),
                                    "sample": f"{done} full step(s) of weight set 0 "
                                              f"({', '.join(f'{K}->{N}' for K, N in shapes)}, batch {batch}) "
                                              f"in {el:.1f} s, fp64 C oracle",

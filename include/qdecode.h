@@ -289,6 +289,18 @@ qd_status qattn_decode(const uint16_t* q, const uint16_t* k_new, const uint16_t*
                        int32_t pos, float scale, float* out,
                        void* workspace, size_t ws_bytes, qd_stream stream);
 
+/*
+ * Measurement: reads `bytes` bytes of device memory at buf once, as the
+ * GEMV reads its codes (16-byte buffer loads per lane, waves sweeping the
+ * buffer in the GEMV's interleaved order), and does nothing
+ * else. Its rate over buffers of a workload's size is the practical HBM read
+ * ceiling that the GEMV's achieved bandwidth is compared against. sink (4
+ * bytes of device memory, 16-byte aligned) is written (with 0x9E3779B9) only
+ * when the XOR of the words one lane loaded equals 0x9E3779B9.
+ * Asynchronous on stream.
+ */
+qd_status qd_stream_read(const void* buf, size_t bytes, uint32_t* sink, qd_stream stream);
+
 /* Human-readable name of a status. */
 const char* qd_status_string(qd_status status);
 
