@@ -12,6 +12,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
@@ -95,6 +96,16 @@ qd_status gemv_common(const char* fn, int bits, int fmt, int max_batch, const ui
                     fn);
 }
 
+// The activation field as an int: C callers may store any int in an enum
+// field, and reading an out-of-range value through the C++ enum type is
+// undefined, so the bytes are copied instead.
+int moe_act(const qd_moe_weights* w) {
+    int act;
+    static_assert(sizeof(act) == sizeof(w->act), "qd_act is int-sized");
+    std::memcpy(&act, &w->act, sizeof act);
+    return act;
+}
+
 qd_status check_moe(const char* fn, const qd_moe_weights* w) {
     if (!w) return fail(QD_ERR_INVALID_ARGUMENT, "%s: weights is NULL", fn);
     if (w->group_size != 64)
@@ -108,8 +119,8 @@ qd_status check_moe(const char* fn, const qd_moe_weights* w) {
                     w->I, w->I_shared);
     if (w->H > (1 << 20) || w->I > (1 << 20) || w->I_shared > (1 << 20))
         return fail(QD_ERR_UNSUPPORTED, "%s: H, I and I_shared are limited to 2^20", fn);
-    if (w->act != QD_GELU_ERF && w->act != QD_GELU_TANH)
-        return fail(QD_ERR_UNSUPPORTED, "%s: act %d", fn, (int)w->act);
+    if (moe_act(w) != QD_GELU_ERF && moe_act(w) != QD_GELU_TANH)
+        return fail(QD_ERR_UNSUPPORTED, "%s: act %d", fn, moe_act(w));
     CHECK_PTR(w->gu_q);
     CHECK_PTR(w->gu_s);
     CHECK_PTR(w->gu_b);
@@ -131,7 +142,7 @@ qd::MoeArgs moe_args(const qd_moe_weights* w) {
     m.H = w->H;
     m.I = w->I;
     m.Is = w->I_shared;
-    m.act = (int)w->act;
+    m.act = moe_act(w);
     m.gu_q = w->gu_q;
     m.dn_q = w->dn_q;
     m.sgu_q = w->sgu_q;
