@@ -6,14 +6,20 @@
 // path ("성능과 제약": affine 4-bit, group 64, w = s*q + b).
 //
 // Rounding w itself to bf16 would lose too much (8 significant bits), so
-// the matrix-core operand is the exact code: OR-ing a nibble into the low
-// mantissa of bf16 128.0 (0x4300) gives exactly 128 + q. Per group g of 64
-// inputs one v_mfma_f32_32x32x16_bf16 chain (4 x K=16) yields
-//     P_g[m][n] = sum_{k in g} X[m][k] (128 + q[n][k])        (fp32)
-// and the epilogue adds, in fp32,
-//     acc[m][n] += s[n][g] * P_g[m][n] + (b[n][g] - 128 s[n][g]) * Xsum_g[m]
-// with Xsum_g[m] = sum_{k in g} X[m][k], computed while X is staged.
-//
+// the matrix-core operand is the exact centred code (mfma.h): with
+// w = s (q - 8) + (b + 8 s), one v_mfma_f32_32x32x16_bf16 chain per group of
+// 64 inputs (4 x K=16) on the operand 16 (q - 8) yields
+//     P_g[m][n] = sum_{k in g} X[m][k] 16 (q[n][k] - 8)          (fp32)
+// and the epilogue adds
+//     acc[m][n] += (s[n][g] / 16) P_g[m][n] + (b[n][g] + 8 s[n][g]) Xsum_g[m]
+// with Xsum_g[m] = sum_{k in g} X[m][k], computed while X is staged: the
+// first term as an fp32 FMA per group, the second once per stage on the
+// matrix core from three-part bf16 splits of both factors, about as exact
+// as an fp32 product (the two terms cancel where weights sit near zero).
+// The products carry no offset, so the fp32 sums round in proportion to
+// |s (q - 8) x| and a weight at the centre contributes nothing (fp16
+// activations: the operand is q - 8 on an fp16 MFMA, scale s).
+
 // Tiling: a workgroup owns 128 rows (the whole chunk) x 64 output columns
 // with 8 waves: two column waves (32 columns each, all 128 rows as four 32x32
 // MFMA blocks) times four K-sets that take alternate groups of K; the K-sets'
@@ -58,13 +64,13 @@ struct ChunkArgs {
 
 // A workgroup owns MT = 32 MB WM rows (one row tile) and 64 columns. LDS
 // layout (dynamic): xs[2 buffers][SG groups][MT rows][XS_STRIDE] uint4, then
-// xsum[2][MT rows][SG groups] fp32, then (fp16 activations only) the same
-// sums transposed, xsumT[2][SG groups][MT rows].
+// the per-group row sums as bias-product parts (bias_row_parts),
+// xsum[2][MT rows][SG groups] uint2.
 template <int SG, int MT_, bool F16 = false>
 struct ChunkLds {
     static constexpr int MT = MT_;
     static constexpr int XS = SG * MT * XS_STRIDE;   // uint4 per buffer
-    static constexpr size_t bytes = 2 * (size_t)XS * 16 + (F16 ? 4 : 2) * SG * MT * 4;
+    static constexpr size_t bytes = 2 * (size_t)XS * 16 + 2 * SG * MT * 8;
 };
 
 // Group visited at step g (clamped to the last step) when a workgroup starts
@@ -104,8 +110,7 @@ struct StageIO {
         }
     }
 
-    __device__ static __forceinline__ void store(uint4* xs, float* xsum, const uint4 (&xr)[SG][XPT],
-                                                 float* xsumT = nullptr) {
+    __device__ static __forceinline__ void store(uint4* xs, uint2* xsum, const uint4 (&xr)[SG][XPT]) {
         // rows past M hold copies of row M - 1 (the loads clamp); they only
         // feed output rows that are never stored
         const int t = threadIdx.x;
@@ -131,8 +136,7 @@ struct StageIO {
                 }
             }
             acc = seg_sum<TPR>(acc);   // the TPR adjacent lanes of the row
-            xsum[r * SG + gi] = acc;   // every lane of the row stores the same sum
-            if constexpr (F16) xsumT[gi * MT + r] = acc;
+            xsum[r * SG + gi] = bias_row_parts(acc);   // every lane of the row stores the same
         }
     }
 };
@@ -173,10 +177,10 @@ __device__ __forceinline__ int opaque(int v) {
 // XD = stages of X held in registers ahead of LDS: with 1, the next stage is
 // read while the current one is consumed; with 2 (small row tiles, whose
 // stages hold little matrix work) the stage after that is also in flight.
-// F16: fp16 activations; the codes enter an fp16 MFMA as 1024 + q and the
-// offset part -1024 s Xsum is added in fp32 per group (in the bias MFMA's
-// 16-bit split it would lose too much next to the result); bf16 activations
-// fold -128 s into the bias MFMA.
+// F16: fp16 activations on an fp16 MFMA (operand q - 8, scale s); bf16
+// activations take the operand 16 (q - 8) and scale s / 16. Either way the
+// bias term (b + 8 s) Xsum, of the size of the result, runs on the matrix
+// core once per stage.
 template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
@@ -190,8 +194,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     using IO = StageIO<SG, MT, 64 * WS * NKS, F16>;
     extern __shared__ uint4 smem[];
     uint4* xs_raw = smem;                                    // [2][XS]
-    float* xsum_raw = (float*)(smem + 2 * L::XS);            // [2][MT][SG]
-    float* xsumT_raw = xsum_raw + 2 * SG * MT;               // [2][SG][MT] (F16)
+    uint2* xsum_raw = (uint2*)(smem + 2 * L::XS);            // [2][MT][SG]
     const int RT = (a.M + MT - 1) / MT;                      // row tiles
     const int b = blockIdx.x;
     const int ct = (b / (8 * RT)) * 8 + b % 8;
@@ -236,16 +239,15 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     // stage parity picks the slot, and rounds hold an even number of stages)
     uint4 xr[XD][SG][IO::XPT];
     IO::load(a, m0, 0, G, rot, xr[0]);
-    IO::store(xs_raw, xsum_raw, xr[0], xsumT_raw);
+    IO::store(xs_raw, xsum_raw, xr[0]);
     if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
     __syncthreads();
 
     // one group (step g, slot e): MFMAs into P, then acc += s P, then the
     // slot is refilled with step g + D. xs: this lane's A-operand row (row
-    // 32 MB wm + l32, k-half h) of the group. The bias part, (b - 128 s) Xsum,
+    // 32 MB wm + l32, k-half h) of the group. The bias part, (b + 8 s) Xsum,
     // is added per stage on the matrix core (bias_mfma below).
-    auto group = [&](const int g, auto ec, const uint4* xs, const float* xt)
-                     __attribute__((always_inline)) {
+    auto group = [&](const int g, auto ec, const uint4* xs) __attribute__((always_inline)) {
         constexpr int e = decltype(ec)::value;
         // the 4 steps' B operands, then the row blocks PH at a time (fewer
         // live accumulators than all MB at once)
@@ -254,8 +256,9 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         bf16x8_t bfrag[4];
 #pragma unroll
         for (int stp = 0; stp < 4; ++stp)
-            bfrag[stp] = __builtin_bit_cast(bf16x8_t, codes_to_16n(wv[stp], F16 ? 0x64006400u : 0x43004300u));
-        const float sf = h2f((uint16_t)bs[e]);
+            bfrag[stp] = __builtin_bit_cast(bf16x8_t, F16 ? codes_centred_f16(wv[stp])
+                                                          : codes_centred_bf16x16(wv[stp]));
+        const float sf = h2f((uint16_t)bs[e]) * (F16 ? 1.f : 0.0625f);
 #pragma unroll
         for (int m0b = 0; m0b < MB; m0b += PH) {
             floatx16 P[PH];
@@ -277,26 +280,10 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
                             __builtin_bit_cast(bf16x8_t, av), bfrag[stp], P[pb], 0, 0, 0);
                 }
             }
-            if constexpr (F16) {
-                // rows 8 (i / 4) + 4 h + i % 4 of the block: quarter i / 4
-                const float mo = -1024.f * sf;
 #pragma unroll
-                for (int pb = 0; pb < PH; ++pb)
+            for (int pb = 0; pb < PH; ++pb)
 #pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const float4 xq = *(const float4*)(xt + 32 * (m0b + pb) + 8 * qq);
-                        const float xv[4] = {xq.x, xq.y, xq.z, xq.w};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[m0b + pb][4 * qq + j] = fmaf(sf, P[pb][4 * qq + j],
-                                                             fmaf(mo, xv[j], acc[m0b + pb][4 * qq + j]));
-                    }
-            } else {
-#pragma unroll
-                for (int pb = 0; pb < PH; ++pb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[m0b + pb][i] = fmaf(sf, P[pb][i], acc[m0b + pb][i]);
-            }
+                for (int i = 0; i < 16; ++i) acc[m0b + pb][i] = fmaf(sf, P[pb][i], acc[m0b + pb][i]);
             __builtin_amdgcn_sched_barrier(0);   // keep the passes apart (registers)
         }
         // finish this group's epilogue here: left alone, the compiler sinks it
@@ -313,51 +300,30 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Bias of this wave's groups of one stage: acc += sum_g Xsum_g[m] (b_g -
-    // 128 s_g)[n] as one MFMA per row block. Both factors are split into bf16
-    // hi + lo parts and the K = 16 slots carry the four cross products: lane
-    // half h supplies slots 8h..8h+7 as A = (x_h, x_h) over 4 group slots,
-    // with x_0 = hi, x_1 = lo, and B = (hi, lo), so the slots sum to
-    // (xhi + xlo)(bhi + blo). Each product is exact in fp32; the parts keep 16
-    // significant bits. Group slot j < JS is the wave's j-th group of the
-    // stage; slots JS..3 are zero.
-    auto bias_mfma = [&](const int st, auto sjc, auto checked, const float* xsum)
+    // Bias of this wave's groups of one stage: acc += sum_g Xsum_g[m] (b_g +
+    // 8 s_g)[n] as one MFMA per row block, both factors as three bf16 parts
+    // (mfma.h: six exact cross products, within 2^-25 of the fp32 product).
+    // Lane half h carries the wave's group j = h of the stage (JS = 2); with
+    // one group per wave (JS = 1) half 1 has B = 0. xsum: this lane's staged
+    // parts of that group for row 0 of the tile.
+    static_assert(JS == 1 || JS == 2, "bias slots");
+    auto bias_mfma = [&](const int st, auto sjc, auto checked, const uint2* xsum)
                          __attribute__((always_inline)) {
         constexpr int sj = decltype(sjc)::value;
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        float bv[JS];
 #pragma unroll
         for (int j = 0; j < JS; ++j) {
             const int e = sj * JS + j;
-            const float sf = h2f((uint16_t)bs[e]);
-            bv[j] = h2f((uint16_t)bb[e]) - (F16 ? 0.f : 128.f * sf);
+            bv[j] = fmaf(8.f, h2f((uint16_t)bs[e]), h2f((uint16_t)bb[e]));
             if constexpr (decltype(checked)::value)
                 if (st * SG + NKS * j + ks >= G) bv[j] = 0.f;
         }
-        auto split = [](float a0, float a1, uint32_t& hi, uint32_t& lo) __attribute__((always_inline)) {
-            const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
-            hi = __builtin_bit_cast(uint32_t, hv);
-            const bf16x2_t lv = {(__bf16)(a0 - __uint_as_float(hi << 16)),
-                                 (__bf16)(a1 - __uint_as_float(hi & 0xFFFF0000u))};
-            lo = __builtin_bit_cast(uint32_t, lv);
-        };
-        uint32_t bh01, bl01, bh23 = 0, bl23 = 0;
-        split(bv[0], JS > 1 ? bv[1] : 0.f, bh01, bl01);
-        if constexpr (JS > 2) split(bv[2], bv[3], bh23, bl23);
-        const bf16x8_t bfrag = __builtin_bit_cast(bf16x8_t, make_uint4(bh01, bh23, bl01, bl23));
+        const float bsel = JS == 2 ? (h ? bv[JS - 1] : bv[0]) : (h ? 0.f : bv[0]);
+        const bf16x8_t bfrag = __builtin_bit_cast(bf16x8_t, bias_b_operand(bsel));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            // this set's groups of the row: NKS j + ks (read by address: a
-            // select on ks would become branches)
-            const float* xrow = xsum + (32 * MB * wm + 32 * mb + l32) * SG;
-            float xg[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < JS; ++j) xg[j] = xrow[NKS * j];
-            uint32_t xh01, xl01, xh23 = 0, xl23 = 0;
-            split(xg[0], JS > 1 ? xg[1] : 0.f, xh01, xl01);
-            if constexpr (JS > 2) split(xg[2], xg[3], xh23, xl23);
-            const uint32_t a01 = h ? xl01 : xh01, a23 = h ? xl23 : xh23;
-            const bf16x8_t afrag = __builtin_bit_cast(bf16x8_t, make_uint4(a01, a23, a01, a23));
+            const uint2 r = xsum[(32 * MB * wm + 32 * mb + l32) * SG];
+            const bf16x8_t afrag = __builtin_bit_cast(bf16x8_t, bias_a_operand(r));
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[mb], 0, 0, 0);
         }
     };
@@ -372,27 +338,22 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         // stage st + 2 while slot (st + 1) % 2 holds stage st + 1
         constexpr int ld = XD == 1 ? 0 : sj % 2, sv = XD == 1 ? 0 : (sj + 1) % 2;
         IO::load(a, m0, (st + XD) * SG, G, rot, xr[ld]);
-        bias_mfma(st, sjc, checked, xsum_raw + opaque(buf * SG * MT + ks));
+        bias_mfma(st, sjc, checked, xsum_raw + opaque(buf * SG * MT + ks + (JS == 2 ? NKS * h : 0)));
         // group j of this wave is stage group NKS j + ks
         const uint4* xs = xs_raw + opaque(buf * L::XS + ks * MT * XS_STRIDE +
                                           (32 * MB * wm + l32) * XS_STRIDE + 4 * h);
-        // fp16 only: this lane's accumulator rows of the row sums, group ks
-        const float* xt = F16 ? xsumT_raw + opaque(buf * SG * MT + ks * MT + 32 * MB * wm + 4 * h)
-                              : nullptr;
         static_for<0, JS>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
             const int g = st * SG + NKS * j + ks;
             constexpr std::integral_constant<int, sj * JS + j> ec{};
             const uint4* xsj = xs + NKS * j * MT * XS_STRIDE;
-            const float* xtj = F16 ? xt + NKS * j * MT : nullptr;
             if constexpr (decltype(checked)::value) {
-                if (g < G) group(g, ec, xsj, xtj);
+                if (g < G) group(g, ec, xsj);
             } else {
-                group(g, ec, xsj, xtj);
+                group(g, ec, xsj);
             }
         });
-        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr[sv],
-                  xsumT_raw + (buf ^ 1) * SG * MT);
+        IO::store(xs_raw + (buf ^ 1) * L::XS, xsum_raw + (buf ^ 1) * SG * MT, xr[sv]);
         __syncthreads();
     };
 

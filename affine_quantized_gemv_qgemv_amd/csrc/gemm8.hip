@@ -9,17 +9,17 @@
 // experts x hidden) rather than a GEMV. The 8-bit router format is the
 // affine format of the decode path with 8-bit codes.
 //
-// The matrix-core operand is the exact code. For f16 activations a code byte
-// placed in the low mantissa of f16 1024.0 (0x6400) gives 1024 + q exactly,
-// and one v_mfma_f32_32x32x16_f16 per 16 inputs yields
-//     P = sum_k x (1024 + q).
-// bf16 has too few mantissa bits for 1024 + q, so for bf16 activations the
-// code is split into nibbles, each exact as 128 + nibble (0x4300), and two
-// bf16 MFMAs yield P_lo + 16 P_hi = sum_k x q + 2176 Xsum. A third MFMA
-// against an all-ones operand gives the row sums Xsum directly in the
-// accumulator layout. Per group, in fp32:
-//     acc += s P' + (b - off s) Xsum,   off = 1024 (f16) or 2176 (bf16).
-//
+// The matrix-core operand is the exact centred code q - 128 (w = s (q - 128)
+// + (b + 128 s)): for f16 activations a code byte in the low mantissa of f16
+// 1024.0 gives 1024 + q, and one v_pk_add_f16 with -1152 leaves q - 128; for
+// bf16 activations the code XOR 0x80 is the signed byte q - 128, converted
+// exactly (mfma.h). One MFMA per 16 inputs yields P = sum_k x (q - 128), a
+// second against an all-ones operand gives the row sums Xsum in the
+// accumulator layout, and per group, in fp32,
+//     acc += s P + (b + 128 s) Xsum.
+// The products carry no offset, so the sums round in proportion to the
+// weights' own size.
+
 // Tiling: a workgroup owns 32 tokens x 32 outputs and has 8 waves that take
 // alternate groups of K (wave w: groups w, w + 8, ...), each loading up to
 // four of its groups at once before using them; the 8 partial sums are added
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
     const uint16_t* xrow = a.x + (int64_t)tc * a.K + 32 * h;          // k = 32h.. of group 0
     const uint16_t* srow = a.s + (int64_t)nc * G;
     const uint16_t* brow = a.b + (int64_t)nc * G;
-    const uint32_t magic = in_vgpr(XF == 0 ? 0x64646464u : 0x43434343u);
+    const uint32_t magic = in_vgpr(0x64646464u);   // fp16 1024 in the bytes the codes skip
     const uint32_t one2 = XF == 0 ? 0x3C003C00u : 0x3F803F80u;   // (1.0, 1.0)
 
     floatx16 acc;
@@ -92,11 +92,10 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
             if (g0 + G8_WAVES * j >= G) break;   // uniform
             const uint32_t wv[8] = {wb[j][0].x, wb[j][0].y, wb[j][0].z, wb[j][0].w,
                                     wb[j][1].x, wb[j][1].y, wb[j][1].z, wb[j][1].w};
-            floatx16 P, Ph, X1;
+            floatx16 P, X1;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 P[i] = 0.f;
-                Ph[i] = 0.f;
                 X1[i] = 0.f;
             }
             // step st: k = 32h + 8st + (0..7) = bytes of words 8h + 2st, 8h + 2st + 1
@@ -105,43 +104,29 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
                 const uint32_t w0 = wv[2 * st], w1 = wv[2 * st + 1];
                 const uint4 ones = make_uint4(one2, one2, one2, one2);
                 if constexpr (XF == 0) {
-                    const uint4 bq = make_uint4(byte_pair(w0, magic, 0x04010400u),
-                                                byte_pair(w0, magic, 0x04030402u),
-                                                byte_pair(w1, magic, 0x04010400u),
-                                                byte_pair(w1, magic, 0x04030402u));
+                    const uint4 bq = make_uint4(pk_addh(byte_pair(w0, magic, 0x04010400u), kNeg1152),
+                                                pk_addh(byte_pair(w0, magic, 0x04030402u), kNeg1152),
+                                                pk_addh(byte_pair(w1, magic, 0x04010400u), kNeg1152),
+                                                pk_addh(byte_pair(w1, magic, 0x04030402u), kNeg1152));
                     const f16x8_t av = __builtin_bit_cast(f16x8_t, xa[j][st]);
                     P = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8_t, bq), P,
                                                                0, 0, 0);
                     X1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(f16x8_t, ones),
                                                                 X1, 0, 0, 0);
                 } else {
-                    const uint32_t l0 = w0 & 0x0F0F0F0Fu, h0 = (w0 >> 4) & 0x0F0F0F0Fu;
-                    const uint32_t l1 = w1 & 0x0F0F0F0Fu, h1 = (w1 >> 4) & 0x0F0F0F0Fu;
-                    const uint4 bl = make_uint4(byte_pair(l0, magic, 0x04010400u),
-                                                byte_pair(l0, magic, 0x04030402u),
-                                                byte_pair(l1, magic, 0x04010400u),
-                                                byte_pair(l1, magic, 0x04030402u));
-                    const uint4 bh = make_uint4(byte_pair(h0, magic, 0x04010400u),
-                                                byte_pair(h0, magic, 0x04030402u),
-                                                byte_pair(h1, magic, 0x04010400u),
-                                                byte_pair(h1, magic, 0x04030402u));
+                    const uint2 c0 = bytes_centred_bf16(w0), c1 = bytes_centred_bf16(w1);
+                    const uint4 bq = make_uint4(c0.x, c0.y, c1.x, c1.y);
                     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[j][st]);
-                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bl), P,
+                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bq), P,
                                                                 0, 0, 0);
-                    Ph = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bh), Ph,
-                                                                 0, 0, 0);
                     X1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, ones),
                                                                  X1, 0, 0, 0);
                 }
             }
             const float sf = h2f(sv[j]);
-            const float off = XF == 0 ? 1024.f : 2176.f;
-            const float bf = h2f(bv[j]) - off * sf;
+            const float bf = fmaf(128.f, sf, h2f(bv[j]));   // b + 128 s
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pc = XF == 0 ? P[i] : fmaf(16.f, Ph[i], P[i]);
-                acc[i] = fmaf(bf, X1[i], fmaf(sf, pc, acc[i]));
-            }
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf(bf, X1[i], fmaf(sf, P[i], acc[i]));
         }
     }
 

@@ -30,9 +30,118 @@ __device__ __forceinline__ uint4 codes_to_16n(uint32_t w, uint32_t magic) {
     return make_uint4(p01, p23, p45, p67);
 }
 
+// ---------------------------------------------------------------------------
+// Centred codes as matrix-core operands: w = s (q - c) + (b + c s), with the
+// operand holding q - c exactly, so the fp32 products and sums carry no
+// offset and a weight at the centre contributes exactly zero.
+//  * fp16 operands: the code in the low mantissa of fp16 1024.0 is 1024 + q;
+//    one v_pk_add_f16 with -(1024 + c) leaves q - c (exact in fp16).
+//  * bf16 operands (no packed bf16 add on gfx950): a 4-bit code XOR 8, read
+//    as a signed nibble, is q - 8; placed in the top half of a byte it reads
+//    as the signed byte 16 (q - 8), which v_cvt_f32_i32 (SDWA byte select,
+//    sign-extended) converts exactly and v_cvt_pk_bf16_f32 packs exactly
+//    (|16 (q - 8)| <= 128 needs 4 significant bits). The factor 16 is taken
+//    out of the scale (an exact power of two). An 8-bit code XOR 0x80 is the
+//    signed byte q - 128, exact in bf16 (at most 8 significant bits).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};   // exact for these integers
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte I of v as a signed integer, in fp32.
+template <int I>
+__device__ __forceinline__ float sbyte(uint32_t v) {
+    return (float)(int8_t)(v >> (8 * I));
+}
+
+// 8 codes of one word, natural k order, as fp16 q - 8.
+__device__ __forceinline__ uint4 codes_centred_f16(uint32_t w) {
+    const uint4 p = codes_to_16n(w, 0x64006400u);
+    return make_uint4(pk_addh(p.x, kNeg1032), pk_addh(p.y, kNeg1032), pk_addh(p.z, kNeg1032),
+                      pk_addh(p.w, kNeg1032));
+}
+
+// 8 codes of one word, natural k order, as bf16 16 (q - 8).
+__device__ __forceinline__ uint4 codes_centred_bf16x16(uint32_t w) {
+    const uint32_t c = w ^ 0x88888888u;
+    const uint32_t lo = (c << 4) & 0xF0F0F0F0u;   // codes 0, 2, 4, 6 in the top of bytes 0..3
+    const uint32_t hi = c & 0xF0F0F0F0u;          // codes 1, 3, 5, 7
+    return make_uint4(pk_bf16(sbyte<0>(lo), sbyte<0>(hi)), pk_bf16(sbyte<1>(lo), sbyte<1>(hi)),
+                      pk_bf16(sbyte<2>(lo), sbyte<2>(hi)), pk_bf16(sbyte<3>(lo), sbyte<3>(hi)));
+}
+
+// The same in the k order [0, 4, 1, 5, 2, 6, 3, 7] (fp16: the magic in a VGPR).
+__device__ __forceinline__ uint4 codes_centred_f16_p(uint32_t w, uint32_t magic) {
+    return make_uint4(pk_addh((w & 0x000F000Fu) | magic, kNeg1032),
+                      pk_addh(((w >> 4) & 0x000F000Fu) | magic, kNeg1032),
+                      pk_addh(((w >> 8) & 0x000F000Fu) | magic, kNeg1032),
+                      pk_addh(((w >> 12) & 0x000F000Fu) | magic, kNeg1032));
+}
+
+__device__ __forceinline__ uint4 codes_centred_bf16x16_p(uint32_t w) {
+    const uint32_t c = w ^ 0x88888888u;
+    const uint32_t lo = (c << 4) & 0xF0F0F0F0u;
+    const uint32_t hi = c & 0xF0F0F0F0u;
+    return make_uint4(pk_bf16(sbyte<0>(lo), sbyte<2>(lo)), pk_bf16(sbyte<0>(hi), sbyte<2>(hi)),
+                      pk_bf16(sbyte<1>(lo), sbyte<3>(lo)), pk_bf16(sbyte<1>(hi), sbyte<3>(hi)));
+}
+
+// 4 8-bit codes of one word, natural order, as two bf16 pairs q - 128.
+__device__ __forceinline__ uint2 bytes_centred_bf16(uint32_t w) {
+    const uint32_t c = w ^ 0x80808080u;
+    return make_uint2(pk_bf16(sbyte<0>(c), sbyte<1>(c)), pk_bf16(sbyte<2>(c), sbyte<3>(c)));
+}
+
+// ---------------------------------------------------------------------------
+// Bias products on the matrix core: acc[m][n] += X[m] V[n] with fp32 factors
+// (a group's row sum and its b + c s). With centred codes this term cancels
+// against s P where weights sit near zero, so it must be about as exact as
+// an fp32 product. Each factor is split into three bf16 parts a = hi + mid +
+// lo (each part the rounding of what the earlier ones leave; every residual
+// is exact in fp32, so the parts hold 24 significant bits and miss a by at
+// most 2^-27 |a|). The six cross products of weight down to 2^-18 fill six
+// K slots of one lane half: A = (xh, xm, xl, xh, xm, xh, 0, 0) against
+// B = (vh, vh, vh, vm, vm, vl, 0, 0); the dropped ones (xm vl, xl vm, xl vl)
+// are below 2^-26 |x v|. Each product is exact in fp32.
+// ---------------------------------------------------------------------------
+struct Bf16x3 {
+    uint32_t h, m, l;   // bf16 bits in the low half
+};
+
+__device__ __forceinline__ uint32_t bf16_bits(float a) {
+    return __builtin_bit_cast(uint16_t, (__bf16)a);   // round to nearest even
+}
+
+__device__ __forceinline__ Bf16x3 split3_bf16(float a) {
+    const uint32_t h = bf16_bits(a);
+    const float r1 = a - __uint_as_float(h << 16);
+    const uint32_t m = bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float(m << 16);
+    return {h, m, bf16_bits(r2)};
+}
+
+// Row factor as staged in LDS: (hi | mid << 16, lo | hi << 16).
+__device__ __forceinline__ uint2 bias_row_parts(float x) {
+    const Bf16x3 p = split3_bf16(x);
+    return make_uint2(p.h | (p.m << 16), p.l | (p.h << 16));
+}
+
+// A operand of one lane half from the staged parts: (xh, xm, xl, xh, xm, xh, 0, 0).
+__device__ __forceinline__ uint4 bias_a_operand(uint2 r) {
+    return make_uint4(r.x, r.y, (r.x >> 16) | (r.x << 16), 0u);
+}
+
+// B operand of one lane half: (vh, vh, vh, vm, vm, vl, 0, 0).
+__device__ __forceinline__ uint4 bias_b_operand(float v) {
+    const Bf16x3 p = split3_bf16(v);
+    return make_uint4(p.h | (p.h << 16), p.h | (p.m << 16), p.m | (p.l << 16), 0u);
+}
+
 __device__ __forceinline__ float bf16_pair_sum(uint32_t v, float acc) {
     // v_dot2_f32_bf16 with (1, 1): adds both bf16 halves into an fp32 sum
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), ones, acc, false);
 }

@@ -200,16 +200,12 @@ __device__ __forceinline__ int opaque_i(int v) {
     return r;
 }
 
-// 8 codes of one word -> 16-bit (offset + q) in the k order
-// [0, 4, 1, 5, 2, 6, 3, 7]: one v_and_or_b32 per pair (magic = the offset's
-// bit pattern in both halves, bf16 128.0 or fp16 1024.0, kept in a VGPR).
-// The activations are staged in LDS in the same order (perm8 below).
-__device__ __forceinline__ uint4 codes_to_16p(uint32_t w, uint32_t magic) {
-    return make_uint4((w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
-                      ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic);
-}
+// The codes enter the matrix core centred (mfma.h): fp16 q - 8 or bf16
+// 16 (q - 8), in the k order [0, 4, 1, 5, 2, 6, 3, 7] (one v_and_or_b32 and
+// one v_pk_add_f16 per pair on the fp16 path). The activations are staged in
+// LDS in the same order (perm8 below).
 
-// 8 16-bit values e0..e7 -> e0 e4 e1 e5 e2 e6 e3 e7 (matches codes_to_16p).
+// 8 16-bit values e0..e7 -> e0 e4 e1 e5 e2 e6 e3 e7 (the codes' order).
 __device__ __forceinline__ uint4 perm8(uint4 v) {
     // v_perm_b32(src0, src1, sel): selector bytes 0..3 pick src1's bytes, 4..7 src0's
     return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
@@ -226,9 +222,10 @@ __device__ __forceinline__ uint4 perm8(uint4 v) {
 // sums, so each activation byte is fetched once per workgroup rather than
 // once per wave. Each wave keeps its codes, scales and biases XD groups
 // ahead in a register ring. Per group a wave runs one MFMA chain per
-// activation plane and adds s P; the bias term, (b - off s) Xsum, is added
-// once per stage on the matrix core.
+// activation plane on the centred codes and adds s P (s / 16 for bf16); the
+// bias term, (b + 8 s) Xsum, is added once per stage on the matrix core.
 constexpr int XSG = 4;       // groups per stage
+static_assert(XSG == 4, "the stage bias runs two groups per MFMA, two MFMAs");
 constexpr int XD = 4;        // groups of codes in flight per wave (whole stages)
 constexpr int XPF = 1;       // stages of activations in flight (1 or 2)
 constexpr int GU_WAVES = 4;  // gate+up workgroup: 2 gate + 2 up waves
@@ -238,16 +235,16 @@ constexpr int DN_WAVES = 4;  // down workgroup: 4 column tiles
 constexpr int XWPE = 2;
 
 // LDS: [2 buffers][PLANES][XSG groups][32 rows][XS_STRIDE] uint4, then the
-// per-group row sums (over the planes) twice, as xsum [2 buffers][32 rows]
-// [XSG] and xsumT [2 buffers][XSG][32 rows] fp32. NW waves stage: TPG =
-// NW / 2 threads share a (row, group) and each holds UPT = 8 / TPG of its
-// 16-byte chunks.
+// per-group row sums (over the planes) as bias-product parts
+// (bias_row_parts), xsum [2 buffers][32 rows][XSG] uint2.
+// NW waves stage: TPG = NW / 2 threads share a (row, group) and each holds
+// UPT = 8 / TPG of its 16-byte chunks.
 template <int PLANES, bool F16, int NW>
 struct XStage {
     static constexpr int PER = XSG * 32 * XS_STRIDE;   // uint4 per plane per buffer
     static constexpr int BUF = PLANES * PER;
-    static constexpr int SUMS = 2 * 32 * XSG;          // floats per copy (both buffers)
-    static constexpr int LDS_UINT4 = 2 * BUF + (2 * SUMS) / 4;
+    static constexpr int SUMS = 2 * 32 * XSG;          // uint2 (both buffers)
+    static constexpr int LDS_UINT4 = 2 * BUF + SUMS / 2;
     static constexpr int TPG = NW / 2;
     static constexpr int UPT = 8 / TPG;
     static_assert(TPG * XSG * 32 == 64 * NW, "staging split");
@@ -269,7 +266,7 @@ struct XStage {
             }
         }
     }
-    __device__ static __forceinline__ void store(uint4* buf, float* xsum, const uint4 (&r)[PLANES][UPT]) {
+    __device__ static __forceinline__ void store(uint4* buf, uint2* xsum, const uint4 (&r)[PLANES][UPT]) {
         const int rr = threadIdx.x / (TPG * XSG), part = threadIdx.x % (TPG * XSG);
         const int gi = part / TPG, c = UPT * (part % TPG);
         float acc = 0.f;
@@ -287,9 +284,8 @@ struct XStage {
             }
         }
         acc = seg_sum<TPG>(acc);   // the TPG adjacent lanes of (row, group)
-        // the TPG threads of (row, group) store the same sum
-        xsum[rr * XSG + gi] = acc;
-        xsum[SUMS + gi * 32 + rr] = acc;
+        // the TPG threads of (row, group) store the same parts
+        xsum[rr * XSG + gi] = bias_row_parts(acc);
     }
 };
 
@@ -320,31 +316,24 @@ struct CodeRing {
 
 // Streams the G groups of a wave's weight row against the staged activation
 // planes: acc (D layout, 32 rows x this lane's column) += sum over groups of
-// s (P_g - off Xsum_g) + b Xsum_g. The first part runs in fp32 per group (P_g
-// and off Xsum_g nearly cancel, so it needs full precision); b Xsum_g, of the
-// size of the result, runs once per stage on the matrix core. NQ = row
-// quarters (8 rows) that hold data: the per-group scaling skips the others. Whole rounds of XD groups run with no
+// s P_g + (b + 8 s) Xsum_g, with P_g the group's product on the centred codes
+// (s / 16 on the bf16 path, whose operand is 16 (q - 8)). The first part
+// runs in fp32 per group; the second, once per stage on the matrix core. NQ =
+// row quarters (8 rows) that hold data: the per-group scaling skips the
+// others. Whole rounds of XD groups run with no
 // data-dependent exits (an exit inside a round would make the compiler wait
 // for every load in flight where the paths join); the last partial round runs
 // with checks.
 template <int PLANES, bool F16, int NW, int NQ>
 __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t* const (&row)[PLANES],
-                                              CodeRing<XD>& ring, float off, floatx16& acc) {
+                                              CodeRing<XD>& ring, floatx16& acc) {
     using XS = XStage<PLANES, F16, NW>;
     constexpr int SPR = XD / XSG;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, l32 = lane & 31;
-    float* xsum_raw = (float*)(lds + 2 * XS::BUF);
+    uint2* xsum_raw = (uint2*)(lds + 2 * XS::BUF);
     const int NS = (G + XSG - 1) / XSG;
-    const uint32_t magic = in_vgpr(F16 ? 0x64006400u : 0x43004300u);
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    auto split = [](float a0, float a1, uint32_t& hi, uint32_t& lo) __attribute__((always_inline)) {
-        const bf16x2_t hv = {(__bf16)a0, (__bf16)a1};
-        hi = __builtin_bit_cast(uint32_t, hv);
-        const bf16x2_t lv = {(__bf16)(a0 - __uint_as_float(hi << 16)),
-                             (__bf16)(a1 - __uint_as_float(hi & 0xFFFF0000u))};
-        lo = __builtin_bit_cast(uint32_t, lv);
-    };
+    const uint32_t magic = in_vgpr(0x64006400u);   // fp16 1024 (fp16 path)
 
     // activations run XPF stages ahead. XPF = 2: register set st & 1 receives
     // stage st + 2 while set (st + 1) & 1 holds stage st + 1 until it is
@@ -362,32 +351,24 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
         auto& xin = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 1) return xr1; else return xr0; }();
         auto& xout = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 0) return xr1; else return xr0; }();
         XS::load(row, (st + XPF) * XSG, G, xin);
-        // bias of the stage's groups as one MFMA: factors split into bf16
-        // hi + lo; lane half h supplies K slots 8h..8h+7 as A = (x_h, x_h)
-        // over the 4 groups (x_0 = hi, x_1 = lo) and B = (hi, lo), so the
-        // slots sum to (xhi + xlo)(bhi + blo), each product exact in fp32
+        // bias of the stage's groups as two MFMAs (groups 2p + h on lane
+        // half h), both factors as three bf16 parts (mfma.h: six exact cross
+        // products per group, within 2^-25 of the fp32 product)
         {
             float bv[4];
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                bv[gi] = h2f((uint16_t)ring.b[sj * XSG + gi]);
+            for (int gi = 0; gi < 4; ++gi) {   // b + 8 s
+                bv[gi] = fmaf(8.f, h2f((uint16_t)ring.s[sj * XSG + gi]), h2f((uint16_t)ring.b[sj * XSG + gi]));
                 if constexpr (chk)
                     if (st * XSG + gi >= G) bv[gi] = 0.f;
             }
-            uint32_t bh01, bl01, bh23, bl23;
-            split(bv[0], bv[1], bh01, bl01);
-            split(bv[2], bv[3], bh23, bl23);
-            const float4 xv =
-                *(const float4*)(xsum_raw + buf * 32 * XSG + opaque_i(l32 * XSG));
-            uint32_t xh01, xl01, xh23, xl23;
-            split(xv.x, xv.y, xh01, xl01);
-            split(xv.z, xv.w, xh23, xl23);
-            const uint32_t a01 = h ? xl01 : xh01, a23 = h ? xl23 : xh23;
-            acc = mfma16<false>(make_uint4(a01, a23, a01, a23), make_uint4(bh01, bh23, bl01, bl23), acc);
+            const uint2* xp = xsum_raw + buf * 32 * XSG + opaque_i(l32 * XSG + h);
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                acc = mfma16<false>(bias_a_operand(xp[2 * p]),
+                                    bias_b_operand(h ? bv[2 * p + 1] : bv[2 * p]), acc);
         }
         const uint4* xs = lds + opaque_i(buf * XS::BUF + l32 * XS_STRIDE + 4 * h);
-        // row sums in the accumulator layout: rows 8 q + 4 h + (0..3) of group gi
-        const float* xt = xsum_raw + opaque_i(XS::SUMS + buf * 32 * XSG + 4 * h);
         // groups in pairs: two independent MFMA chains interleave on the matrix
         // core (one chain alone would wait on each MFMA's result)
         static_for<0, XSG / 2>([&](auto pc) __attribute__((always_inline)) {
@@ -406,29 +387,22 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
             const uint32_t w1[4] = {ring.q[d1].x, ring.q[d1].y, ring.q[d1].z, ring.q[d1].w};
 #pragma unroll
             for (int stp = 0; stp < 4; ++stp) {
-                const uint4 b0 = codes_to_16p(w0[stp], magic);
-                const uint4 b1 = codes_to_16p(w1[stp], magic);
+                const uint4 b0 = F16 ? codes_centred_f16_p(w0[stp], magic) : codes_centred_bf16x16_p(w0[stp]);
+                const uint4 b1 = F16 ? codes_centred_f16_p(w1[stp], magic) : codes_centred_bf16x16_p(w1[stp]);
 #pragma unroll
                 for (int pl = 0; pl < PLANES; ++pl) {
                     P0 = mfma16<F16>(xs[pl * XS::PER + g0i * 32 * XS_STRIDE + stp], b0, P0);
                     P1 = mfma16<F16>(xs[pl * XS::PER + (g0i + 1) * 32 * XS_STRIDE + stp], b1, P1);
                 }
             }
-            auto epilogue = [&](const floatx16& P, int gi, int d) __attribute__((always_inline)) {
-                const float sf = h2f((uint16_t)ring.s[d]);
-                const float mo = -off * sf;
+            auto epilogue = [&](const floatx16& P, int d) __attribute__((always_inline)) {
+                const float sf = h2f((uint16_t)ring.s[d]) * (F16 ? 1.f : 0.0625f);
                 // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
 #pragma unroll
-                for (int qq = 0; qq < NQ; ++qq) {
-                    const float4 xq = *(const float4*)(xt + gi * 32 + 8 * qq);
-                    acc[4 * qq + 0] = fmaf(sf, P[4 * qq + 0], fmaf(mo, xq.x, acc[4 * qq + 0]));
-                    acc[4 * qq + 1] = fmaf(sf, P[4 * qq + 1], fmaf(mo, xq.y, acc[4 * qq + 1]));
-                    acc[4 * qq + 2] = fmaf(sf, P[4 * qq + 2], fmaf(mo, xq.z, acc[4 * qq + 2]));
-                    acc[4 * qq + 3] = fmaf(sf, P[4 * qq + 3], fmaf(mo, xq.w, acc[4 * qq + 3]));
-                }
+                for (int i = 0; i < 4 * NQ; ++i) acc[i] = fmaf(sf, P[i], acc[i]);
             };
-            epilogue(P0, g0i, d0);
-            if (second) epilogue(P1, g0i + 1, d1);
+            epilogue(P0, d0);
+            if (second) epilogue(P1, d1);
             pin(acc);
             ring.fill(d0, g + XD);   // the slots' contents are dead now
             ring.fill(d1, g + 1 + XD);
@@ -452,16 +426,16 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
 template <int PLANES, bool F16, int NW>
 __device__ __forceinline__ void stream_expert_m(int M, int G, uint4* lds,
                                                 const uint16_t* const (&row)[PLANES],
-                                                CodeRing<XD>& ring, float off, floatx16& acc) {
+                                                CodeRing<XD>& ring, floatx16& acc) {
     const int nq = (M + 7) / 8;
     if (nq <= 1)
-        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, off, acc);
+        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, acc);
     else if (nq == 2)
-        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, off, acc);
+        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, acc);
     else if (nq == 3)
-        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, off, acc);
+        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, acc);
     else
-        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, off, acc);
+        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,7 +515,7 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, F16 ? 1024.f : 128.f, acc);
+    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, acc);
 
     // up waves -> LDS; each gate wave forms h' = p GELU(gate) up
     if (wave >= GT) {
@@ -640,7 +614,7 @@ __global__ __launch_bounds__(64 * DN_WAVES) __attribute__((amdgpu_waves_per_eu(X
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, 128.f, acc);
+    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, acc);
 
     if (n < a.H) {
 #pragma unroll

@@ -280,13 +280,17 @@ class MoEWeights:
 
 
 def moe_weights(E: int, H: int, I: int, Is: int, cfg: int, layer: int,
-                identical_experts: bool = False, flat_router: bool = False) -> MoEWeights:
+                identical_experts: bool = False, flat_router: bool = False,
+                expert_codes: dict | None = None) -> MoEWeights:
     """Draw one MoE layer. Tensor ids are spaced by 8 per matrix.
 
     identical_experts: every routed expert gets expert 0's tensors.
     flat_router: router codes all zero, and scales and biases all equal, so every
     router row holds the same stored values and all logits tie exactly.
+    expert_codes: keyword arguments of ``affine_weights`` (codes, const_code,
+    code_set, bias_code) for every expert matrix, routed and shared.
     """
+    ek = dict(expert_codes or {})
     router = affine_weights(8, E, H, cfg, layer, 0)
     if flat_router:
         router = AffineWeights(8, E, H, np.zeros_like(router.wq),
@@ -295,10 +299,10 @@ def moe_weights(E: int, H: int, I: int, Is: int, cfg: int, layer: int,
     gus, dns = [], []
     for e in range(E):
         src = 0 if identical_experts else e
-        gus.append(affine_weights(4, 2 * I, H, cfg, layer, 16 + 16 * src))
-        dns.append(affine_weights(4, H, I, cfg, layer, 24 + 16 * src))
-    sgu = affine_weights(4, 2 * Is, H, cfg, layer, 8)
-    sdn = affine_weights(4, H, Is, cfg, layer, 12)
+        gus.append(affine_weights(4, 2 * I, H, cfg, layer, 16 + 16 * src, **ek))
+        dns.append(affine_weights(4, H, I, cfg, layer, 24 + 16 * src, **ek))
+    sgu = affine_weights(4, 2 * Is, H, cfg, layer, 8, **ek)
+    sdn = affine_weights(4, H, Is, cfg, layer, 12, **ek)
     return MoEWeights(
         E, H, I, Is, router,
         np.stack([a.wq for a in gus]), np.stack([a.scales for a in gus]),
