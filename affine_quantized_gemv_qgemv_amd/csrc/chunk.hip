@@ -6,19 +6,18 @@
 // path ("성능과 제약": affine 4-bit, group 64, w = s*q + b).
 //
 // Rounding w itself to bf16 would lose too much (8 significant bits), so
-// the matrix-core operand is the exact centred code (mfma.h): with
-// w = s (q - 8) + (b + 8 s), one v_mfma_f32_32x32x16_bf16 chain per group of
-// 64 inputs (4 x K=16) on the operand 16 (q - 8) yields
-//     P_g[m][n] = sum_{k in g} X[m][k] 16 (q[n][k] - 8)          (fp32)
+// the matrix-core operand is the exact code q (4 bits; mfma.h converts the
+// nibbles through the fp8 converter, which maps them exactly): one
+// v_mfma_f32_32x32x16_bf16 chain per group of 64 inputs (4 x K=16) yields
+//     P_g[m][n] = sum_{k in g} X[m][k] q[n][k]                    (fp32)
 // and the epilogue adds
-//     acc[m][n] += (s[n][g] / 16) P_g[m][n] + (b[n][g] + 8 s[n][g]) Xsum_g[m]
+//     acc[m][n] += s[n][g] P_g[m][n] + b[n][g] Xsum_g[m]
 // with Xsum_g[m] = sum_{k in g} X[m][k], computed while X is staged: the
 // first term as an fp32 FMA per group, the second once per stage on the
 // matrix core from three-part bf16 splits of both factors, about as exact
-// as an fp32 product (the two terms cancel where weights sit near zero).
-// The products carry no offset, so the fp32 sums round in proportion to
-// |s (q - 8) x| and a weight at the centre contributes nothing (fp16
-// activations: the operand is q - 8 on an fp16 MFMA, scale s).
+// as an fp32 product (the two terms cancel where weights sit near zero,
+// b ~ -q s; the products are exact and the fp32 sums round in proportion to
+// |s q x| <= 15 |s x|). fp16 activations run the same on an fp16 MFMA.
 
 // Tiling: a workgroup owns 128 rows (the whole chunk) x 64 output columns
 // with 8 waves: two column waves (32 columns each, all 128 rows as four 32x32
@@ -34,9 +33,11 @@
 //
 // Cost notes: a wave64 vector instruction occupies its SIMD for 4 cycles, so
 // the per-group vector work (unpacking codes, scaling P) is kept small next
-// to the MFMAs: the bias term is done on the matrix core once per stage, the
-// MFMA results stay in ordinary VGPRs, and each unpacked code word feeds 16
-// MFMAs (four row blocks).
+// to the MFMAs and issued while they run: each row block's MFMA chain is
+// followed by the previous block's scaling (independent of it), the bias
+// term is done on the matrix core once per stage, the MFMA results stay in
+// ordinary VGPRs, and each unpacked code word feeds 16 MFMAs (four row
+// blocks).
 #include <type_traits>
 
 #include "common.h"
@@ -65,7 +66,8 @@ struct ChunkArgs {
 // A workgroup owns MT = 32 MB WM rows (one row tile) and 64 columns. LDS
 // layout (dynamic): xs[2 buffers][SG groups][MT rows][XS_STRIDE] uint4, then
 // the per-group row sums as bias-product parts (bias_row_parts),
-// xsum[2][MT rows][SG groups] uint2.
+// xsum[2][SG groups][MT rows] uint2 (row-contiguous: a lane per row reads
+// without bank conflicts).
 template <int SG, int MT_, bool F16 = false>
 struct ChunkLds {
     static constexpr int MT = MT_;
@@ -136,7 +138,7 @@ struct StageIO {
                 }
             }
             acc = seg_sum<TPR>(acc);   // the TPR adjacent lanes of the row
-            xsum[r * SG + gi] = bias_row_parts(acc);   // every lane of the row stores the same
+            xsum[gi * MT + r] = bias_row_parts(acc);   // every lane of the row stores the same
         }
     }
 };
@@ -177,10 +179,9 @@ __device__ __forceinline__ int opaque(int v) {
 // XD = stages of X held in registers ahead of LDS: with 1, the next stage is
 // read while the current one is consumed; with 2 (small row tiles, whose
 // stages hold little matrix work) the stage after that is also in flight.
-// F16: fp16 activations on an fp16 MFMA (operand q - 8, scale s); bf16
-// activations take the operand 16 (q - 8) and scale s / 16. Either way the
-// bias term (b + 8 s) Xsum, of the size of the result, runs on the matrix
-// core once per stage.
+// F16: fp16 activations on an fp16 MFMA, else bf16; the operand is the code
+// q either way. The bias term b Xsum, of the size of the result, runs on the
+// matrix core once per stage.
 template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     using IO = StageIO<SG, MT, 64 * WS * NKS, F16>;
     extern __shared__ uint4 smem[];
     uint4* xs_raw = smem;                                    // [2][XS]
-    uint2* xsum_raw = (uint2*)(smem + 2 * L::XS);            // [2][MT][SG]
+    uint2* xsum_raw = (uint2*)(smem + 2 * L::XS);            // [2][SG][MT]
     const int RT = (a.M + MT - 1) / MT;                      // row tiles
     const int b = blockIdx.x;
     const int ct = (b / (8 * RT)) * 8 + b % 8;
@@ -243,49 +244,47 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
     __syncthreads();
 
-    // one group (step g, slot e): MFMAs into P, then acc += s P, then the
-    // slot is refilled with step g + D. xs: this lane's A-operand row (row
-    // 32 MB wm + l32, k-half h) of the group. The bias part, (b + 8 s) Xsum,
-    // is added per stage on the matrix core (bias_mfma below).
+    // one group (step g, slot e): the row blocks' MFMA chains in turn into
+    // a two-slot ring P; block mb - 1's scaling, acc += s P, is issued after
+    // block mb's MFMAs (it does not depend on them, so it runs while they
+    // do); then the slot is refilled with step g + D. xs: this lane's
+    // A-operand row (row 32 MB wm + l32, k-half h) of the group. The bias
+    // part, b Xsum, is added per stage on the matrix core (bias_mfma below).
     auto group = [&](const int g, auto ec, const uint4* xs) __attribute__((always_inline)) {
         constexpr int e = decltype(ec)::value;
-        // the 4 steps' B operands, then the row blocks PH at a time (fewer
-        // live accumulators than all MB at once)
-        constexpr int PH = MB < 2 ? MB : 2;
         const uint32_t wv[4] = {bq[e].x, bq[e].y, bq[e].z, bq[e].w};
         bf16x8_t bfrag[4];
 #pragma unroll
         for (int stp = 0; stp < 4; ++stp)
-            bfrag[stp] = __builtin_bit_cast(bf16x8_t, F16 ? codes_centred_f16(wv[stp])
-                                                          : codes_centred_bf16x16(wv[stp]));
-        const float sf = h2f((uint16_t)bs[e]) * (F16 ? 1.f : 0.0625f);
+            bfrag[stp] = __builtin_bit_cast(bf16x8_t, F16 ? codes_f16(wv[stp]) : codes_bf16(wv[stp]));
+        // one conversion here: folded into each FMA, the compiler would emit the
+        // mixed-precision FMA, which issues at half the rate of a plain one
+        float sf = h2f((uint16_t)bs[e]);
+        asm volatile("" : "+v"(sf));
+        floatx16 P[2];
+        auto scale = [&](auto mbc) __attribute__((always_inline)) {
+            constexpr int mb = decltype(mbc)::value;
 #pragma unroll
-        for (int m0b = 0; m0b < MB; m0b += PH) {
-            floatx16 P[PH];
+            for (int i = 0; i < 16; ++i) acc[mb][i] = fmaf(sf, P[mb & 1][i], acc[mb][i]);
+        };
+        static_for<0, MB>([&](auto mbc) __attribute__((always_inline)) {
+            constexpr int mb = decltype(mbc)::value;
 #pragma unroll
-            for (int pb = 0; pb < PH; ++pb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) P[pb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) P[mb & 1][i] = 0.f;
 #pragma unroll
             for (int stp = 0; stp < 4; ++stp) {
-#pragma unroll
-                for (int pb = 0; pb < PH; ++pb) {
-                    const uint4 av = xs[32 * (m0b + pb) * XS_STRIDE + stp];
-                    if constexpr (F16)
-                        P[pb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(halfx8_c, av), __builtin_bit_cast(halfx8_c, bfrag[stp]),
-                            P[pb], 0, 0, 0);
-                    else
-                        P[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8_t, av), bfrag[stp], P[pb], 0, 0, 0);
-                }
+                const uint4 av = xs[32 * mb * XS_STRIDE + stp];
+                if constexpr (F16)
+                    P[mb & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(halfx8_c, av), __builtin_bit_cast(halfx8_c, bfrag[stp]),
+                        P[mb & 1], 0, 0, 0);
+                else
+                    P[mb & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), bfrag[stp], P[mb & 1], 0, 0, 0);
             }
-#pragma unroll
-            for (int pb = 0; pb < PH; ++pb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[m0b + pb][i] = fmaf(sf, P[pb][i], acc[m0b + pb][i]);
-            __builtin_amdgcn_sched_barrier(0);   // keep the passes apart (registers)
-        }
+            if constexpr (mb > 0) scale(std::integral_constant<int, mb - 1>{});
+        });
+        scale(std::integral_constant<int, MB - 1>{});
         // finish this group's epilogue here: left alone, the compiler sinks it
         // to the end of the stage and holds several groups' P at once
 #pragma unroll
@@ -300,8 +299,8 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Bias of this wave's groups of one stage: acc += sum_g Xsum_g[m] (b_g +
-    // 8 s_g)[n] as one MFMA per row block, both factors as three bf16 parts
+    // Bias of this wave's groups of one stage: acc += sum_g Xsum_g[m] b_g[n]
+    // as one MFMA per row block, both factors as three bf16 parts
     // (mfma.h: six exact cross products, within 2^-25 of the fp32 product).
     // Lane half h carries the wave's group j = h of the stage (JS = 2); with
     // one group per wave (JS = 1) half 1 has B = 0. xsum: this lane's staged
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
 #pragma unroll
         for (int j = 0; j < JS; ++j) {
             const int e = sj * JS + j;
-            bv[j] = fmaf(8.f, h2f((uint16_t)bs[e]), h2f((uint16_t)bb[e]));
+            bv[j] = h2f((uint16_t)bb[e]);
             if constexpr (decltype(checked)::value)
                 if (st * SG + NKS * j + ks >= G) bv[j] = 0.f;
         }
@@ -322,7 +321,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         const bf16x8_t bfrag = __builtin_bit_cast(bf16x8_t, bias_b_operand(bsel));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const uint2 r = xsum[(32 * MB * wm + 32 * mb + l32) * SG];
+            const uint2 r = xsum[32 * MB * wm + 32 * mb + l32];
             const bf16x8_t afrag = __builtin_bit_cast(bf16x8_t, bias_a_operand(r));
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[mb], 0, 0, 0);
         }
@@ -338,7 +337,7 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         // stage st + 2 while slot (st + 1) % 2 holds stage st + 1
         constexpr int ld = XD == 1 ? 0 : sj % 2, sv = XD == 1 ? 0 : (sj + 1) % 2;
         IO::load(a, m0, (st + XD) * SG, G, rot, xr[ld]);
-        bias_mfma(st, sjc, checked, xsum_raw + opaque(buf * SG * MT + ks + (JS == 2 ? NKS * h : 0)));
+        bias_mfma(st, sjc, checked, xsum_raw + opaque(buf * SG * MT + (ks + (JS == 2 ? NKS * h : 0)) * MT));
         // group j of this wave is stage group NKS j + ks
         const uint4* xs = xs_raw + opaque(buf * L::XS + ks * MT * XS_STRIDE +
                                           (32 * MB * wm + l32) * XS_STRIDE + 4 * h);

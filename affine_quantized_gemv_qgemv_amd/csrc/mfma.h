@@ -89,6 +89,38 @@ __device__ __forceinline__ uint4 codes_centred_bf16x16_p(uint32_t w) {
                       pk_bf16(sbyte<1>(lo), sbyte<3>(lo)), pk_bf16(sbyte<1>(hi), sbyte<3>(hi)));
 }
 
+// ---------------------------------------------------------------------------
+// Codes through the fp8 converter: a byte 0000qqqq read as OCP E4M3 is
+// exactly q 2^-9 (exponent field 0 or 1 with the code's top bit, mantissa
+// its low three bits: the subnormal and first normal binade join up), so
+// v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 2^9 turns two such bytes into
+// the codes themselves, exactly, in one instruction. 8 codes of one word,
+// natural k order: the nibbles are first spread to bytes (2 ANDs, 1 shift,
+// 2 byte permutes), then 4 conversions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint2 codes_to_bytes(uint32_t w) {
+    const uint32_t t = w & 0x0F0F0F0Fu;          // q0 q2 q4 q6
+    const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;   // q1 q3 q5 q7
+    // v_perm_b32(u, t, sel): selector bytes 0..3 pick t's bytes, 4..7 u's
+    return make_uint2(__builtin_amdgcn_perm(u, t, 0x05010400u), __builtin_amdgcn_perm(u, t, 0x07030602u));
+}
+
+__device__ __forceinline__ uint4 codes_bf16(uint32_t w) {
+    const uint2 b = codes_to_bytes(w);
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 512.f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 512.f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 512.f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 512.f, true)));
+}
+
+__device__ __forceinline__ uint4 codes_f16(uint32_t w) {
+    const uint2 b = codes_to_bytes(w);
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 512.f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 512.f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 512.f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 512.f, true)));
+}
+
 // 4 8-bit codes of one word, natural order, as two bf16 pairs q - 128.
 __device__ __forceinline__ uint2 bytes_centred_bf16(uint32_t w) {
     const uint32_t c = w ^ 0x80808080u;
