@@ -322,28 +322,33 @@ __device__ void stage_x(const void* x, int kind, int64_t xstride, int nb, int c0
 // the chunk's base, so the reads in group_rows take immediate offsets
 // instead of one address add each. Vectors b >= nb are not staged; their
 // results are never stored.
-template <int BITS, int B, int CPL = 1>
-__device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int nc, uint4* lds) {
+template <int BITS, int B, int CPL>
+struct StageCm {
     using St = Stage<BITS, 0>;
-    constexpr int CC = St::CC;
-    constexpr int QPC = St::QPC;
-    constexpr int SC = B * QPC + 1;
-    uint4* xs = lds;
-    float* cs = (float*)(xs + (size_t)nc * SC);
-    for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
+    static constexpr int CC = St::CC;
+    static constexpr int QPC = St::QPC;
+    static constexpr int SC = B * QPC + 1;
+    static constexpr int NQ = BITS == 4 ? 4 : 2;   // uint4 of fp16 per chunk
+    __device__ static __forceinline__ const uint16_t* src(const void* x, int64_t xstride, int nc,
+                                                          int c0, int item) {
+        const int b = item / nc, cc = item - b * nc;
+        return (const uint16_t*)x + (int64_t)b * xstride + (int64_t)(c0 + cc) * CC;
+    }
+    __device__ static __forceinline__ void put(int nc, uint4* lds, int item, const uint4 (&raw)[NQ]) {
+        uint4* xs = lds;
+        float* cs = (float*)(xs + (size_t)nc * SC);
         const int b = item / nc, cc = item - b * nc;
         const int c = xslot<CPL>(cc, nc);
-        const uint16_t* xp = (const uint16_t*)x + (int64_t)b * xstride + (int64_t)(c0 + cc) * CC;
         float s1 = 0.f, s16 = 0.f;
         if constexpr (BITS == 4) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 raw = *(const uint4*)(xp + 8 * q);
+                const uint4 r = raw[q];
                 uint16_t h[8];
-                h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
-                h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
-                h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
-                h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                h[0] = r.x & 0xFFFF; h[1] = r.x >> 16;
+                h[2] = r.y & 0xFFFF; h[3] = r.y >> 16;
+                h[4] = r.z & 0xFFFF; h[5] = r.z >> 16;
+                h[6] = r.w & 0xFFFF; h[7] = r.w >> 16;
                 xs[c * SC + b * QPC + q] = make_uint4(pack_h2(h[0], h[4]), pack_h2(h[1], h[5]),
                                                       pack_h2(h[2], h[6]), pack_h2(h[3], h[7]));
                 s1 += (h2f(h[0]) + h2f(h[4])) + (h2f(h[2]) + h2f(h[6]));
@@ -353,12 +358,12 @@ __device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int n
         } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const uint4 raw = *(const uint4*)(xp + 8 * q);
+                const uint4 r = raw[q];
                 uint16_t h[8];
-                h[0] = raw.x & 0xFFFF; h[1] = raw.x >> 16;
-                h[2] = raw.y & 0xFFFF; h[3] = raw.y >> 16;
-                h[4] = raw.z & 0xFFFF; h[5] = raw.z >> 16;
-                h[6] = raw.w & 0xFFFF; h[7] = raw.w >> 16;
+                h[0] = r.x & 0xFFFF; h[1] = r.x >> 16;
+                h[2] = r.y & 0xFFFF; h[3] = r.y >> 16;
+                h[4] = r.z & 0xFFFF; h[5] = r.z >> 16;
+                h[6] = r.w & 0xFFFF; h[7] = r.w >> 16;
                 xs[c * SC + b * QPC + q] = make_uint4(pack_h2(h[0], h[2]), pack_h2(h[1], h[3]),
                                                       pack_h2(h[4], h[6]), pack_h2(h[5], h[7]));
 #pragma unroll
@@ -366,6 +371,49 @@ __device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int n
             }
             cs[c * (B + 1) + b] = s1;
         }
+    }
+};
+
+template <int BITS, int B, int CPL>
+__device__ void stage_x_cm(const void* x, int64_t xstride, int nb, int c0, int nc, uint4* lds) {
+    using S = StageCm<BITS, B, CPL>;
+    for (int item = threadIdx.x; item < nb * nc; item += blockDim.x) {
+        uint4 raw[S::NQ];
+        const uint16_t* xp = S::src(x, xstride, nc, c0, item);
+#pragma unroll
+        for (int q = 0; q < S::NQ; ++q) raw[q] = *(const uint4*)(xp + 8 * q);
+        S::put(nc, lds, item, raw);
+    }
+}
+
+// The same with the caller's loads (after_loads) issued behind each
+// thread's first activation chunk. Vector-memory counters complete in
+// order, so the activation waits do not wait for those loads; the first
+// chunk's loads are unconditional (clamped index) and its LDS writes sit in
+// a branch without loads, so the compiler's counter bookkeeping stays exact
+// (a load under a branch would make it wait for everything at the join).
+// Further chunks of a thread (more chunks than threads) wait for all.
+template <int BITS, int B, int CPL, typename F>
+__device__ __forceinline__ void stage_x_cm_overlap(const void* x, int64_t xstride, int nb, int c0,
+                                                   int nc, uint4* lds, F&& after_loads) {
+    using S = StageCm<BITS, B, CPL>;
+    const int items = nb * nc;
+    const int i0 = min((int)threadIdx.x, items - 1);
+    uint4 raw[S::NQ];
+    {
+        const uint16_t* xp = S::src(x, xstride, nc, c0, i0);
+#pragma unroll
+        for (int q = 0; q < S::NQ; ++q) raw[q] = *(const uint4*)(xp + 8 * q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    after_loads();
+    __builtin_amdgcn_sched_barrier(0);
+    if ((int)threadIdx.x < items) S::put(nc, lds, i0, raw);
+    for (int item = threadIdx.x + blockDim.x; item < items; item += blockDim.x) {
+        const uint16_t* xp = S::src(x, xstride, nc, c0, item);
+#pragma unroll
+        for (int q = 0; q < S::NQ; ++q) raw[q] = *(const uint4*)(xp + 8 * q);
+        S::put(nc, lds, item, raw);
     }
 }
 

@@ -99,10 +99,15 @@ Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
         return c;
     }
     if (S1 <= 8 || !even) {
-        // few rows: one row per tile, up to four steps per round
+        // few rows: one row per tile, up to four steps per round (no more
+        // than a row has: the first round requests all of its steps)
         if (even && c.lpr == 64) c.cpl = 2;
         c.r = 1;
         c.u = 4;
+        if (c.cpl == 2) {
+            const int S = chunks / 128;
+            c.u = S <= 1 ? 1 : (S <= 2 ? 2 : 4);
+        }
         c.nw = 16;
         return c;
     }

@@ -160,7 +160,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
     // row, so per-lane offsets are 32-bit and the chunk and step offsets are
     // instruction immediates.
     const uint32_t rowb = (uint32_t)(wpr * 4);   // bytes of codes per row (< 2^24)
-    auto issue = [&](Round<R, U, CPL>& buf, int tile, int sg) {
+    // all: request every step of the round (the peeled first round, so that
+    // no branch sits among the prologue's loads)
+    auto issue = [&](Round<R, U, CPL>& buf, int tile, int sg, bool all = false) {
         const int64_t r0 = (int64_t)tile * ROWS;
         const int rlast = a.N - 1 - (int)r0;     // last row of the matrix, tile-relative
         const auto wr = buf_rsrc(a.wq + r0 * wpr, (a.N - r0) * (int64_t)rowb);
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
             br = buf_rsrc(a.zp + r0 * a.zstride, (a.N - r0) * (int64_t)a.zstride);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (sg * U + u >= S) break;  // uniform
+            if (!all && sg * U + u >= S) break;  // uniform
             const int c = (((sg * U + u) * F + f) * LPR + sl) * CPL;
             const int gc = c0 + min(c, nc - CPL);
 #pragma unroll
@@ -321,6 +323,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WPE))) voi
         stage_x_rot<BITS, CPL>((const uint16_t*)a.x, a.xkind, a.K, a.nb, c0, nc, a.gamma,
                                a.signs, a.eps, rot, lds,
                                [&]() { if (ntl > 0) issue(A, t0, 0); });
+    } else if constexpr (XF == 0) {
+        // behind the activation loads, unconditionally (a wave with no tile
+        // requests a clamped one and never uses it)
+        stage_x_cm_overlap<BITS, B, CPL>(a.x, a.K, a.nb, c0, nc, lds, [&]() {
+            issue(A, min(t0, ntiles - 1), 0, true);
+        });
     } else {
         if (ntl > 0) issue(A, t0, 0);
         stage_x_any<BITS, XF, B, CPL>(a.x, a.xkind, a.K, a.nb, c0, nc, lds);
@@ -462,7 +470,8 @@ template <int BITS, int XF, int B, int FMT>
 hipError_t run_b(const GemvArgs& a, const Cfg& c, hipStream_t st) {
     if constexpr (B == 1) {
         QD_LPRS(1, 4, 1) QD_LPRS(1, 8, 1)
-        QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(1, 4, 1) QD_LPRS2(1, 8, 1)
+        QD_LPRS2(2, 1, 1) QD_LPRS2(2, 2, 1) QD_LPRS2(1, 1, 1) QD_LPRS2(1, 2, 1) QD_LPRS2(1, 4, 1)
+        QD_LPRS2(1, 8, 1)
     } else if constexpr (B == 2 || B == 4) {
         QD_TRY(64, 2, 1, 1, 2) QD_TRY(32, 2, 1, 1, 2) QD_TRY(32, 4, 1, 1, 1)
     } else {

@@ -194,14 +194,6 @@ __global__ __launch_bounds__(1024) void moe_gateup_kernel(MoeAArgs a) {
 // ---------------------------------------------------------------------------
 // B. down rows of the k selected experts and the shared expert, combined.
 // ---------------------------------------------------------------------------
-struct SegInfo {             // one 16-byte code chunk of the concatenated row
-    const uint32_t* q;       // chunk address in row 0
-    const uint16_t* s;       // scale address in row 0
-    const uint16_t* b;       // bias address in row 0
-    int qstride;             // words per row (negative: chunk contributes nothing)
-    int gstride;             // groups per row
-};
-
 struct MoeBArgs {
     const uint32_t *dn_q, *sdn_q;
     const uint16_t *dn_s, *dn_b, *sdn_s, *sdn_b;
@@ -212,70 +204,61 @@ struct MoeBArgs {
     int E, H, I, Is, k;
 };
 
+// Chunk c (16 bytes = 32 codes) of the concatenated down row: the routed
+// segment j = c / (I/32) of expert idx[j], or the shared expert's row.
+// Addresses are those of row 0; row n adds n * qs words and n * gs groups.
+struct DnChunk {
+    const uint32_t* q;
+    const uint16_t *s, *b;
+    int qs, gs;
+    bool ok;   // false: an expert id outside [0, E) (contributes nothing)
+};
+
+// idv: lane j < k holds the expert id of slot j (read with a lane shuffle,
+// so every lane of the wave must call this).
+__device__ __forceinline__ DnChunk dn_chunk(const MoeBArgs& a, int c, int idv) {
+    const int cpe = a.I / 32;
+    DnChunk d;
+    const int jr = min(c / cpe, a.k - 1);
+    const int er = __shfl(idv, jr);
+    if (c < a.k * cpe) {
+        const int j = c / cpe, cl = c - j * cpe;
+        int e = er;
+        d.ok = e >= 0 && e < a.E;
+        if (!d.ok) e = 0;
+        const int64_t mq = (int64_t)e * a.H * (a.I / 8);
+        const int64_t mg = (int64_t)e * a.H * (a.I / 64);
+        d.q = a.dn_q + mq + (int64_t)cl * 4;
+        d.s = a.dn_s + mg + cl / 2;
+        d.b = a.dn_b + mg + cl / 2;
+        d.qs = a.I / 8;
+        d.gs = a.I / 64;
+    } else {
+        const int cl = c - a.k * cpe;
+        d.q = a.sdn_q + (int64_t)cl * 4;
+        d.s = a.sdn_s + cl / 2;
+        d.b = a.sdn_b + cl / 2;
+        d.qs = a.Is / 8;
+        d.gs = a.Is / 64;
+        d.ok = true;
+    }
+    return d;
+}
+
+// A wave's lanes take LPR-lane segments of one row each (R rows per
+// segment); a lane reads CPL consecutive chunks per step. The first step
+// batch of the wave's first tile is requested before the activations are
+// staged, so the weight fetch overlaps the staging.
+constexpr int DN_MAX_WAVES = 12;   // 168 VGPRs: the early-requested chunks live across the staging
+
 template <int LPR, int R, int U, int CPL>
-__global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
+__global__ __launch_bounds__(64 * DN_MAX_WAVES) void moe_down_kernel(MoeBArgs a) {
     extern __shared__ uint4 lds[];
     constexpr int RPI = 64 / LPR;
     constexpr int ROWS = RPI * R;
     const int cpe = a.I / 32;                  // chunks per routed segment
     const int C = a.k * cpe + a.Is / 32;       // chunks of the concatenated row
-    // LDS: staged activations (fp32 layout for 4-bit codes), then SegInfo[C]
     using St = Stage<4, 1>;
-    const size_t xbytes = (St::bytes(1, C) + 15) & ~(size_t)15;
-    SegInfo* info = (SegInfo*)((char*)lds + xbytes);
-
-    // stage h' = (p_j h_j | h_s) and the chunk table
-    for (int c = threadIdx.x; c < C; c += blockDim.x) {
-        float scale = 1.f;
-        SegInfo si;
-        if (c < a.k * cpe) {
-            const int j = c / cpe, cl = c - j * cpe;
-            int e = a.idx[j];
-            const bool ok = e >= 0 && e < a.E;
-            scale = ok ? a.p[j] : 0.f;
-            if (!ok) e = 0;
-            const int64_t mq = (int64_t)e * a.H * (a.I / 8);
-            const int64_t mg = (int64_t)e * a.H * (a.I / 64);
-            si.q = a.dn_q + mq + (int64_t)cl * 4;
-            si.s = a.dn_s + mg + cl / 2;
-            si.b = a.dn_b + mg + cl / 2;
-            si.qstride = ok ? a.I / 8 : -(a.I / 8);
-            si.gstride = a.I / 64;
-        } else {
-            const int cl = c - a.k * cpe;
-            si.q = a.sdn_q + (int64_t)cl * 4;
-            si.s = a.sdn_s + cl / 2;
-            si.b = a.sdn_b + cl / 2;
-            si.qstride = a.Is / 8;
-            si.gstride = a.Is / 64;
-        }
-        info[c] = si;
-        const float* hv = a.h + (int64_t)c * 32;
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-            const float4 t = *(const float4*)(hv + i);
-            v[i] = t.x * scale;
-            v[i + 1] = t.y * scale;
-            v[i + 2] = t.z * scale;
-            v[i + 3] = t.w * scale;
-        }
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sum += v[i];
-        constexpr int QPC = St::QPC;
-        const int sl = xslot<CPL>(c, C);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {   // the pair order of the 4-bit unpack
-            const float* u = v + 8 * w;
-            lds[(2 * w) * C + sl] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[4]),
-                                               __float_as_uint(u[2]), __float_as_uint(u[6]));
-            lds[(2 * w + 1) * C + sl] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[5]),
-                                                   __float_as_uint(u[3]), __float_as_uint(u[7]));
-        }
-        ((float*)(lds + (size_t)QPC * C))[sl] = sum;
-    }
-    __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int seg = lane / LPR, sl = lane % LPR;
@@ -286,42 +269,118 @@ __global__ __launch_bounds__(1024) void moe_down_kernel(MoeBArgs a) {
     const int ntiles = (a.H + ROWS - 1) / ROWS;
     const int t0 = (int)((int64_t)ntiles * gw / W);
     const int t1 = (int)((int64_t)ntiles * (gw + 1) / W);
-    const uint32_t magic = in_vgpr(kMagic16);
 
+    // Load order (vector-memory counters complete in order): the routing,
+    // this thread's first activation chunk, then the first code batch, so
+    // waiting for the first two never waits for code fetches. The loads are
+    // unconditional (clamped addresses): a branch around one would make the
+    // compiler's counter bookkeeping wait for everything at the join.
+    const int ls = min(lane, a.k - 1);   // k <= 32
+    const int idv = a.idx[ls];
+    const float pv = a.p[ls];
+    const int cst = threadIdx.x;   // first staged chunk of this thread
+    float4 hv[8];
+    {
+        const float* hp = a.h + (int64_t)min(cst, C - 1) * 32;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = *(const float4*)(hp + 4 * i);
+    }
+    // routing weight of that chunk (all lanes active for the shuffles)
+    float scale0;
+    {
+        const int jr = min(cst / cpe, a.k - 1);
+        const int er = __shfl(idv, jr);
+        const float pr = __shfl(pv, jr);
+        scale0 = cst < a.k * cpe ? ((er >= 0 && er < a.E) ? pr : 0.f) : 1.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint4 cw[U][CPL][R];
+    uint16_t sr[U][R], br[U][R];
+    bool live[U];
+    // all U steps are requested (clamped): a data-dependent exit would make
+    // the counters at the join conservative
+    auto load = [&](int tile, int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cu = ((s0 + u) * LPR + sl) * CPL;
+            const int c = min(cu, C - CPL);
+            const DnChunk d = dn_chunk(a, c, idv);
+            live[u] = cu < C && d.ok;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int n = min(tile * ROWS + r * RPI + seg, a.H - 1);
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch)
+                    cw[u][ch][r] = *(const uint4*)(d.q + (int64_t)n * d.qs + 4 * ch);
+                sr[u][r] = d.s[(int64_t)n * d.gs];
+                br[u][r] = d.b[(int64_t)n * d.gs];
+            }
+        }
+    };
+    load(min(t0, ntiles - 1), 0);   // unconditional (see above)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage h' = (p_j h_j | h_s) (fp32 layout for 4-bit codes); the first
+    // chunk straight-line (a loop around it would join its counters with
+    // those of later iterations), further ones (more chunks than threads)
+    // in a loop
+    auto stage_chunk = [&](int c, float scale) __attribute__((always_inline)) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) {
+            const float4 t = hv[i / 4];
+            v[i] = t.x * scale;
+            v[i + 1] = t.y * scale;
+            v[i + 2] = t.z * scale;
+            v[i + 3] = t.w * scale;
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sum += v[i];
+        constexpr int QPC = St::QPC;
+        const int sl2 = xslot<CPL>(c, C);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {   // the pair order of the 4-bit unpack
+            const float* u = v + 8 * w;
+            lds[(2 * w) * C + sl2] = make_uint4(__float_as_uint(u[0]), __float_as_uint(u[4]),
+                                                __float_as_uint(u[2]), __float_as_uint(u[6]));
+            lds[(2 * w + 1) * C + sl2] = make_uint4(__float_as_uint(u[1]), __float_as_uint(u[5]),
+                                                    __float_as_uint(u[3]), __float_as_uint(u[7]));
+        }
+        ((float*)(lds + (size_t)QPC * C))[sl2] = sum;
+    };
+    if (cst < C) stage_chunk(cst, scale0);
+    for (int c = cst + (int)blockDim.x; c < C; c += blockDim.x) {
+        float scale = 1.f;
+        if (c < a.k * cpe) {
+            const int j = c / cpe;
+            const int e = a.idx[j];
+            scale = (e >= 0 && e < a.E) ? a.p[j] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = *(const float4*)(a.h + (int64_t)c * 32 + 4 * i);
+        stage_chunk(c, scale);
+    }
+    __syncthreads();
+
+    const uint32_t magic = in_vgpr(kMagic16);
     for (int tile = t0; tile < t1; ++tile) {
         float y[R][1];
 #pragma unroll
         for (int r = 0; r < R; ++r) y[r][0] = 0.f;
         for (int s0 = 0; s0 < S; s0 += U) {
-            uint4 cw[U][CPL][R];
-            uint16_t sr[U][R], br[U][R];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (s0 + u >= S) break;
-                const int c = min(((s0 + u) * LPR + sl) * CPL, C - CPL);
-                const SegInfo si = info[c];
-                const int qs = si.qstride < 0 ? -si.qstride : si.qstride;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int n = min(tile * ROWS + r * RPI + seg, a.H - 1);
-#pragma unroll
-                    for (int ch = 0; ch < CPL; ++ch)
-                        cw[u][ch][r] = *(const uint4*)(si.q + (int64_t)n * qs + 4 * ch);
-                    sr[u][r] = si.s[(int64_t)n * si.gstride];
-                    br[u][r] = si.b[(int64_t)n * si.gstride];
-                }
-            }
+            if (tile != t0 || s0 != 0) load(tile, s0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (s0 + u >= S) break;
                 const int cu = ((s0 + u) * LPR + sl) * CPL;
                 const int c = min(cu, C - CPL);
-                const bool live = cu < C && info[c].qstride > 0;
                 float sc[R], bi[R];   // scale and centred bias b + 8 s
                 uint32_t n1[R], n16[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const bool ok = live && (tile * ROWS + r * RPI + seg < a.H);
+                    const bool ok = live[u] && (tile * ROWS + r * RPI + seg < a.H);
                     sc[r] = ok ? h2f(sr[u][r]) : 0.f;
                     bi[r] = ok ? fmaf(8.f, sc[r], h2f(br[u][r])) : 0.f;
                     n1[r] = kNeg1032;
@@ -387,15 +446,15 @@ template <int R>
 hipError_t launch_down_r(const MoeBArgs& a, int nw, hipStream_t st) {
     constexpr int LPR = 64, U = 2, CPL = 2;
     const int C = a.k * (a.I / 32) + a.Is / 32;
-    const size_t lds = ((Stage<4, 1>::bytes(1, C) + 15) & ~(size_t)15) + (size_t)C * sizeof(SegInfo);
+    const size_t lds = Stage<4, 1>::bytes(1, C);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     const int ntiles = (a.H + (64 / LPR) * R - 1) / ((64 / LPR) * R);
     auto kern = moe_down_kernel<LPR, R, U, CPL>;
     // Every workgroup stages all k*I + Is activations: at most one per CU,
-    // each with just enough waves (up to 16) that the rows spread over all
-    // CUs (2816 rows: 256 workgroups of 11 waves rather than 176 of 16).
+    // each with just enough waves (up to 12) that the rows spread over all
+    // CUs (2816 rows: 256 workgroups of 11 waves rather than 235 of 12).
     const int cus = device_info().cus;
-    if (nw <= 0) nw = std::min(16, std::max(1, (ntiles + cus - 1) / cus));
+    if (nw <= 0) nw = std::min(DN_MAX_WAVES, std::max(1, (ntiles + cus - 1) / cus));
     const int threads = 64 * nw;
     const int grid = std::min(grid_for(kern, threads, lds, ntiles), device_info().cus);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
