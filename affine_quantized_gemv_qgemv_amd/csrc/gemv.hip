@@ -100,7 +100,8 @@ Cfg default_cfg(int bits, int xf, int nb, int N, int K) {
     }
     if (S1 <= 8 || !even) {
         // few rows: one row per tile, up to four steps per round (no more
-        // than a row has: the first round requests all of its steps)
+        // than a row has: the first round requests all of its steps; eight
+        // steps per round measured slower, fewer waves fit)
         if (even && c.lpr == 64) c.cpl = 2;
         c.r = 1;
         c.u = 4;

@@ -17,32 +17,11 @@ constexpr int XS_STRIDE = 9;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// 8 codes of one word -> 16-bit (off + q) in natural k order: the nibble in
-// the low mantissa of magic (per half: 0x4300 = bf16 128, 0x6400 = fp16 1024).
-__device__ __forceinline__ uint4 codes_to_16n(uint32_t w, uint32_t magic) {
-    const uint32_t t = w & 0x0F0F0F0Fu;         // q0 q2 q4 q6 in bytes 0..3
-    const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;  // q1 q3 q5 q7
-    // v_perm_b32(u, t, sel): selector bytes 0..3 pick t's bytes, 4..7 u's, 0x0C gives 0
-    const uint32_t p01 = __builtin_amdgcn_perm(u, t, 0x0C040C00u) | magic;
-    const uint32_t p23 = __builtin_amdgcn_perm(u, t, 0x0C050C01u) | magic;
-    const uint32_t p45 = __builtin_amdgcn_perm(u, t, 0x0C060C02u) | magic;
-    const uint32_t p67 = __builtin_amdgcn_perm(u, t, 0x0C070C03u) | magic;
-    return make_uint4(p01, p23, p45, p67);
-}
-
 // ---------------------------------------------------------------------------
-// Centred codes as matrix-core operands: w = s (q - c) + (b + c s), with the
-// operand holding q - c exactly, so the fp32 products and sums carry no
-// offset and a weight at the centre contributes exactly zero.
-//  * fp16 operands: the code in the low mantissa of fp16 1024.0 is 1024 + q;
-//    one v_pk_add_f16 with -(1024 + c) leaves q - c (exact in fp16).
-//  * bf16 operands (no packed bf16 add on gfx950): a 4-bit code XOR 8, read
-//    as a signed nibble, is q - 8; placed in the top half of a byte it reads
-//    as the signed byte 16 (q - 8), which v_cvt_f32_i32 (SDWA byte select,
-//    sign-extended) converts exactly and v_cvt_pk_bf16_f32 packs exactly
-//    (|16 (q - 8)| <= 128 needs 4 significant bits). The factor 16 is taken
-//    out of the scale (an exact power of two). An 8-bit code XOR 0x80 is the
-//    signed byte q - 128, exact in bf16 (at most 8 significant bits).
+// 8-bit codes as matrix-core operands (the router over a token chunk): a
+// code XOR 0x80 is the signed byte q - 128, which v_cvt_f32_i32 (SDWA byte
+// select, sign-extended) converts exactly and v_cvt_pk_bf16_f32 packs
+// exactly (at most 8 significant bits); see bytes_centred_bf16 below.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -55,38 +34,6 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 template <int I>
 __device__ __forceinline__ float sbyte(uint32_t v) {
     return (float)(int8_t)(v >> (8 * I));
-}
-
-// 8 codes of one word, natural k order, as fp16 q - 8.
-__device__ __forceinline__ uint4 codes_centred_f16(uint32_t w) {
-    const uint4 p = codes_to_16n(w, 0x64006400u);
-    return make_uint4(pk_addh(p.x, kNeg1032), pk_addh(p.y, kNeg1032), pk_addh(p.z, kNeg1032),
-                      pk_addh(p.w, kNeg1032));
-}
-
-// 8 codes of one word, natural k order, as bf16 16 (q - 8).
-__device__ __forceinline__ uint4 codes_centred_bf16x16(uint32_t w) {
-    const uint32_t c = w ^ 0x88888888u;
-    const uint32_t lo = (c << 4) & 0xF0F0F0F0u;   // codes 0, 2, 4, 6 in the top of bytes 0..3
-    const uint32_t hi = c & 0xF0F0F0F0u;          // codes 1, 3, 5, 7
-    return make_uint4(pk_bf16(sbyte<0>(lo), sbyte<0>(hi)), pk_bf16(sbyte<1>(lo), sbyte<1>(hi)),
-                      pk_bf16(sbyte<2>(lo), sbyte<2>(hi)), pk_bf16(sbyte<3>(lo), sbyte<3>(hi)));
-}
-
-// The same in the k order [0, 4, 1, 5, 2, 6, 3, 7] (fp16: the magic in a VGPR).
-__device__ __forceinline__ uint4 codes_centred_f16_p(uint32_t w, uint32_t magic) {
-    return make_uint4(pk_addh((w & 0x000F000Fu) | magic, kNeg1032),
-                      pk_addh(((w >> 4) & 0x000F000Fu) | magic, kNeg1032),
-                      pk_addh(((w >> 8) & 0x000F000Fu) | magic, kNeg1032),
-                      pk_addh(((w >> 12) & 0x000F000Fu) | magic, kNeg1032));
-}
-
-__device__ __forceinline__ uint4 codes_centred_bf16x16_p(uint32_t w) {
-    const uint32_t c = w ^ 0x88888888u;
-    const uint32_t lo = (c << 4) & 0xF0F0F0F0u;
-    const uint32_t hi = c & 0xF0F0F0F0u;
-    return make_uint4(pk_bf16(sbyte<0>(lo), sbyte<2>(lo)), pk_bf16(sbyte<0>(hi), sbyte<2>(hi)),
-                      pk_bf16(sbyte<1>(lo), sbyte<3>(lo)), pk_bf16(sbyte<1>(hi), sbyte<3>(hi)));
 }
 
 // ---------------------------------------------------------------------------
@@ -121,6 +68,29 @@ __device__ __forceinline__ uint4 codes_f16(uint32_t w) {
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 512.f, true)));
 }
 
+// The same codes in the k order [0, 4, 1, 5, 2, 6, 3, 7] (bytes q0 q4 q1 q5
+// and q2 q6 q3 q7 before the conversions).
+__device__ __forceinline__ uint2 codes_to_bytes_p(uint32_t w) {
+    const uint32_t t = w & 0x0F0F0F0Fu;          // q0 q2 q4 q6
+    const uint32_t u = (w >> 4) & 0x0F0F0F0Fu;   // q1 q3 q5 q7
+    return make_uint2(__builtin_amdgcn_perm(u, t, 0x06040200u), __builtin_amdgcn_perm(u, t, 0x07050301u));
+}
+
+template <bool F16>
+__device__ __forceinline__ uint4 codes_p(uint32_t w) {
+    const uint2 b = codes_to_bytes_p(w);
+    if constexpr (F16)
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 512.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 512.f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 512.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 512.f, true)));
+    else
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 512.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.x, 512.f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 512.f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b.y, 512.f, true)));
+}
+
 // 4 8-bit codes of one word, natural order, as two bf16 pairs q - 128.
 __device__ __forceinline__ uint2 bytes_centred_bf16(uint32_t w) {
     const uint32_t c = w ^ 0x80808080u;
@@ -129,9 +99,9 @@ __device__ __forceinline__ uint2 bytes_centred_bf16(uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // Bias products on the matrix core: acc[m][n] += X[m] V[n] with fp32 factors
-// (a group's row sum and its b + c s). With centred codes this term cancels
-// against s P where weights sit near zero, so it must be about as exact as
-// an fp32 product. Each factor is split into three bf16 parts a = hi + mid +
+// (a group's row sum and its bias, or b + c s for an operand centred at c).
+// Where weights sit near zero (b ~ -q s) this term cancels against s P, so
+// it must be about as exact as an fp32 product. Each factor is split into three bf16 parts a = hi + mid +
 // lo (each part the rounding of what the earlier ones leave; every residual
 // is exact in fp32, so the parts hold 24 significant bits and miss a by at
 // most 2^-27 |a|). The six cross products of weight down to 2^-18 fill six

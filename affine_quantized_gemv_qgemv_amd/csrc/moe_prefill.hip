@@ -200,10 +200,9 @@ __device__ __forceinline__ int opaque_i(int v) {
     return r;
 }
 
-// The codes enter the matrix core centred (mfma.h): fp16 q - 8 or bf16
-// 16 (q - 8), in the k order [0, 4, 1, 5, 2, 6, 3, 7] (one v_and_or_b32 and
-// one v_pk_add_f16 per pair on the fp16 path). The activations are staged in
-// LDS in the same order (perm8 below).
+// The codes enter the matrix core as the codes q themselves (fp16 or bf16,
+// through the fp8 converter: mfma.h), in the k order [0, 4, 1, 5, 2, 6, 3, 7].
+// The activations are staged in LDS in the same order (perm8 below).
 
 // 8 16-bit values e0..e7 -> e0 e4 e1 e5 e2 e6 e3 e7 (the codes' order).
 __device__ __forceinline__ uint4 perm8(uint4 v) {
@@ -222,8 +221,8 @@ __device__ __forceinline__ uint4 perm8(uint4 v) {
 // sums, so each activation byte is fetched once per workgroup rather than
 // once per wave. Each wave keeps its codes, scales and biases XD groups
 // ahead in a register ring. Per group a wave runs one MFMA chain per
-// activation plane on the centred codes and adds s P (s / 16 for bf16); the
-// bias term, (b + 8 s) Xsum, is added once per stage on the matrix core.
+// activation plane on the codes and adds s P; the bias term, b Xsum, is
+// added once per stage on the matrix core.
 constexpr int XSG = 4;       // groups per stage
 static_assert(XSG == 4, "the stage bias runs two groups per MFMA, two MFMAs");
 constexpr int XD = 4;        // groups of codes in flight per wave (whole stages)
@@ -316,8 +315,7 @@ struct CodeRing {
 
 // Streams the G groups of a wave's weight row against the staged activation
 // planes: acc (D layout, 32 rows x this lane's column) += sum over groups of
-// s P_g + (b + 8 s) Xsum_g, with P_g the group's product on the centred codes
-// (s / 16 on the bf16 path, whose operand is 16 (q - 8)). The first part
+// s P_g + b Xsum_g, with P_g the group's product on the codes q. The first part
 // runs in fp32 per group; the second, once per stage on the matrix core. NQ =
 // row quarters (8 rows) that hold data: the per-group scaling skips the
 // others. Whole rounds of XD groups run with no
@@ -333,7 +331,6 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
     const int h = lane >> 5, l32 = lane & 31;
     uint2* xsum_raw = (uint2*)(lds + 2 * XS::BUF);
     const int NS = (G + XSG - 1) / XSG;
-    const uint32_t magic = in_vgpr(0x64006400u);   // fp16 1024 (fp16 path)
 
     // activations run XPF stages ahead. XPF = 2: register set st & 1 receives
     // stage st + 2 while set (st + 1) & 1 holds stage st + 1 until it is
@@ -357,8 +354,8 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
         {
             float bv[4];
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {   // b + 8 s
-                bv[gi] = fmaf(8.f, h2f((uint16_t)ring.s[sj * XSG + gi]), h2f((uint16_t)ring.b[sj * XSG + gi]));
+            for (int gi = 0; gi < 4; ++gi) {   // b
+                bv[gi] = h2f((uint16_t)ring.b[sj * XSG + gi]);
                 if constexpr (chk)
                     if (st * XSG + gi >= G) bv[gi] = 0.f;
             }
@@ -387,8 +384,8 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
             const uint32_t w1[4] = {ring.q[d1].x, ring.q[d1].y, ring.q[d1].z, ring.q[d1].w};
 #pragma unroll
             for (int stp = 0; stp < 4; ++stp) {
-                const uint4 b0 = F16 ? codes_centred_f16_p(w0[stp], magic) : codes_centred_bf16x16_p(w0[stp]);
-                const uint4 b1 = F16 ? codes_centred_f16_p(w1[stp], magic) : codes_centred_bf16x16_p(w1[stp]);
+                const uint4 b0 = codes_p<F16>(w0[stp]);
+                const uint4 b1 = codes_p<F16>(w1[stp]);
 #pragma unroll
                 for (int pl = 0; pl < PLANES; ++pl) {
                     P0 = mfma16<F16>(xs[pl * XS::PER + g0i * 32 * XS_STRIDE + stp], b0, P0);
@@ -396,7 +393,10 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
                 }
             }
             auto epilogue = [&](const floatx16& P, int d) __attribute__((always_inline)) {
-                const float sf = h2f((uint16_t)ring.s[d]) * (F16 ? 1.f : 0.0625f);
+                // one conversion (folded into each FMA the compiler would
+                // emit the half-rate mixed-precision form)
+                float sf = h2f((uint16_t)ring.s[d]);
+                asm volatile("" : "+v"(sf));
                 // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
 #pragma unroll
                 for (int i = 0; i < 4 * NQ; ++i) acc[i] = fmaf(sf, P[i], acc[i]);
