@@ -289,7 +289,8 @@ struct XStage {
 };
 
 // Per-wave ring of one weight row's codes, scales and biases (lane: words
-// 4h..4h+3 of each group).
+// 4h..4h+3 of each group). The scale and bias rows are either global
+// memory or a copy in LDS (sb_block below); the codes are always global.
 template <int D>
 struct CodeRing {
     uint4 q[D];
@@ -305,11 +306,61 @@ struct CodeRing {
 #pragma unroll
         for (int d = 0; d < D; ++d) fill(d, d);
     }
+    // codes only (the scale and bias rows are set later)
+    __device__ __forceinline__ void init_q(const uint32_t* w, int g) {
+        wrow = w;
+        G = g;
+#pragma unroll
+        for (int d = 0; d < D; ++d) q[d] = *(const uint4*)(wrow + (int64_t)min(d, G - 1) * 8);
+    }
+    __device__ __forceinline__ void init_sb(const uint16_t* sr, const uint16_t* br) {
+        srow = sr;
+        brow = br;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int g = min(d, G - 1);
+            s[d] = srow[g];
+            b[d] = brow[g];
+        }
+    }
     __device__ __forceinline__ void fill(int d, int g) {
         g = min(g, G - 1);
         q[d] = *(const uint4*)(wrow + (int64_t)g * 8);
         s[d] = srow[g];
         b[d] = brow[g];
+    }
+};
+
+// Scales and biases of a wave's 32 consecutive weight rows through LDS. Read
+// per lane (one row each), every 2-byte value would cost its own cache-line
+// access; the rows' values are one contiguous block of 32 G halfwords (64 G
+// bytes, 16-byte aligned when the arrays are), so the wave copies each block
+// with 16-byte loads, lane after lane, and the ring reads its values from LDS.
+// Up to SB_GMAX groups per row (4 loads per lane per block).
+constexpr int SB_GMAX = 64;
+struct SbBlock {
+    uint4 vs[SB_GMAX / 16], vb[SB_GMAX / 16];
+    // issue the loads of both blocks (indices clamp to the block)
+    __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b, int G) {
+        const int lane = threadIdx.x & 63, n16 = 4 * G;
+#pragma unroll
+        for (int k = 0; k < SB_GMAX / 16; ++k) {
+            const int i = min(lane + 64 * k, n16 - 1);
+            vs[k] = ((const uint4*)s)[i];
+            vb[k] = ((const uint4*)b)[i];
+        }
+    }
+    // store them at dst: [32 G] scales, then [32 G] biases
+    __device__ __forceinline__ void store(uint16_t* dst, int G) const {
+        const int lane = threadIdx.x & 63, n16 = 4 * G;
+#pragma unroll
+        for (int k = 0; k < SB_GMAX / 16; ++k) {
+            const int i = lane + 64 * k;
+            if (i < n16) {
+                ((uint4*)dst)[i] = vs[k];
+                ((uint4*)dst)[n16 + i] = vb[k];
+            }
+        }
     }
 };
 
@@ -322,9 +373,15 @@ struct CodeRing {
 // data-dependent exits (an exit inside a round would make the compiler wait
 // for every load in flight where the paths join); the last partial round runs
 // with checks.
-template <int PLANES, bool F16, int NW, int NQ>
+//
+// Prologue: the first stage of activations is requested first, then issue()
+// requests the ring's first weights (a wave's loads return in order, so the
+// staging waits only for the activations), and finish() runs after the
+// staging stores, before the barrier.
+template <int PLANES, bool F16, int NW, int NQ, typename Issue, typename Finish>
 __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t* const (&row)[PLANES],
-                                              CodeRing<XD>& ring, floatx16& acc) {
+                                              CodeRing<XD>& ring, floatx16& acc, Issue&& issue,
+                                              Finish&& finish) {
     using XS = XStage<PLANES, F16, NW>;
     constexpr int SPR = XD / XSG;
     const int lane = threadIdx.x & 63;
@@ -339,7 +396,11 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
     uint4 xr0[PLANES][XS::UPT], xr1[PLANES][XS::UPT];
     XS::load(row, 0, G, xr0);
     if constexpr (XPF == 2) XS::load(row, XSG, G, xr1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
     XS::store(lds, xsum_raw, xr0);
+    finish();
     __syncthreads();
     auto stage = [&](const int st, auto sjc, auto checked) __attribute__((always_inline)) {
         constexpr int sj = decltype(sjc)::value;   // st mod SPR (rounds hold SPR stages)
@@ -423,19 +484,20 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
 }
 
 // Runs stream_expert with NQ = ceil(M / 8) fixed at compile time.
-template <int PLANES, bool F16, int NW>
+template <int PLANES, bool F16, int NW, typename Issue, typename Finish>
 __device__ __forceinline__ void stream_expert_m(int M, int G, uint4* lds,
                                                 const uint16_t* const (&row)[PLANES],
-                                                CodeRing<XD>& ring, floatx16& acc) {
+                                                CodeRing<XD>& ring, floatx16& acc, Issue&& issue,
+                                                Finish&& finish) {
     const int nq = (M + 7) / 8;
     if (nq <= 1)
-        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, acc);
+        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, acc, issue, finish);
     else if (nq == 2)
-        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, acc);
+        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, acc, issue, finish);
     else if (nq == 3)
-        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, acc);
+        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, acc, issue, finish);
     else
-        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, acc);
+        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, acc, issue, finish);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,12 +516,14 @@ struct GuArgs {
 // Workgroup = (32-row block, GT = NW / 2 column tiles of 32): waves 0..GT-1
 // the gate rows of tiles GT q + w, waves GT..NW-1 the matching up rows.
 // Routed blocks come first (expert from the row-block table), then the
-// shared expert's blocks of all T tokens.
-template <bool F16>
+// shared expert's blocks of all T tokens. SBL: scales and biases through
+// LDS (SbBlock; dynamic LDS of NW x 128 G bytes).
+template <bool F16, bool SBL>
 __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(XWPE, XWPE))) void moe_gu_kernel(GuArgs a) {
     constexpr int NW = GU_WAVES, GT = NW / 2;
     __shared__ __align__(16) uint4 lds[XStage<1, F16, NW>::LDS_UINT4];
     __shared__ float zb[GT][32][33];
+    extern __shared__ __align__(16) uint4 sbl_raw[];   // SBL: [NW][2][32 G] halfwords
     const int ntc = a.I / 32, ntcs = a.Is / 32;
     const int nq = (ntc + GT - 1) / GT, nqs = (ntcs + GT - 1) / GT;
     const int item = blockIdx.x;
@@ -504,9 +568,25 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     const int h = lane >> 5, l32 = lane & 31;
     const int G = a.H / 64;
     const int tile = min(GT * q + wave % GT, ntl - 1);   // clamped: waves past the last tile store nothing
-    const int col = (wave >= GT ? Iw : 0) + 32 * tile + l32;   // weight row of this lane
+    const int c0 = (wave >= GT ? Iw : 0) + 32 * tile;   // first weight row of this wave
+    const int col = c0 + l32;                            // weight row of this lane
     CodeRing<XD> ring;
-    ring.init(Wq + (int64_t)col * (a.H / 8) + 4 * h, Ws + (int64_t)col * G, Wb + (int64_t)col * G, G);
+    SbBlock sbb;
+    uint16_t* sbl = (uint16_t*)sbl_raw + wave * 64 * G;   // SBL: this wave's block copy
+    auto issue = [&]() __attribute__((always_inline)) {
+        if constexpr (SBL) {
+            sbb.load(Ws + (int64_t)c0 * G, Wb + (int64_t)c0 * G, G);
+            ring.init_q(Wq + (int64_t)col * (a.H / 8) + 4 * h, G);
+        } else {
+            ring.init(Wq + (int64_t)col * (a.H / 8) + 4 * h, Ws + (int64_t)col * G, Wb + (int64_t)col * G, G);
+        }
+    };
+    auto finish = [&]() __attribute__((always_inline)) {
+        if constexpr (SBL) {
+            sbb.store(sbl, G);   // read back below by other lanes of this wave only
+            ring.init_sb(sbl + l32 * G, sbl + 32 * G + l32 * G);
+        }
+    };
     // staged row of this thread (rows past M repeat row M - 1; their results
     // are never stored)
     const int sr = min(tid / (NW * 2), M - 1);
@@ -515,7 +595,7 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, acc);
+    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, acc, issue, finish);
 
     // up waves -> LDS; each gate wave forms h' = p GELU(gate) up
     if (wave >= GT) {
@@ -608,13 +688,15 @@ __global__ __launch_bounds__(64 * DN_WAVES) __attribute__((amdgpu_waves_per_eu(X
     const int n = 32 * NW * o8 + 32 * wave + l32;
     const int nc = min(n, a.H - 1);
     CodeRing<XD> ring;
-    ring.init(Wq + (int64_t)nc * (K / 8) + 4 * h, Ws + (int64_t)nc * G, Wb + (int64_t)nc * G, G);
+    auto issue = [&]() __attribute__((always_inline)) {
+        ring.init(Wq + (int64_t)nc * (K / 8) + 4 * h, Ws + (int64_t)nc * G, Wb + (int64_t)nc * G, G);
+    };
     const int64_t sro = (int64_t)(row0 + min(tid / (NW * 2), M - 1)) * K;
     const uint16_t* const arow[2] = {Ahi + sro, Alo + sro};
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, acc);
+    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, acc, issue, [] {});
 
     if (n < a.H) {
 #pragma unroll
@@ -675,10 +757,22 @@ hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float*
     ga.w = w;
     constexpr int GT = GU_WAVES / 2;
     const int gu_items = rb_max * ((m.I / 32 + GT - 1) / GT) + rb_shared * ((m.Is / 32 + GT - 1) / GT);
-    if (xkind == X_F16)
-        hipLaunchKernelGGL(moe_gu_kernel<true>, dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
-    else
-        hipLaunchKernelGGL(moe_gu_kernel<false>, dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
+    // scales and biases through LDS when the rows are short enough (the
+    // arrays are 16-byte aligned: the boundary rejects others)
+    const int Ggu = m.H / 64;
+    const bool sbl = Ggu <= SB_GMAX;
+    const size_t sbl_bytes = sbl ? (size_t)GU_WAVES * 128 * Ggu : 0;
+    if (xkind == X_F16) {
+        if (sbl)
+            hipLaunchKernelGGL((moe_gu_kernel<true, true>), dim3(gu_items), dim3(64 * GU_WAVES), sbl_bytes, st, ga);
+        else
+            hipLaunchKernelGGL((moe_gu_kernel<true, false>), dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
+    } else {
+        if (sbl)
+            hipLaunchKernelGGL((moe_gu_kernel<false, true>), dim3(gu_items), dim3(64 * GU_WAVES), sbl_bytes, st, ga);
+        else
+            hipLaunchKernelGGL((moe_gu_kernel<false, false>), dim3(gu_items), dim3(64 * GU_WAVES), 0, st, ga);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -171,6 +171,15 @@ def test_invalid_expert_ids_contribute_nothing():
     assert_within(y, yr, a, "invalid ids")
 
 
+def test_prefill_long_rows():
+    # H / 64 = 65 groups: more than the gate+up kernel copies into LDS, so its
+    # scales and biases come per lane from global memory (every shorter layer
+    # here takes the LDS copy)
+    mw = synth.moe_weights(E=4, H=4160, I=64, Is=64, cfg=409, layer=0)
+    xb = synth.x_f16(3, 4160, cfg=409, set_id=0)
+    check_layer(mw, xb, 2, what="H=4160")
+
+
 def test_deterministic():
     mw = synth.moe_weights(**TINY, cfg=405, layer=0)
     w = dev_moe(mw)
