@@ -162,6 +162,49 @@ __device__ __forceinline__ int opaque(int v) {
     return r;
 }
 
+// Scales and biases of a workgroup's 64 columns through LDS (SBL): read per
+// lane, a column each, every 2-byte value costs its own cache-line access.
+// The tile's 64 rows are one contiguous run of 64 G halfwords in each array
+// (16-byte aligned: the arrays are, and tiles start every 64 rows), copied
+// with 16-byte loads by all NTH threads before the first barrier; the ring
+// then reads its values from LDS. In LDS each row is padded by one dword
+// (rows of G + 2 halfwords, an odd number of dwords when 8 divides G), so
+// the 32 rows a wave reads at once fall in different banks. For whole column
+// tiles (N % 64 == 0), 8 | G and G <= CH_SB_GMAX.
+constexpr int CH_SB_GMAX = 64;
+template <int NTH>
+struct ChunkSb {
+    static constexpr int KMAX = (16 * CH_SB_GMAX + NTH - 1) / NTH;   // uint4 per thread
+    uint4 v[KMAX];
+    // all loads issued (indices clamp to the two runs, [8 G] uint4 each)
+    __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b, int G) {
+        const int n8 = 8 * G;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int i = min((int)threadIdx.x + NTH * k, 2 * n8 - 1);
+            const uint4* src = i < n8 ? (const uint4*)s + i : (const uint4*)b + (i - n8);
+            v[k] = *src;
+        }
+    }
+    // dst: [64 rows][G + 2] scales, then the same for the biases
+    __device__ __forceinline__ void store(uint32_t* dst, int G) const {
+        const int n8 = 8 * G, upr = G / 8, rdw = G / 2 + 1;   // uint4 per row, dwords per LDS row
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int i = threadIdx.x + NTH * k;
+            if (i < 2 * n8) {
+                const int arr = i >= n8, j = i - arr * n8;
+                const int r = j / upr, c = j - r * upr;
+                uint32_t* d = dst + (arr * 64 + r) * rdw + 4 * c;
+                d[0] = v[k].x;
+                d[1] = v[k].y;
+                d[2] = v[k].z;
+                d[3] = v[k].w;
+            }
+        }
+    }
+};
+
 // SG groups per barrier. A K-set of 2 WM waves covers the tile: wave
 // (wm, wn) computes rows [32 MB wm, 32 MB (wm + 1)) x columns [32 wn, 32 wn
 // + 32) as MB 32x32 MFMA blocks. The workgroup has NKS K-sets, set ks taking
@@ -182,7 +225,10 @@ __device__ __forceinline__ int opaque(int v) {
 // F16: fp16 activations on an fp16 MFMA, else bf16; the operand is the code
 // q either way. The bias term b Xsum, of the size of the result, runs on the
 // matrix core once per stage.
-template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false>
+//
+// SBL: scales and biases from an LDS copy (ChunkSb), placed after the
+// staging buffers in the dynamic LDS.
+template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false, bool SBL = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
     constexpr int SPR = D / SG;     // stages per round
@@ -214,8 +260,10 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     const int n = ct * CH_NT + wn * 32 + l32;                // this lane's column
     const int nc = min(n, a.N - 1);
     const uint32_t* wrow = a.wq + (int64_t)nc * wpr + 4 * h;  // words 4h..4h+3 of group 0
-    const uint16_t* srow = a.s + (int64_t)nc * G;
-    const uint16_t* brow = a.b + (int64_t)nc * G;
+    // SBL: the tile's copy in LDS ([64 G] scales, then [64 G] biases)
+    uint16_t* sbl = (uint16_t*)(smem + L::bytes / 16);
+    const uint16_t* srow = SBL ? sbl + (nc - ct * CH_NT) * (G + 2) : a.s + (int64_t)nc * G;
+    const uint16_t* brow = SBL ? sbl + (64 + nc - ct * CH_NT) * (G + 2) : a.b + (int64_t)nc * G;
 
     floatx16 acc[MB];
 #pragma unroll
@@ -229,20 +277,42 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     // force a wait on each refill.
     uint4 bq[DW];
     uint32_t bs[DW], bb[DW];
-#pragma unroll
-    for (int e = 0; e < DW; ++e) {
-        const int g = rot_group(NKS * e + ks, G, rot);
-        bq[e] = *(const uint4*)(wrow + (int64_t)g * 8);
-        bs[e] = srow[g];
-        bb[e] = brow[g];
-    }
     // xr[i]: X of stage st + 1 + i while stage st runs (a ring when XD = 2;
     // stage parity picks the slot, and rounds hold an even number of stages)
     uint4 xr[XD][SG][IO::XPT];
-    IO::load(a, m0, 0, G, rot, xr[0]);
-    IO::store(xs_raw, xsum_raw, xr[0]);
-    if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
-    __syncthreads();
+    if constexpr (SBL) {
+        // X first, then the scale/bias runs, then the codes: a wave's loads
+        // return in order, so each store below waits only for its own data
+        IO::load(a, m0, 0, G, rot, xr[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        ChunkSb<128 * WM * NKS> sbc;
+        sbc.load(a.s + (int64_t)ct * CH_NT * G, a.b + (int64_t)ct * CH_NT * G, G);
+#pragma unroll
+        for (int e = 0; e < DW; ++e) bq[e] = *(const uint4*)(wrow + (int64_t)rot_group(NKS * e + ks, G, rot) * 8);
+        __builtin_amdgcn_sched_barrier(0);
+        IO::store(xs_raw, xsum_raw, xr[0]);
+        sbc.store((uint32_t*)sbl, G);
+        if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < DW; ++e) {
+            const int g = rot_group(NKS * e + ks, G, rot);
+            bs[e] = srow[g];
+            bb[e] = brow[g];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < DW; ++e) {
+            const int g = rot_group(NKS * e + ks, G, rot);
+            bq[e] = *(const uint4*)(wrow + (int64_t)g * 8);
+            bs[e] = srow[g];
+            bb[e] = brow[g];
+        }
+        IO::load(a, m0, 0, G, rot, xr[0]);
+        IO::store(xs_raw, xsum_raw, xr[0]);
+        if constexpr (XD == 2) IO::load(a, m0, SG, G, rot, xr[1]);
+        __syncthreads();
+    }
 
     // one group (step g, slot e): the row blocks' MFMA chains in turn into
     // a two-slot ring P; block mb - 1's scaling, acc += s P, is issued after
@@ -401,18 +471,28 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     }
 }
 
-template <int SG, int D, int MB, int WM, int NKS, bool F16>
+template <int SG, int D, int MB, int WM, int NKS, bool F16, bool SBL = false>
 static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st) {
     constexpr int MT = 32 * MB * WM;
     const int RT = (a.M + MT - 1) / MT;
     const int grid = ((a.ncol_tiles + 7) / 8) * 8 * RT;
-    const size_t lds = ChunkLds<SG, MT, F16>::bytes;
+    const size_t lds = ChunkLds<SG, MT, F16>::bytes + (SBL ? (size_t)256 * (a.K / 64 + 2) : 0);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     constexpr int threads = 128 * WM * NKS;
-    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16>;
+    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16, SBL>;
     (void)occupancy((const void*)kern, threads, lds);  // sets the dynamic-LDS limit once
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
     return hipGetLastError();
+}
+
+// Up to 64 rows the tile's scales and biases go through LDS when the column
+// tiles are whole and the rows short enough (ChunkSb).
+template <int SG, int D, int MB, int WM, int NKS, bool F16>
+static hipError_t launch_chunk_sb(const ChunkArgs& a, hipStream_t st) {
+    const int G = a.K / 64;
+    if (a.N % CH_NT == 0 && G % 8 == 0 && G <= CH_SB_GMAX)
+        return launch_chunk_cfg<SG, D, MB, WM, NKS, F16, true>(a, st);
+    return launch_chunk_cfg<SG, D, MB, WM, NKS, F16, false>(a, st);
 }
 
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
@@ -437,12 +517,12 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
 // column waves x 4 K-sets = 8 waves (2 per SIMD). All use 4 groups per stage
 // and a ring of 8 groups.
     if (xkind == X_F16) {
-        if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2, true>(a, st);
-        if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4, true>(a, st);
+        if (M <= 32) return launch_chunk_sb<4, 8, 1, 1, 2, true>(a, st);
+        if (M <= 64) return launch_chunk_sb<4, 8, 2, 1, 4, true>(a, st);
         return launch_chunk_cfg<4, 8, 4, 1, 4, true>(a, st);
     }
-    if (M <= 32) return launch_chunk_cfg<4, 8, 1, 1, 2, false>(a, st);
-    if (M <= 64) return launch_chunk_cfg<4, 8, 2, 1, 4, false>(a, st);
+    if (M <= 32) return launch_chunk_sb<4, 8, 1, 1, 2, false>(a, st);
+    if (M <= 64) return launch_chunk_sb<4, 8, 2, 1, 4, false>(a, st);
     return launch_chunk_cfg<4, 8, 4, 1, 4, false>(a, st);
 }
 
