@@ -329,6 +329,9 @@ struct CodeRing {
         s[d] = srow[g];
         b[d] = brow[g];
     }
+    __device__ __forceinline__ void fill_q(int d, int g) {
+        q[d] = *(const uint4*)(wrow + (int64_t)min(g, G - 1) * 8);
+    }
 };
 
 // Scales and biases of a wave's 32 consecutive weight rows through LDS. Read
@@ -364,6 +367,42 @@ struct SbBlock {
     }
 };
 
+// Where stream_expert takes the scales and biases from. SbInRing: the ring
+// holds them (per lane from global memory, or from an SbBlock copy).
+struct SbInRing {
+    static constexpr bool staged = false;
+    __device__ __forceinline__ void load(int) {}
+    __device__ __forceinline__ void store(int) {}
+    __device__ __forceinline__ void read(int, uint2&, uint2&) const {}
+};
+
+// SbStaged: staged per stage with the activations, for a workgroup of 4 waves
+// over 128 consecutive weight rows. Thread t requests the stage's 4 values of
+// row t mod 128 in array t / 128 (scales, then biases): those rows lie a few
+// cache lines apart, so a wave instruction touches a few lines instead of
+// one per lane. They go to LDS with the activations; a lane then reads its
+// row's 4 scales and 4 biases with two 8-byte LDS reads.
+struct SbStaged {
+    static constexpr bool staged = true;
+    uint2 (*lds)[2][128];   // [2 buffers][2 arrays][128 rows]
+    const uint16_t* row;    // this thread's row of its array
+    int G;
+    uint32_t v[4];
+    __device__ __forceinline__ void load(int st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = row[min(4 * st + i, G - 1)];
+    }
+    __device__ __forceinline__ void store(int buf) {
+        lds[buf][threadIdx.x / 128][threadIdx.x % 128] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+    }
+    // this lane's row of the workgroup: 32 wave + l32
+    __device__ __forceinline__ void read(int buf, uint2& s4, uint2& b4) const {
+        const int r = 32 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) + (threadIdx.x & 31);
+        s4 = lds[buf][0][r];
+        b4 = lds[buf][1][r];
+    }
+};
+
 // Streams the G groups of a wave's weight row against the staged activation
 // planes: acc (D layout, 32 rows x this lane's column) += sum over groups of
 // s P_g + b Xsum_g, with P_g the group's product on the codes q. The first part
@@ -378,10 +417,11 @@ struct SbBlock {
 // requests the ring's first weights (a wave's loads return in order, so the
 // staging waits only for the activations), and finish() runs after the
 // staging stores, before the barrier.
-template <int PLANES, bool F16, int NW, int NQ, typename Issue, typename Finish>
+template <int PLANES, bool F16, int NW, int NQ, typename Sb, typename Issue, typename Finish>
 __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t* const (&row)[PLANES],
-                                              CodeRing<XD>& ring, floatx16& acc, Issue&& issue,
+                                              CodeRing<XD>& ring, Sb& sb, floatx16& acc, Issue&& issue,
                                               Finish&& finish) {
+    static_assert(!Sb::staged || NW == 4, "staged scales: 4 waves over 128 rows");
     using XS = XStage<PLANES, F16, NW>;
     constexpr int SPR = XD / XSG;
     const int lane = threadIdx.x & 63;
@@ -396,10 +436,12 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
     uint4 xr0[PLANES][XS::UPT], xr1[PLANES][XS::UPT];
     XS::load(row, 0, G, xr0);
     if constexpr (XPF == 2) XS::load(row, XSG, G, xr1);
+    sb.load(0);
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);
     XS::store(lds, xsum_raw, xr0);
+    sb.store(0);
     finish();
     __syncthreads();
     auto stage = [&](const int st, auto sjc, auto checked) __attribute__((always_inline)) {
@@ -409,6 +451,14 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
         auto& xin = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 1) return xr1; else return xr0; }();
         auto& xout = [&]() -> auto& { if constexpr (XPF == 2 && sj % 2 == 0) return xr1; else return xr0; }();
         XS::load(row, (st + XPF) * XSG, G, xin);
+        sb.load(st + 1);
+        // staged scales and biases of this stage (4 each, 16-bit halves)
+        uint2 s4, b4;
+        sb.read(buf, s4, b4);
+        auto half16 = [](const uint2& v, int gi) __attribute__((always_inline)) {
+            const uint32_t w = gi < 2 ? v.x : v.y;
+            return (gi & 1) ? (w >> 16) : (w & 0xFFFFu);
+        };
         // bias of the stage's groups as two MFMAs (groups 2p + h on lane
         // half h), both factors as three bf16 parts (mfma.h: six exact cross
         // products per group, within 2^-25 of the fp32 product)
@@ -416,7 +466,7 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
             float bv[4];
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {   // b
-                bv[gi] = h2f((uint16_t)ring.b[sj * XSG + gi]);
+                bv[gi] = h2f((uint16_t)(Sb::staged ? half16(b4, gi) : ring.b[sj * XSG + gi]));
                 if constexpr (chk)
                     if (st * XSG + gi >= G) bv[gi] = 0.f;
             }
@@ -456,7 +506,7 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
             auto epilogue = [&](const floatx16& P, int d) __attribute__((always_inline)) {
                 // one conversion (folded into each FMA the compiler would
                 // emit the half-rate mixed-precision form)
-                float sf = h2f((uint16_t)ring.s[d]);
+                float sf = h2f((uint16_t)(Sb::staged ? half16(s4, d % XSG) : ring.s[d]));
                 asm volatile("" : "+v"(sf));
                 // rows 8 (i / 4) + 4 h + i % 4: quarter i / 4
 #pragma unroll
@@ -465,11 +515,17 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
             epilogue(P0, d0);
             if (second) epilogue(P1, d1);
             pin(acc);
-            ring.fill(d0, g + XD);   // the slots' contents are dead now
-            ring.fill(d1, g + 1 + XD);
+            if constexpr (Sb::staged) {   // the slots' contents are dead now
+                ring.fill_q(d0, g + XD);
+                ring.fill_q(d1, g + 1 + XD);
+            } else {
+                ring.fill(d0, g + XD);
+                ring.fill(d1, g + 1 + XD);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
         XS::store(lds + (buf ^ 1) * XS::BUF, xsum_raw + (buf ^ 1) * 32 * XSG, xout);
+        sb.store(buf ^ 1);
         __syncthreads();
     };
     const int rounds = G / XD;
@@ -484,20 +540,20 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
 }
 
 // Runs stream_expert with NQ = ceil(M / 8) fixed at compile time.
-template <int PLANES, bool F16, int NW, typename Issue, typename Finish>
+template <int PLANES, bool F16, int NW, typename Sb, typename Issue, typename Finish>
 __device__ __forceinline__ void stream_expert_m(int M, int G, uint4* lds,
                                                 const uint16_t* const (&row)[PLANES],
-                                                CodeRing<XD>& ring, floatx16& acc, Issue&& issue,
-                                                Finish&& finish) {
+                                                CodeRing<XD>& ring, Sb& sb, floatx16& acc,
+                                                Issue&& issue, Finish&& finish) {
     const int nq = (M + 7) / 8;
     if (nq <= 1)
-        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, acc, issue, finish);
+        stream_expert<PLANES, F16, NW, 1>(G, lds, row, ring, sb, acc, issue, finish);
     else if (nq == 2)
-        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, acc, issue, finish);
+        stream_expert<PLANES, F16, NW, 2>(G, lds, row, ring, sb, acc, issue, finish);
     else if (nq == 3)
-        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, acc, issue, finish);
+        stream_expert<PLANES, F16, NW, 3>(G, lds, row, ring, sb, acc, issue, finish);
     else
-        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, acc, issue, finish);
+        stream_expert<PLANES, F16, NW, 4>(G, lds, row, ring, sb, acc, issue, finish);
 }
 
 // ---------------------------------------------------------------------------
@@ -595,7 +651,8 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, acc, issue, finish);
+    SbInRing sbr;
+    stream_expert_m<1, F16, NW>(M, G, lds, xrow, ring, sbr, acc, issue, finish);
 
     // up waves -> LDS; each gate wave forms h' = p GELU(gate) up
     if (wave >= GT) {
@@ -642,10 +699,12 @@ struct DnArgs {
 
 // Workgroup = (32-row block, 32 NW columns of H); wave w takes columns
 // 32 NW o + 32 w + (0..31). The activation h' arrives as bf16 hi + lo planes,
-// so each step runs two MFMAs against the same codes.
+// so each step runs two MFMAs against the same codes. Scales and biases are
+// staged per stage (SbStaged).
 __global__ __launch_bounds__(64 * DN_WAVES) __attribute__((amdgpu_waves_per_eu(XWPE, XWPE))) void moe_dn_kernel(DnArgs a) {
     constexpr int NW = DN_WAVES;
     __shared__ __align__(16) uint4 lds[XStage<2, false, NW>::LDS_UINT4];
+    __shared__ uint2 sbs_lds[2][2][128];
     const int ntH = (a.H + 32 * NW - 1) / (32 * NW);
     const int item = blockIdx.x;
     const int rbi = item / ntH, o8 = item - rbi * ntH;
@@ -688,15 +747,21 @@ __global__ __launch_bounds__(64 * DN_WAVES) __attribute__((amdgpu_waves_per_eu(X
     const int n = 32 * NW * o8 + 32 * wave + l32;
     const int nc = min(n, a.H - 1);
     CodeRing<XD> ring;
-    auto issue = [&]() __attribute__((always_inline)) {
-        ring.init(Wq + (int64_t)nc * (K / 8) + 4 * h, Ws + (int64_t)nc * G, Wb + (int64_t)nc * G, G);
-    };
+    auto issue = [&]() __attribute__((always_inline)) { ring.init_q(Wq + (int64_t)nc * (K / 8) + 4 * h, G); };
+    SbStaged sbs;
+    sbs.lds = sbs_lds;
+    sbs.G = G;
+    {
+        // thread t stages row t mod 128 of the workgroup (clamped) in array t / 128
+        const int srow = min(32 * NW * o8 + (tid & 127), a.H - 1);
+        sbs.row = (tid < 128 ? Ws : Wb) + (int64_t)srow * G;
+    }
     const int64_t sro = (int64_t)(row0 + min(tid / (NW * 2), M - 1)) * K;
     const uint16_t* const arow[2] = {Ahi + sro, Alo + sro};
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, acc, issue, [] {});
+    stream_expert_m<2, false, NW>(M, G, lds, arow, ring, sbs, acc, issue, [] {});
 
     if (n < a.H) {
 #pragma unroll
