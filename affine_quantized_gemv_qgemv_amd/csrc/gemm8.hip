@@ -21,9 +21,10 @@
 // weights' own size.
 
 // Tiling: a workgroup owns 32 tokens x 32 outputs and has 8 waves that take
-// alternate groups of K (wave w: groups w, w + 8, ...), each loading up to
-// four of its groups at once before using them; the 8 partial sums are added
-// in LDS in a fixed order, so results do not depend on timing.
+// alternate groups of K (wave w: groups w, w + 8, ...), each loading six of
+// its groups at once before using them (a 2816-input router in one round);
+// the 8 partial sums are added in LDS in a fixed order, so results do not
+// depend on timing.
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -42,7 +43,7 @@ struct G8Args {
 };
 
 constexpr int G8_WAVES = 8;
-constexpr int G8_SLOTS = 4;   // groups loaded together per wave
+constexpr int G8_SLOTS = 6;   // groups loaded together per wave
 
 // Two code bytes of w (bytes j, j + 1) beside magic bytes m:
 // dword = [w.b(j), m, w.b(j+1), m].
@@ -87,9 +88,14 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
             sv[j] = srow[g];
             bv[j] = brow[g];
         }
+        // every slot's loads are in flight before the first is used: slots
+        // past G run on their clamped copies with zero factors rather than
+        // being skipped (a branch around them would let the compiler sink
+        // each slot's loads into it, one memory round trip per group)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < G8_SLOTS; ++j) {
-            if (g0 + G8_WAVES * j >= G) break;   // uniform
+            const bool valid = g0 + G8_WAVES * j < G;   // uniform
             const uint32_t wv[8] = {wb[j][0].x, wb[j][0].y, wb[j][0].z, wb[j][0].w,
                                     wb[j][1].x, wb[j][1].y, wb[j][1].z, wb[j][1].w};
             floatx16 P, X1;
@@ -123,8 +129,8 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
                                                                  X1, 0, 0, 0);
                 }
             }
-            const float sf = h2f(sv[j]);
-            const float bf = fmaf(128.f, sf, h2f(bv[j]));   // b + 128 s
+            const float sf = valid ? h2f(sv[j]) : 0.f;
+            const float bf = valid ? fmaf(128.f, sf, h2f(bv[j])) : 0.f;   // b + 128 s
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf(bf, X1[i], fmaf(sf, P[i], acc[i]));
         }
