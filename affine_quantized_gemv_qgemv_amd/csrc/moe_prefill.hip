@@ -233,14 +233,17 @@ constexpr int DN_WAVES = 4;  // down workgroup: 4 column tiles
 // phases (start, stage barriers) overlap the other's work
 constexpr int XWPE = 2;
 
-// LDS: [2 buffers][PLANES][XSG groups][32 rows][XS_STRIDE] uint4, then the
-// per-group row sums (over the planes) as bias-product parts
-// (bias_row_parts), xsum [2 buffers][32 rows][XSG] uint2.
+// LDS: [2 buffers][PLANES][XSG groups][GS] uint4 (a group = 32 rows of
+// XS_STRIDE uint4 plus one, so that the staging stores of a row's groups
+// start in different banks), then the per-group row sums (over the planes)
+// as bias-product parts (bias_row_parts), xsum [2 buffers][XSG][32 rows]
+// uint2 (row-contiguous: the lanes of a bias read hit distinct banks).
 // NW waves stage: TPG = NW / 2 threads share a (row, group) and each holds
 // UPT = 8 / TPG of its 16-byte chunks.
 template <int PLANES, bool F16, int NW>
 struct XStage {
-    static constexpr int PER = XSG * 32 * XS_STRIDE;   // uint4 per plane per buffer
+    static constexpr int GS = 32 * XS_STRIDE + 1;       // uint4 per staged group
+    static constexpr int PER = XSG * GS;                // uint4 per plane per buffer
     static constexpr int BUF = PLANES * PER;
     static constexpr int SUMS = 2 * 32 * XSG;          // uint2 (both buffers)
     static constexpr int LDS_UINT4 = 2 * BUF + SUMS / 2;
@@ -271,7 +274,7 @@ struct XStage {
         float acc = 0.f;
 #pragma unroll
         for (int pl = 0; pl < PLANES; ++pl) {
-            uint4* dst = buf + pl * PER + (gi * 32 + rr) * XS_STRIDE + c;
+            uint4* dst = buf + pl * PER + gi * GS + rr * XS_STRIDE + c;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
                 const uint4 v = r[pl][i];
@@ -284,7 +287,7 @@ struct XStage {
         }
         acc = seg_sum<TPG>(acc);   // the TPG adjacent lanes of (row, group)
         // the TPG threads of (row, group) store the same parts
-        xsum[rr * XSG + gi] = bias_row_parts(acc);
+        xsum[gi * 32 + rr] = bias_row_parts(acc);
     }
 };
 
@@ -339,8 +342,12 @@ struct CodeRing {
 // access; the rows' values are one contiguous block of 32 G halfwords (64 G
 // bytes, 16-byte aligned when the arrays are), so the wave copies each block
 // with 16-byte loads, lane after lane, and the ring reads its values from LDS.
-// Up to SB_GMAX groups per row (4 loads per lane per block).
+// For even G the rows are stored RS = 2 ((G / 2) | 1) halfwords apart (an odd
+// number of dwords, so the 32 rows a wave reads at once fall in different
+// banks); for odd G they stay G apart. Up to SB_GMAX groups per row (4 loads
+// per lane per block); the LDS copy takes 2 x 32 RS halfwords.
 constexpr int SB_GMAX = 64;
+__host__ __device__ constexpr int sb_row_stride(int G) { return G % 2 ? G : 2 * ((G / 2) | 1); }
 struct SbBlock {
     uint4 vs[SB_GMAX / 16], vb[SB_GMAX / 16];
     // issue the loads of both blocks (indices clamp to the block)
@@ -353,15 +360,35 @@ struct SbBlock {
             vb[k] = ((const uint4*)b)[i];
         }
     }
-    // store them at dst: [32 G] scales, then [32 G] biases
+    // store them at dst: [32 rows][RS] scales, then the same for the biases
     __device__ __forceinline__ void store(uint16_t* dst, int G) const {
-        const int lane = threadIdx.x & 63, n16 = 4 * G;
+        const int lane = threadIdx.x & 63, n16 = 4 * G, rs = sb_row_stride(G);
+        if (G % 2) {
+#pragma unroll
+            for (int k = 0; k < SB_GMAX / 16; ++k) {
+                const int i = lane + 64 * k;
+                if (i < n16) {
+                    ((uint4*)dst)[i] = vs[k];
+                    ((uint4*)dst)[n16 + i] = vb[k];
+                }
+            }
+            return;
+        }
+        // dword j of a block: row j / (G / 2), column j mod (G / 2)
+        const int rdw = G / 2, prdw = rs / 2;
+        uint32_t* d = (uint32_t*)dst;
 #pragma unroll
         for (int k = 0; k < SB_GMAX / 16; ++k) {
             const int i = lane + 64 * k;
             if (i < n16) {
-                ((uint4*)dst)[i] = vs[k];
-                ((uint4*)dst)[n16 + i] = vb[k];
+                const uint32_t ws[4] = {vs[k].x, vs[k].y, vs[k].z, vs[k].w};
+                const uint32_t wb[4] = {vb[k].x, vb[k].y, vb[k].z, vb[k].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * i + e, r = j / rdw, c = j - r * rdw;
+                    d[r * prdw + c] = ws[e];
+                    d[(32 + r) * prdw + c] = wb[e];
+                }
             }
         }
     }
@@ -470,10 +497,10 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
                 if constexpr (chk)
                     if (st * XSG + gi >= G) bv[gi] = 0.f;
             }
-            const uint2* xp = xsum_raw + buf * 32 * XSG + opaque_i(l32 * XSG + h);
+            const uint2* xp = xsum_raw + buf * 32 * XSG + opaque_i(h * 32 + l32);
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                acc = mfma16<false>(bias_a_operand(xp[2 * p]),
+                acc = mfma16<false>(bias_a_operand(xp[2 * p * 32]),
                                     bias_b_operand(h ? bv[2 * p + 1] : bv[2 * p]), acc);
         }
         const uint4* xs = lds + opaque_i(buf * XS::BUF + l32 * XS_STRIDE + 4 * h);
@@ -499,8 +526,8 @@ __device__ __forceinline__ void stream_expert(int G, uint4* lds, const uint16_t*
                 const uint4 b1 = codes_p<F16>(w1[stp]);
 #pragma unroll
                 for (int pl = 0; pl < PLANES; ++pl) {
-                    P0 = mfma16<F16>(xs[pl * XS::PER + g0i * 32 * XS_STRIDE + stp], b0, P0);
-                    P1 = mfma16<F16>(xs[pl * XS::PER + (g0i + 1) * 32 * XS_STRIDE + stp], b1, P1);
+                    P0 = mfma16<F16>(xs[pl * XS::PER + g0i * XS::GS + stp], b0, P0);
+                    P1 = mfma16<F16>(xs[pl * XS::PER + (g0i + 1) * XS::GS + stp], b1, P1);
                 }
             }
             auto epilogue = [&](const floatx16& P, int d) __attribute__((always_inline)) {
@@ -573,7 +600,7 @@ struct GuArgs {
 // the gate rows of tiles GT q + w, waves GT..NW-1 the matching up rows.
 // Routed blocks come first (expert from the row-block table), then the
 // shared expert's blocks of all T tokens. SBL: scales and biases through
-// LDS (SbBlock; dynamic LDS of NW x 128 G bytes).
+// LDS (SbBlock; dynamic LDS of NW x 128 RS bytes).
 template <bool F16, bool SBL>
 __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(XWPE, XWPE))) void moe_gu_kernel(GuArgs a) {
     constexpr int NW = GU_WAVES, GT = NW / 2;
@@ -628,7 +655,8 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     const int col = c0 + l32;                            // weight row of this lane
     CodeRing<XD> ring;
     SbBlock sbb;
-    uint16_t* sbl = (uint16_t*)sbl_raw + wave * 64 * G;   // SBL: this wave's block copy
+    const int rs = sb_row_stride(G);
+    uint16_t* sbl = (uint16_t*)sbl_raw + wave * 64 * rs;   // SBL: this wave's block copy
     auto issue = [&]() __attribute__((always_inline)) {
         if constexpr (SBL) {
             sbb.load(Ws + (int64_t)c0 * G, Wb + (int64_t)c0 * G, G);
@@ -640,7 +668,7 @@ __global__ __launch_bounds__(64 * GU_WAVES) __attribute__((amdgpu_waves_per_eu(X
     auto finish = [&]() __attribute__((always_inline)) {
         if constexpr (SBL) {
             sbb.store(sbl, G);   // read back below by other lanes of this wave only
-            ring.init_sb(sbl + l32 * G, sbl + 32 * G + l32 * G);
+            ring.init_sb(sbl + l32 * rs, sbl + (32 + l32) * rs);
         }
     };
     // staged row of this thread (rows past M repeat row M - 1; their results
@@ -826,7 +854,7 @@ hipError_t launch_moe_prefill(const MoeArgs& m, const int32_t* idx, const float*
     // arrays are 16-byte aligned: the boundary rejects others)
     const int Ggu = m.H / 64;
     const bool sbl = Ggu <= SB_GMAX;
-    const size_t sbl_bytes = sbl ? (size_t)GU_WAVES * 128 * Ggu : 0;
+    const size_t sbl_bytes = sbl ? (size_t)GU_WAVES * 128 * sb_row_stride(Ggu) : 0;
     if (xkind == X_F16) {
         if (sbl)
             hipLaunchKernelGGL((moe_gu_kernel<true, true>), dim3(gu_items), dim3(64 * GU_WAVES), sbl_bytes, st, ga);
