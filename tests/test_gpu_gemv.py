@@ -152,6 +152,16 @@ def test_one_hot_is_bit_exact(bits):
         y = run_gemv(bits, w, xb).cpu().numpy().astype(np.float64)
         yr, _ = ref_gemv(w, xb)
         assert np.array_equal(y, yr), f"k={k}"
+    # several one-hot vectors in one launch (batch 3..8 of 4-bit codes runs
+    # on the matrix core): each result is s q + b, exact in fp32
+    ks = (0, 9, 63, 64, 127, 128, 1000, 2047)
+    for batch in (3, 8):
+        xb = np.zeros((batch, K), np.uint16)
+        for i in range(batch):
+            xb[i, ks[i]] = one
+        y = run_gemv(bits, w, xb).cpu().numpy().astype(np.float64)
+        yr, _ = ref_gemv(w, xb)
+        assert np.array_equal(y, yr), f"batch={batch}"
 
 
 def test_zero_activation_gives_zero():
@@ -170,6 +180,14 @@ def test_power_of_two_scaling_is_exact():
         xs = (x.astype(np.float32) * 2.0 ** j).astype(np.float16).view(np.uint16)
         yj = run_gemv(4, w, xs).cpu().numpy()
         assert np.array_equal(yj, y1 * np.float32(2.0 ** j)), f"2^{j}"
+    # the matrix-core path (batch 3..8)
+    xb = synth.x_f16(6, K, cfg=205, set_id=1)
+    x = xb.view(np.float16)
+    y1 = run_gemv(4, w, xb).cpu().numpy()
+    for j in (1, 3):
+        xs = (x.astype(np.float32) * 2.0 ** j).astype(np.float16).view(np.uint16)
+        yj = run_gemv(4, w, xs).cpu().numpy()
+        assert np.array_equal(yj, y1 * np.float32(2.0 ** j)), f"batch 6, 2^{j}"
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -177,10 +195,11 @@ def test_constant_and_zero_codes(bits):
     K = 1024
     for kind, c in (("zero", 0), ("const", 5), ("const", (1 << bits) - 1)):
         w = synth.affine_weights(bits, 50, K, cfg=206, set_id=c, codes=kind, const_code=c)
-        xb = synth.x_f16(2, K, cfg=206, set_id=c)
-        y = run_gemv(bits, w, xb).cpu().numpy()
-        yr, a = ref_gemv(w, xb)
-        assert_within(y, yr, a, f"{kind} {c}")
+        for batch in (2, 5):
+            xb = synth.x_f16(batch, K, cfg=206, set_id=c + batch)
+            y = run_gemv(bits, w, xb).cpu().numpy()
+            yr, a = ref_gemv(w, xb)
+            assert_within(y, yr, a, f"{kind} {c} batch={batch}")
 
 
 # Weights at and near zero (TurboFieldfare article, section "성능과 제약":
