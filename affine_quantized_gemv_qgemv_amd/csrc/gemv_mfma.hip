@@ -155,44 +155,44 @@ __global__ __launch_bounds__(1024) void gemv_mfma_kernel(GemvMfmaArgs a) {
         bf.sv = buf_load16(sr, go);
         bf.bv = buf_load16(br, go);
     };
-    // Staging of slice sl in two halves: stage_load requests the nb vectors'
-    // chunks (zero past K; at most GM_SB per thread, the host sizes slices so
-    // that one batch covers a slice), stage_store writes them and the group
-    // sums. Vector-memory counters complete in order, so the activation loads
-    // are requested before the next weight round: the stores then wait for
-    // the activations only.
+    // Staging of slice sl in two halves: stage_load requests the chunks
+    // (8 vector slots x 16 chunks per step, so a thread's items decode with
+    // shifts; slots past nb and steps past the slice are out of range and
+    // cost nothing), stage_store writes them and the group sums. At most
+    // GM_SB chunks per thread: the host sizes slices so that one batch covers
+    // a slice. Vector-memory counters complete in order, so the activation
+    // loads are requested before the next weight round: the stores then
+    // wait for the activations only.
     uint4 xv[GM_SB];
-    const int per = a.nb * 16;   // chunks per step
     // live == false: every offset out of range (the loads return zeros and
     // touch no memory), so a round can request them unconditionally
     auto stage_load = [&](int sl, bool live) __attribute__((always_inline)) {
         const int s0 = sl * SS;
-        const int items = live ? min(SS, a.steps - s0) * per : 0;
+        const int ns = live ? min(SS, a.steps - s0) : 0;
         const auto xr = buf_rsrc(a.x, (int64_t)a.nb * a.K * 2);
 #pragma unroll
         for (int e = 0; e < GM_SB; ++e) {
             const int it = (int)threadIdx.x + e * (int)blockDim.x;
-            const int ss = it / per, rem = it - ss * per;
-            const int k = (s0 + ss) * 128 + 8 * (rem & 15);
-            const bool ok = it < items && k < a.K;
-            xv[e] = buf_load16(xr, ok ? (uint32_t)((rem >> 4) * a.K + k) * 2u : 0x7FFFFFF0u);
+            const int ss = it >> 7, bvec = (it >> 4) & 7, w = it & 15;
+            const bool ok = ss < ns && bvec < a.nb;
+            const uint32_t k = (uint32_t)(s0 + ss) * 128u + 8u * (uint32_t)w;
+            xv[e] = buf_load16(xr, ok ? ((uint32_t)bvec * (uint32_t)a.K + k) * 2u : 0x7FFFFFF0u);
         }
     };
     auto stage_store = [&](int sl) __attribute__((always_inline)) {
-        const int items = min(SS, a.steps - sl * SS) * per;
+        const int ns = min(SS, a.steps - sl * SS);
 #pragma unroll
         for (int e = 0; e < GM_SB; ++e) {
             const int it = (int)threadIdx.x + e * (int)blockDim.x;
-            const int ss = it / per, rem = it - ss * per, bvec = rem >> 4, w = rem & 15;
+            const int ss = it >> 7, bvec = (it >> 4) & 7, w = it & 15;
             const uint32_t h[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
             float sum = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sum += h2f((uint16_t)(h[q] & 0xFFFF)) + h2f((uint16_t)(h[q] >> 16));
-            // the 8 chunks of one group sit in 8 consecutive lanes (per is a
-            // multiple of 16, so they are all in range or all out)
+            // the 8 chunks of one group sit in 8 consecutive lanes
             sum = seg_sum<8>(sum);
-            if (it < items) {
+            if (ss < ns) {
                 // the pairs (x0, x4), (x1, x5), (x2, x6), (x3, x7) of the chunk
                 const uint4 v = xv[e];
                 const uint4 o = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),
@@ -343,7 +343,7 @@ hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* s, const uint16_
     auto slice_cap = [&](int Fc) {
         const size_t fixed = gemv_mfma_lds(0, Fc, nwaves);
         const int lds_cap = budget > fixed ? (int)((budget - fixed) / GM_STEP) : 0;
-        return std::min(lds_cap, GM_SB * nwaves * 64 / (nb * 16));
+        return std::min(lds_cap, GM_SB * nwaves * 64 / 128);
     };
     // a multiple of F U: every wave has the same whole rounds in a full slice
     // (fewer waves per tile when a slice cannot hold that)
