@@ -260,6 +260,31 @@ def test_sliced_k_is_deterministic_and_in_bounds(K, N, batch):
     assert_within(y1.cpu().numpy()[:, rows], yr, a, f"sliced K={K} N={N} batch={batch}")
 
 
+# The matrix-core path (batch 3..8, fp16, K a multiple of 512) streams K
+# through LDS in slices whose length is a multiple of (waves per tile) x 4
+# steps of 128 inputs; when K / 128 is not a multiple of it the last slice is
+# ragged and some waves have no step in it, while every wave still meets the
+# same barriers. Ragged last tiles (N not a multiple of 16) as well.
+RAGGED_SLICES = [(4608, 33, 3), (4608, 300, 8), (5632, 16, 5), (9728, 17, 8), (512, 40, 8),
+                 (14848, 1, 3)]
+
+
+@pytest.mark.parametrize("K,N,batch", RAGGED_SLICES)
+def test_matrix_core_ragged_slices(K, N, batch):
+    print(f"matrix-core K={K} N={N} batch={batch}", flush=True)
+    w = synth.affine_weights(4, N, K, cfg=232, set_id=K + N + batch)
+    xb = synth.x_f16(batch, K, cfg=232, set_id=batch)
+    guard = 4096
+    buf = torch.full((guard + batch * N + guard,), float("nan"), device="cuda")
+    out = buf[guard:guard + batch * N].view(batch, N)
+    y1 = run_gemv(4, w, xb, out=out).clone()
+    y2 = run_gemv(4, w, xb).clone()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + batch * N:]).all()
+    assert torch.equal(y1, y2)
+    yr, a = ref_gemv(w, xb)
+    assert_within(y1.cpu().numpy(), yr, a, f"matrix-core K={K} N={N} batch={batch}")
+
+
 def test_deterministic_and_no_out_of_bounds_writes():
     N, K, batch = 1000, 4096, 3
     w = synth.affine_weights(4, N, K, cfg=207, set_id=0)
