@@ -1,11 +1,14 @@
-// Batch-2..8 GEMV on the matrix core for gfx950: y[b][n] = sum_k w[n][k] x[b][k]
-// with MLX affine 4-bit weights (group 64, w = s q + b) and fp16 activations.
+// GEMV of 2..8 activation vectors on the matrix core for gfx950:
+// y[b][n] = sum_k w[n][k] x[b][k] with MLX affine 4-bit weights (group 64,
+// w = s q + b) and fp16 activations (the launch policy sends batch 3..8
+// here).
 //
 // [TF] jeff.news/article/5193, section "성능과 제약" (performance and
 // constraints): 4-bit affine group-64 weights; the decode GEMV is the hot
 // contraction. With several activation vectors the packed-dot GEMV spends
-// one v_dot2 per code pair and vector, so from batch 2 on its VALU work, not
-// HBM, bounds it. Here the codes go through v_mfma_f32_16x16x32_f16 instead:
+// one v_dot2 per code pair and vector, so its VALU work grows with the batch
+// until it, not HBM, bounds the kernel. Here the codes go through
+// v_mfma_f32_16x16x32_f16 instead:
 //
 //  * B operand = codes. Lane l of a wave holds column n = l mod 16 (a weight
 //    row of the 16-row tile) and the 8 k values 8 (l div 16) + i of each
@@ -28,8 +31,9 @@
 //    groups; a lane swap adds them at the end.
 //  * K is streamed through LDS in slices (all waves of a workgroup consume a
 //    slice, a barrier, the next); F waves share each tile, wave f taking the
-//    steps f, f + F, ... of every slice, and their partial sums meet in LDS
-//    in wave order. Every output is summed in the same order on every run.
+//    rounds (4 consecutive steps) f, f + F, ... of every slice, and their
+//    partial sums meet in LDS in wave order. Every output is summed in the
+//    same order on every run.
 //  * Weight loads go through buffer resources based at the tile. A round is
 //    4 consecutive steps of a wave: four 16-byte code loads per lane and one
 //    16-byte load each for the lane's 8 scales and 8 biases of the round (a
@@ -39,7 +43,6 @@
 //    is staged (weights do not depend on x). K is a multiple of 512.
 #include "common.h"
 #include "launch.h"
-#include "mfma.h"
 
 namespace qd {
 
