@@ -65,6 +65,7 @@ def _load():
     lib.qo_attn_slot.restype = _I64
     lib.qo_attn_decode.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
                                    ctypes.c_double, _P, _P]
+    lib.qo_quant_i8_rows.argtypes = [_P, _I64, _I64, _P, _P]
     lib.qo_set_threads.argtypes = [ctypes.c_int]
     lib.qo_get_threads.restype = ctypes.c_int
     _lib = lib
@@ -149,6 +150,29 @@ def gemv_f16(w, x_bits, rows=None):
 def gemm_chunk(w, x_bits_bf16, rows=None):
     """Prefill chunk: Y[M][N] = X W^T with bf16 activations X[M][K] (raw bits)."""
     return gemv(w, bf16_to_f64(np.atleast_2d(x_bits_bf16)), rows)
+
+
+def quant_i8(x_bits):
+    """Per-token symmetric int8 quantization of fp16 activations (raw bits
+    [M][K]): codes int8 [M][K] and fp32 scales [M], scale = max|x| / 127 and
+    codes round(x / scale) with ties to even, in fp32 (uzu page, section on
+    speculative decoding: activations quantized to 8 bits on the fly for the
+    int8 verification GEMM; the scheme is this oracle's reading)."""
+    x, px = _c(np.atleast_2d(x_bits), np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.int8)
+    sc = np.empty(M, dtype=np.float32)
+    _load().qo_quant_i8_rows(px, M, K, q.ctypes.data_as(_P), sc.ctypes.data_as(_P))
+    return q, sc
+
+
+def verify_i8(w, x_bits, rows=None):
+    """Verification GEMM on dynamically quantized int8 activations:
+    Y = X^ W^T with X^[m] = scale[m] * q[m] from quant_i8 (exact in fp64).
+    Returns (y, A) as gemv does, A = sum_k |w x^|."""
+    q, sc = quant_i8(x_bits)
+    xh = sc.astype(np.float64)[:, None] * q.astype(np.float64)
+    return gemv(w, xh, rows)
 
 
 MIRAI_FMT = {"M": 1, "L": 2}

@@ -151,3 +151,16 @@ def attn_decode(q, k_new, v_new, kc, vc, window: int, pos: int, scale: float):
         p = softmax(scale * (kc[hk, :n] @ q[h]))
         out[h] = p @ vc[hk, :n]
     return out
+
+
+def quant_i8(x_bits):
+    """Per-token int8 quantization by a second route: numpy float32 array
+    arithmetic (maximum of |x|, the scale max/127, x/scale rounded half to
+    even by np.rint), zero rows kept at zero."""
+    x = np.atleast_2d(np.asarray(x_bits, np.uint16)).view(np.float16).astype(np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    sc = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(sc > 0, sc, np.float32(1.0)).astype(np.float32)
+    q = np.rint(x / safe[:, None]).astype(np.float32)
+    q = np.where(sc[:, None] > 0, q, np.float32(0.0)).astype(np.int8)
+    return q, sc

@@ -408,3 +408,31 @@ void qo_attn_decode(const double* q, const double* k_new, const double* v_new,
     }
     free(sc);
 }
+
+/*
+ * Dynamic int8 activations for the verification GEMM (uzu page on
+ * discuss.pytorch.kr, section on speculative decoding: the target model
+ * checks 16-32 drafted tokens on the chip's int8 matrix path and quantizes
+ * its activations to 8 bits on the fly). The page gives no scheme; the
+ * reading taken here: per token (row), symmetric, scale = max |x| / 127 and
+ * code = round(x / scale) with ties to even, the scale and the quotients in
+ * fp32 (the precision in which the kernel takes the same integer decisions);
+ * a row of zeros has scale 0 and codes 0. The quantized activation is
+ * scale * code, which fp64 holds exactly.
+ */
+void qo_quant_i8_rows(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale) {
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* xr = x + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf((float)qo_f16_to_f64(xr[k]));
+            if (v > amax) amax = v;
+        }
+        const float sc = amax / 127.0f;
+        scale[m] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = (float)qo_f16_to_f64(xr[k]);
+            q[m * K + k] = amax > 0.0f ? (int8_t)rintf(v / sc) : (int8_t)0;
+        }
+    }
+}

@@ -123,6 +123,11 @@ void qo_attn_decode(const double* q, const double* k_new, const double* v_new,
                     double* out, double* a);
 
 /* Number of OpenMP threads the oracle uses (0 = runtime default). */
+/* Per-token symmetric int8 quantization of fp16 activations [M][K]: codes
+ * q [M][K] and scales [M] (scale = max|x| / 127, codes rounded to nearest
+ * even, in fp32); the quantized activation is scale * q. */
+void qo_quant_i8_rows(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* scale);
+
 void qo_set_threads(int n);
 int qo_get_threads(void);
 

@@ -640,3 +640,79 @@ def test_attn_large_scores_are_stable():
 def test_attn_slot_rule():
     assert [oracle.attn_slot(p, 4) for p in range(9)] == [0, 1, 2, 3, 0, 1, 2, 3, 0]
     assert [oracle.attn_slot(p, 0) for p in (0, 5, 4095)] == [0, 5, 4095]
+
+
+# ------------------------------------------------ int8 activations (verify)
+# uzu page on discuss.pytorch.kr, section on speculative decoding: the
+# verification GEMM runs on an int8 matrix path with the activations
+# quantized to 8 bits on the fly. Reading: per token, symmetric,
+# scale = max|x| / 127, codes rounded half to even, in fp32.
+
+def _grid_rows(M, K, seed):
+    """fp16 activations on the grid k * 2^-4 (|k| <= 127, each row holding
+    +-127), where scale = 2^-4 exactly and quantization changes nothing."""
+    rng = np.random.default_rng(seed)
+    k = rng.integers(-127, 128, size=(M, K))
+    k[:, rng.integers(0, K, size=M)] = 0
+    for m in range(M):
+        k[m, rng.integers(0, K)] = 127 if m % 2 else -127
+    return (k.astype(np.float64) * 2.0 ** -4).astype(np.float16).view(np.uint16)
+
+
+def test_int8_activations_on_the_exact_grid_reduce_to_the_gemm():
+    w = synth.affine_weights(4, 37, 704, cfg=901, set_id=0)
+    xb = _grid_rows(5, 704, 1)
+    q, sc = oracle.quant_i8(xb)
+    assert np.all(sc == np.float32(2.0 ** -4))
+    assert np.array_equal(q.astype(np.float64) * 2.0 ** -4, xb.view(np.float16).astype(np.float64))
+    y8, a8 = oracle.verify_i8(w, xb)
+    y, a = oracle.gemv_f16(w, xb)
+    assert np.array_equal(y8, y) and np.array_equal(a8, a)
+
+
+def test_int8_activation_ties_go_to_even():
+    # max |x| = 127 gives scale 1 exactly, so x / scale = x and the halves
+    # are exact ties; Python's round() rounds ties to even
+    vals = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5, -1.5, 126.5, -126.5, 0.0]
+    xb = np.array([vals], np.float16).view(np.uint16)
+    q, sc = oracle.quant_i8(xb)
+    assert sc[0] == np.float32(1.0)
+    assert q[0].tolist() == [round(v) for v in vals]
+
+
+def test_int8_activation_bounds_and_extremes():
+    for scale in (1e-4, 1.0, 300.0):
+        x = (synth.x_f16(6, 1024, cfg=902, set_id=int(scale * 7)).view(np.float16).astype(np.float32)
+             * np.float32(scale)).astype(np.float16)
+        q, sc = oracle.quant_i8(x.view(np.uint16))
+        xf = x.astype(np.float64)
+        xh = sc.astype(np.float64)[:, None] * q
+        assert np.all(np.abs(q.astype(np.int32)) <= 127)
+        assert np.all(np.max(np.abs(q.astype(np.int32)), axis=1) == 127)
+        # round to nearest: within half a step (plus the fp32 quotient's rounding)
+        assert np.all(np.abs(xh - xf) <= sc.astype(np.float64)[:, None] * (0.5 + 1e-6))
+
+
+def test_int8_activation_zero_row_and_row_independence():
+    w = synth.affine_weights(4, 20, 256, cfg=903, set_id=0)
+    xb = synth.x_f16(3, 256, cfg=903, set_id=1).copy()
+    q1, s1 = oracle.quant_i8(xb)
+    xb2 = xb.copy()
+    xb2[1] = 0
+    q2, s2 = oracle.quant_i8(xb2)
+    assert s2[1] == 0 and np.all(q2[1] == 0)
+    assert np.array_equal(q1[[0, 2]], q2[[0, 2]]) and np.array_equal(s1[[0, 2]], s2[[0, 2]])
+    y, _ = oracle.verify_i8(w, xb2)
+    assert np.all(y[1] == 0.0)
+
+
+def test_int8_activations_match_the_second_route():
+    w = synth.affine_weights(4, 33, 2112, cfg=904, set_id=0)
+    xb = synth.x_f16(17, 2112, cfg=904, set_id=1)
+    q, sc = oracle.quant_i8(xb)
+    qb, sb = brute.quant_i8(xb)
+    assert np.array_equal(q, qb) and np.array_equal(sc, sb)
+    y, _ = oracle.verify_i8(w, xb)
+    xh = sb.astype(np.float64)[:, None] * qb.astype(np.float64)
+    yb = xh @ brute.dense(w).T
+    assert np.allclose(y, yb, rtol=1e-12, atol=1e-12)

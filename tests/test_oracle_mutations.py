@@ -67,6 +67,12 @@ MUTATIONS = {
     "attention scale dropped": ("sc[j] = scale * acc;", "sc[j] = acc + 0.0 * scale;"),
     "attention unnormalized": ("acc += sc[j] / z * vj[d];", "acc += sc[j] * vj[d] + 0.0 * z;"),
     "attention no max shift": ("sc[j] = exp(sc[j] - smax);", "sc[j] = exp(sc[j]) + 0.0 * smax;"),
+    "int8 activation codes truncated": ("q[m * K + k] = amax > 0.0f ? (int8_t)rintf(v / sc) : (int8_t)0;",
+                                        "q[m * K + k] = amax > 0.0f ? (int8_t)truncf(v / sc) : (int8_t)0;"),
+    "int8 activation scale over 128": ("const float sc = amax / 127.0f;", "const float sc = amax / 128.0f;"),
+    "int8 activation scale dropped": ("scale[m] = sc;", "scale[m] = 1.0f + 0.0f * sc;"),
+    "int8 activation max over half the row": ("const float v = fabsf((float)qo_f16_to_f64(xr[k]));",
+                                              "const float v = fabsf((float)qo_f16_to_f64(xr[k / 2]));"),
     "shared expert halved": ("yt[n] += o[n];\n            if (at) at[n] += oa[n];\n        }\n    }",
                              "yt[n] += 0.5 * o[n];\n            if (at) at[n] += oa[n];\n        }\n    }"),
 }
@@ -107,6 +113,11 @@ PIN_CALLS = [
     (pins.test_attn_circular_equals_linear_over_the_window, {}),
     (pins.test_attn_large_scores_are_stable, {}),
     (pins.test_attn_slot_rule, {}),
+    (pins.test_int8_activations_on_the_exact_grid_reduce_to_the_gemm, {}),
+    (pins.test_int8_activation_ties_go_to_even, {}),
+    (pins.test_int8_activation_bounds_and_extremes, {}),
+    (pins.test_int8_activation_zero_row_and_row_independence, {}),
+    (pins.test_int8_activations_match_the_second_route, {}),
 ]
 
 
