@@ -31,7 +31,8 @@ QD_GELU_ERF, QD_GELU_TANH = 0, 1
 EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
-           "qgemm_affine4_verify", "qattn_decode_workspace_bytes", "qattn_decode",
+           "qgemm_affine4_verify", "qgemm_affine4_verify_i8_workspace_bytes", "qgemm_affine4_verify_i8",
+           "qattn_decode_workspace_bytes", "qattn_decode",
            "qmoe_layer_decode", "qmoe_layer_decode_noalloc", "qd_stream_read",
            "qd_status_string", "qd_last_error")
 
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
                                    _P, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
     L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemm_affine4_verify_i8_workspace_bytes.argtypes = [_I32, _I32]
+    L.qgemm_affine4_verify_i8_workspace_bytes.restype = ctypes.c_size_t
+    L.qgemm_affine4_verify_i8.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, ctypes.c_size_t,
+                                          _P]
     L.qmoe_layer_decode.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P, ctypes.c_int, _P,
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.qmoe_layer_decode_noalloc.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P,
@@ -99,7 +104,7 @@ def lib() -> ctypes.CDLL:
     for fn in ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l",
                "qgemv_mirai_m_rht", "qgemv_mirai_l_rht",
                "qmoe_route_topk", "qmoe_expert_gemv", "qgemm_affine4_chunk", "qgemm_affine4_verify",
-               "qattn_decode", "qmoe_layer_decode", "qmoe_layer_decode_noalloc"):
+               "qgemm_affine4_verify_i8", "qattn_decode", "qmoe_layer_decode", "qmoe_layer_decode_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -434,6 +439,38 @@ def qgemm_affine4_verify(wq, scales, biases, x, out=None):
         raise ValueError("out must be [M][N]")
     _check(lib().qgemm_affine4_verify(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _x_dtype(x),
                                       _ptr(out), M, N, K, 64, _stream()))
+    return out
+
+
+def verify_i8_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().qgemm_affine4_verify_i8_workspace_bytes(M, K))
+
+
+def qgemm_affine4_verify_i8(wq, scales, biases, x, out=None, workspace=None):
+    """Verification GEMM on per-token int8 activations: sx[m] = max|X[m]| / 127,
+    xq = round-half-even(X / sx) in fp32, Y[m][n] = sx[m] sum_k w[n][k] xq[m][k];
+    fp16 X [M][K], M <= 32. `workspace` (uint8, device) defaults to a fresh one."""
+    _need(wq, "wq", _CODES, 2)
+    _need(scales, "scales", _HALF, 2)
+    _need(biases, "biases", _HALF, 2)
+    _need(x, "x", (torch.float16,), 2)
+    N, K = wq.shape[0], wq.shape[1] * 8
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales/biases must be [N][K/64]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M][N]")
+    if workspace is None:
+        need = verify_i8_workspace_bytes(M, K)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().qgemm_affine4_verify_i8(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), M, N,
+                                         K, 64, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream()))
     return out
 
 

@@ -442,6 +442,37 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
                     fn);
 }
 
+size_t qgemm_affine4_verify_i8_workspace_bytes(int32_t M, int32_t K) {
+    if (M < 1 || M > 32 || K < 64 || K % 64 || K > (1 << 22)) return 0;
+    return qd::verify_i8_workspace_bytes(M, K);
+}
+
+qd_status qgemm_affine4_verify_i8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                  const uint16_t* x, float* y, int32_t M, int32_t N, int32_t K,
+                                  int32_t group_size, void* workspace, size_t ws_bytes,
+                                  qd_stream stream) {
+    const char* fn = "qgemm_affine4_verify_i8";
+    qd_status st = check_matrix(fn, N, K, group_size);
+    if (st != QD_OK) return st;
+    if (M < 1 || M > 32)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: M = %d must be in [1, 32]", fn, M);
+    CHECK_PTR(wq);
+    CHECK_PTR(scales);
+    CHECK_PTR(biases);
+    CHECK_PTR(x);
+    CHECK_PTR(y);
+    const size_t need = qd::verify_i8_workspace_bytes(M, K);
+    if (!workspace)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned16(workspace))
+        return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (ws_bytes < need)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    return from_hip(qd::launch_verify_i8(wq, scales, biases, x, y, M, N, K, workspace, ws_bytes,
+                                         (hipStream_t)stream),
+                    fn);
+}
+
 size_t qattn_decode_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t D, int32_t cap) {
     if (Hq < 1 || Hkv < 1 || D < 1 || cap < 1) return 0;
     return qd::attn_workspace_bytes(Hq, Hkv, D, cap);

@@ -79,6 +79,12 @@ hipError_t launch_moe_experts(const MoeArgs& m, const int32_t* idx, const float*
 hipError_t launch_gemv_mfma(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                             const uint16_t* x, float* y, int N, int K, int nb, hipStream_t st);
 
+// Verification GEMM on per-token int8 activations (M <= 32, fp16 X).
+size_t verify_i8_workspace_bytes(int M, int K);
+hipError_t launch_verify_i8(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                            const uint16_t* x, float* y, int M, int N, int K, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+
 // 8-bit weights over T > 8 tokens (f16 or bf16 activations) on the matrix core.
 hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,

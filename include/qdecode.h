@@ -261,6 +261,33 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
                                qd_stream stream);
 
 /*
+ * Verification GEMM on int8 activations (uzu page on discuss.pytorch.kr,
+ * section on speculative decoding: the target model checks 16 to 32 drafted
+ * tokens in one pass on the chip's int8 matrix path, quantizing its
+ * activations to 8 bits as it goes). The page leaves the scheme open; this
+ * call takes it per token and symmetric, in fp32:
+ *   sx[m] = max_k |X[m][k]| / 127 (correctly rounded division),
+ *   xq[m][k] = X[m][k] / sx[m] rounded to the nearest integer, ties to even
+ *   (0 throughout a row of zeros, whose sx is 0),
+ *   Y[m][n] = sx[m] * sum_k w[n][k] * xq[m][k],
+ * with w[n][k] = s q + b from 4-bit codes, scales and biases as
+ * qgemv_affine4. X [M][K] fp16 bits, Y [M][N] fp32, 1 <= M <= 32.
+ *   workspace: device memory, 16-byte aligned, of at least
+ *   qgemm_affine4_verify_i8_workspace_bytes(M, K) bytes (0 for arguments
+ *   out of range); it receives the quantized activations, their per-group
+ *   sums and the scales, and is overwritten by every call, so calls that
+ *   share one must be ordered on a stream. NULL or too small fails with
+ *   QD_ERR_WORKSPACE before any launch.
+ * Two launches on `stream` (quantization, then the GEMM); results do not
+ * depend on timing.
+ */
+size_t qgemm_affine4_verify_i8_workspace_bytes(int32_t M, int32_t K);
+qd_status qgemm_affine4_verify_i8(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                  const uint16_t* x, float* y, int32_t M, int32_t N, int32_t K,
+                                  int32_t group_size, void* workspace, size_t ws_bytes,
+                                  qd_stream stream);
+
+/*
  * Decode attention for one new token ([TF] internals section: sliding-window
  * layers keep keys and values in bounded circular storage, full-attention
  * layers in linear storage, and decode attention is exact).

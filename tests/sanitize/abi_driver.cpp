@@ -94,6 +94,12 @@ int main() {
     EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 14336, 4096, 64, nullptr), QD_OK);
     EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, (qd_dtype)2, y, 32, 14336, 4096, 64, nullptr), QD_ERR_UNSUPPORTED);
     // decode attention
+    const size_t vws = qgemm_affine4_verify_i8_workspace_bytes(32, 4096);
+    if (!(vws > 0) || qgemm_affine4_verify_i8_workspace_bytes(33, 4096) != 0) ++fails;
+    EXPECT(qgemm_affine4_verify_i8(U32 A, U16 A, U16 A, U16 A, y, 32, 14336, 4096, 64, A, vws, nullptr), QD_OK);
+    EXPECT(qgemm_affine4_verify_i8(U32 A, U16 A, U16 A, U16 A, y, 33, 14336, 4096, 64, A, vws, nullptr), QD_ERR_INVALID_ARGUMENT);
+    EXPECT(qgemm_affine4_verify_i8(U32 A, U16 A, U16 A, U16 A, y, 32, 14336, 4096, 64, A, vws - 1, nullptr), QD_ERR_WORKSPACE);
+    EXPECT(qgemm_affine4_verify_i8(U32 A, U16 A, U16 A, U16 A, y, 32, 14336, 4096, 64, nullptr, vws, nullptr), QD_ERR_WORKSPACE);
     const size_t aws = qattn_decode_workspace_bytes(16, 8, 128, 4096);
     const uint16_t* h = U16 A;
     uint16_t* hc = (uint16_t*)A;

@@ -68,6 +68,12 @@ hipError_t launch_chunk_gemm(int, const uint32_t*, const uint16_t*, const uint16
     ++g_launches;
     return hipSuccess;
 }
+size_t verify_i8_workspace_bytes(int M, int K) { return (size_t)((M + 15) / 16 * 16) * K * 2 + 4096; }
+hipError_t launch_verify_i8(const uint32_t*, const uint16_t*, const uint16_t*, const uint16_t*, float*,
+                            int, int, int, void*, size_t, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_stream_read(const void*, int64_t, uint32_t*, hipStream_t) {
     ++g_launches;
     return hipSuccess;

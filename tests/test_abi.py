@@ -226,6 +226,30 @@ def test_verify_argument_errors():
     assert v(x=MIS) == E.QD_ERR_MISALIGNED
 
 
+def test_verify_i8_argument_errors():
+    E = qd
+    L = qd.lib()
+    ws = qd.verify_i8_workspace_bytes(32, 4096)
+    assert ws >= 32 * 4096 + 64 * 32 * 4 + 32 * 4
+    assert qd.verify_i8_workspace_bytes(33, 4096) == 0 and qd.verify_i8_workspace_bytes(1, 100) == 0
+    assert qd.verify_i8_workspace_bytes(16, 4096) < ws
+
+    def v(wq=A, s=A, b=A, x=A, y=A, M=32, N=16, K=4096, gs=64, w=A, wsb=ws):
+        return L.qgemm_affine4_verify_i8(wq, s, b, x, y, M, N, K, gs, w, wsb, None)
+
+    assert v(M=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(M=33) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(K=100) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(N=0) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(gs=32) == E.QD_ERR_UNSUPPORTED
+    assert v(s=None) == E.QD_ERR_INVALID_ARGUMENT
+    assert v(x=MIS) == E.QD_ERR_MISALIGNED
+    assert v(w=None) == E.QD_ERR_WORKSPACE
+    assert v(w=MIS) == E.QD_ERR_MISALIGNED
+    assert v(wsb=ws - 1) == E.QD_ERR_WORKSPACE
+    assert "workspace" in qd.last_error()
+
+
 def test_attention_argument_errors():
     E = qd
     L = qd.lib()
