@@ -20,15 +20,15 @@
 //  2. GEMM: v_mfma_i32_16x16x64_i8, one instruction per group of 64 inputs:
 //     A = 16 tokens x 64 codes, B = 64 weight codes x 16 rows, each lane
 //     holding 16 bytes of one token / one row in the same k order. The
-//     weight codes enter exactly as signed bytes q - 8 (the nibbles spread
-//     to bytes, then + 0x78 and ^ 0x80 per byte: no carry crosses a byte),
-//     so P = sum (q - 8) xq is an exact integer and per group, in fp32,
-//         acc += s P + (b + 8 s) Xsum,   Y = sx acc,
+//     weight codes enter as bytes q (the nibbles spread to bytes), so
+//     P = sum q xq is an exact integer (|P| <= 64 * 15 * 127 < 2^24) and
+//     per group, in fp32,
+//         acc += s P + b Xsum,   Y = sx acc,
 //     with Xsum the group's code sum; the s P terms on the VALU, the bias
-//     terms of 4 groups as one v_mfma_f32_16x16x4_f32. A workgroup owns 64
-//     rows at M <= 16 (32 above) and its VI_W waves split K into contiguous
-//     runs of groups; one activation load then serves every 16-row tile, and
-//     a stage's scales and biases arrive as one vector load per row. The
+//     terms of 4 groups as one v_mfma_f32_16x16x4_f32. A workgroup owns up
+//     to 4 16-row tiles (2 at M > 16) and its 4 or 8 waves split K into
+//     contiguous runs of groups; one activation load then serves every tile,
+//     and the workgroup's scales and biases are staged in LDS once. The
 //     waves' partial sums meet in LDS in wave order, so results do not
 //     depend on timing. Tokens come in one or two blocks of 16 (M <= 32)
 //     sharing each unpacked code word.
@@ -40,8 +40,6 @@ namespace qd {
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int VI_ROWS = 64;   // rows x 16-token blocks per GEMM workgroup: 4 tiles at M <= 16, 2 above
-constexpr int VI_W = 8;    // waves per GEMM workgroup (runs of K groups)
 constexpr int VI_U = 4;    // groups per pipeline stage (the bias MFMA's K)
 
 // Workspace for Mp token rows (M rounded up to 16) and G = K / 64 groups,
@@ -81,90 +79,164 @@ __host__ __device__ constexpr int vi_perm(int i) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. quantize one token row per workgroup (256 threads)
+// 1. quantize one token row per workgroup (1024 threads)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void verify_i8_quant_kernel(const uint16_t* x, int M, int K, ViWs w,
-                                                              int Mp) {
-    __shared__ float wmax[4];
+constexpr int VQ_T = 1024;   // threads per token
+constexpr int VQ_R = 4;      // dwords of codes per thread and pass
+
+// Thread t makes dword d = t % 4 of 16-input block t / 4 (then t + 1024,
+// ...): bytes i = 4d .. 4d + 3 of the block, i.e. inputs vi_perm(i), which
+// all lie in one 8-input half of the block (dwords 0, 1: inputs 0..7, 2, 3:
+// 8..15), so one 16-byte load serves both passes. With K up to 16 VQ_T VQ_R
+// / 4 (16384) the values stay in registers between the max and the codes;
+// longer rows are read again. 16 consecutive lanes hold a group's 64 codes
+// and sum them.
+__device__ __forceinline__ uint4 vq_load(const uint16_t* xr, int e, bool live) {
+    // e: index of the dword of codes; its 8 inputs start at input 8 (e / 2)
+    return live ? *(const uint4*)(xr + 8 * (int64_t)(e >> 1)) : make_uint4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(VQ_T) void verify_i8_quant_kernel(const uint16_t* x, int M, int K, ViWs w,
+                                                               int Mp) {
+    __shared__ float wmax[VQ_T / 64];
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool live = m < M;
     const uint16_t* xr = x + (int64_t)min(m, M - 1) * K;
+    const int nd = K / 4;   // dwords of codes in the row
+    const bool one_pass = nd <= VQ_T * VQ_R;
+    uint4 v[VQ_R];
     float amax = 0.f;
-    if (live)
-        for (int k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(h2f(xr[k])));
+    for (int e0 = 0; e0 < nd; e0 += VQ_T * VQ_R) {
+#pragma unroll
+        for (int r = 0; r < VQ_R; ++r) {
+            const int e = e0 + VQ_T * r + threadIdx.x;
+            v[r] = vq_load(xr, e, live && e < nd);
+        }
+#pragma unroll
+        for (int r = 0; r < VQ_R; ++r) {
+            const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                amax = fmaxf(amax, fmaxf(fabsf(h2f((uint16_t)wd[i])), fabsf(h2f((uint16_t)(wd[i] >> 16)))));
+        }
+    }
     amax = wave_max_f(amax);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    amax = wmax[0];
+#pragma unroll
+    for (int i = 1; i < VQ_T / 64; ++i) amax = fmaxf(amax, wmax[i]);
     const float sc = __fdiv_rn(amax, 127.0f);   // correctly rounded
     if (threadIdx.x == 0) w.sx[m] = live ? sc : 0.f;
-    // thread t takes the blocks of 16 inputs t, t + 256, ...; a group's 4
-    // blocks sit in 4 consecutive lanes, which sum its codes
-    const int nblk = K / 16;
-    for (int b0 = 0; b0 < nblk; b0 += 256) {
-        const int blk = b0 + threadIdx.x;
-        const bool bl = blk < nblk;
-        uint16_t h[16] = {};
-        if (live && bl) {
-            const uint4 lo = *(const uint4*)(xr + 16 * blk), hi = *(const uint4*)(xr + 16 * blk + 8);
-            const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const int d = threadIdx.x & 3;   // dword of the block this thread makes
+    for (int e0 = 0; e0 < nd; e0 += VQ_T * VQ_R) {
+        if (!one_pass) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) h[i] = (uint16_t)(wd[i >> 1] >> (16 * (i & 1)));
+            for (int r = 0; r < VQ_R; ++r) {
+                const int e = e0 + VQ_T * r + threadIdx.x;
+                v[r] = vq_load(xr, e, live && e < nd);
+            }
         }
-        uint32_t d[4] = {0, 0, 0, 0};
-        int sum = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            // a zero scale (a row of zeros) gives code 0 without dividing
-            const int c = amax > 0.f ? (int)rintf(__fdiv_rn(h2f(h[vi_perm(i)]), sc)) : 0;
-            d[i >> 2] |= (uint32_t)(c & 0xFF) << (8 * (i & 3));
-            sum += c;
+        for (int r = 0; r < VQ_R; ++r) {
+            if (e0 + VQ_T * r >= nd) break;   // uniform: the rest of the pass is past the row
+            const int e = e0 + VQ_T * r + threadIdx.x;
+            const bool ok = e < nd;
+            const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+            uint32_t code = 0;
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // input vi_perm(4d + i) of the block: position (vi_perm(4d + i) & 7)
+                // of the loaded half, which for d = 0, 2 is 2i and for d = 1, 3 is 2i + 1
+                const uint16_t h = (uint16_t)(wd[i] >> (16 * (d & 1)));
+                // a zero scale (a row of zeros) gives code 0 without dividing
+                const int c = amax > 0.f ? (int)rintf(__fdiv_rn(h2f(h), sc)) : 0;
+                code |= (uint32_t)(c & 0xFF) << (8 * i);
+                sum += c;
+            }
+            const int blk = e >> 2, g = e >> 4;
+            if (ok) *(uint32_t*)(w.q + ((int64_t)g * Mp + m) * 64 + 16 * (blk & 3) + 4 * d) = code;
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            sum += __shfl_xor(sum, 8);
+            if (ok && (e & 15) == 0) w.xsum[(int64_t)g * Mp + m] = (float)sum;
         }
-        const int g = blk >> 2;
-        if (bl)
-            *(uint4*)(w.q + ((int64_t)g * Mp + m) * 64 + 16 * (blk & 3)) = make_uint4(d[0], d[1], d[2], d[3]);
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        if (bl && (blk & 3) == 0) w.xsum[(int64_t)g * Mp + m] = (float)sum;
     }
 }
 
 // ---------------------------------------------------------------------------
 // 2. the GEMM
 // ---------------------------------------------------------------------------
-// 16 weight codes (words w0, w1 = inputs 16j..16j+15 of a row) as signed
-// bytes q - 8 in the order vi_perm gives.
+// 16 weight codes (words w0, w1 = 16 consecutive inputs of a row) as bytes
+// q in 0..15 (non-negative, so exact as the MFMA's signed int8) in the
+// order vi_perm gives.
 __device__ __forceinline__ int32x4_t vi_codes(uint32_t w0, uint32_t w1) {
-    const uint32_t t0 = w0 & 0x0F0F0F0Fu, u0 = (w0 >> 4) & 0x0F0F0F0Fu;
-    const uint32_t t1 = w1 & 0x0F0F0F0Fu, u1 = (w1 >> 4) & 0x0F0F0F0Fu;
     int32x4_t r;
-    r[0] = (int)((t0 + 0x78787878u) ^ 0x80808080u);
-    r[1] = (int)((u0 + 0x78787878u) ^ 0x80808080u);
-    r[2] = (int)((t1 + 0x78787878u) ^ 0x80808080u);
-    r[3] = (int)((u1 + 0x78787878u) ^ 0x80808080u);
+    r[0] = (int)(w0 & 0x0F0F0F0Fu);
+    r[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
+    r[2] = (int)(w1 & 0x0F0F0F0Fu);
+    r[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
     return r;
+}
+
+// The codes of two groups as loaded (lane (n, j): bytes 16j .. 16j + 15 of
+// a row's 64-byte pair of groups, i.e. lanes j = 0, 1 hold the first group,
+// j = 2, 3 the second) regrouped by two lane swaps between the wave's
+// halves into one MFMA operand per group: afterwards lane j holds, of each
+// group, the 16 inputs of block jb = [0, 2, 1, 3][j] (dwords 0, 1 for the
+// first group, 2, 3 for the second), as bytes q.
+__device__ __forceinline__ void pair_codes(uint4 c, int32x4_t& g0, int32x4_t& g1) {
+    const auto a = __builtin_amdgcn_permlane32_swap(c.x, c.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(c.y, c.w, false, false);
+    g0 = vi_codes(a[0], b[0]);
+    g1 = vi_codes(a[1], b[1]);
 }
 
 // Workgroup: RT 16-row tiles (rows r0 .. r0 + 16 RT - 1), W waves; wave w
 // takes groups [w per, min(G, (w + 1) per)) in stages of 4 groups, loading
 // stage i + 1 while it multiplies stage i. Lane (n, j): row n of each tile
-// and token n of each 16-token block for the operands, inputs 16j .. 16j + 15
-// of each group; results for tokens 4j .. 4j + 3 of each block.
+// and token n of each 16-token block for the operands, inputs 16 jb ..
+// 16 jb + 15 of each group (pair_codes); results for tokens 4j .. 4j + 3 of
+// each block.
 // Per stage and tile the code products enter as s P (VALU) and the bias
 // terms as one v_mfma_f32_16x16x4_f32 contracting the stage's 4 groups:
-// lane (n, j) gives Xsum[token n][group g + j] and (b + 8 s)[row n][group
-// g + j]. VSB: a stage's scales and biases as one 8-byte load per row (needs
-// G even); otherwise 2-byte loads.
-template <int RT, int NB, int W, bool VSB>
+// lane (n, j) gives Xsum[token n][group g + j] and b[row n][group g + j].
+// SBL: the workgroup's scales and biases are first copied to LDS with
+// row-contiguous loads and each stage reads its 4 per row from there, so the
+// stage's global loads are the codes and the activations alone (per-row
+// scale loads would touch as many cache lines as the codes); otherwise (odd
+// G, or rows too long for the LDS) one 2-byte global load per group.
+constexpr int VI_LDS_MAX = 128 * 1024;
+
+// Halves per LDS row of scales (or biases): G rounded up to 4, plus 4, so
+// that the 16 rows one instruction reads fall in different banks.
+static inline int vi_sb_stride(int G) { return (G + 3) / 4 * 4 + 4; }
+
+template <int RT, int NB, int W>
+static size_t vi_lds_bytes(int G, bool sbl) {
+    const size_t red = (size_t)W * RT * NB * 4 * 64 * 4;
+    const size_t sb = sbl ? (size_t)2 * 16 * RT * vi_sb_stride(G) * 2 : 0;
+    return red > sb ? red : sb;
+}
+
+template <int RT, int NB, int W, bool SBL>
 __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
     const uint32_t* wq, const uint16_t* s, const uint16_t* b, ViWs ws, float* y, int M, int N, int K,
-    int Mp, int per) {
+    int Mp, int per, int str) {
     constexpr int U = 4;
-    __shared__ float red[W][RT * NB * 4][64];
+    extern __shared__ uint4 vi_smem[];
+    // the scales and biases [16 RT][str] during the loop, the waves' partial
+    // sums [W][RT NB 4][64] after it
+    uint16_t* sl = (uint16_t*)vi_smem;
+    uint16_t* bl = sl + 16 * RT * str;
+    float* red = (float*)vi_smem;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, j = lane >> 4;
+    const int jb = ((j & 1) << 1) | (j >> 1);   // the 16-input block of a group lane j holds
     const int G = K >> 6;
     const int r0 = blockIdx.x * 16 * RT;
     const int rows = min(16 * RT, N - r0);
@@ -177,12 +249,37 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
     const auto xr = buf_rsrc(ws.xsum, (int64_t)G * Mp * 4);
     constexpr uint32_t OOB = 0x7FFFFFF0u;   // past every resource: reads zero, touches nothing
 
+    if constexpr (SBL) {
+        // dword c of row r (G is even), 8 per thread per round, loads first
+        const int dpr = G / 2, tot = 16 * RT * dpr;
+        for (int i0 = 0; i0 < tot; i0 += 8 * 64 * W) {
+            uint32_t sv[8], bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = i0 + e * 64 * W + (int)threadIdx.x;
+                const int r = i / dpr, c = i - r * dpr;
+                const uint32_t off = i < tot ? ((uint32_t)r * (uint32_t)G + 2u * (uint32_t)c) * 2u : OOB;
+                sv[e] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)off, 0, 0);
+                bv[e] = __builtin_amdgcn_raw_buffer_load_b32(br, (int)off, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = i0 + e * 64 * W + (int)threadIdx.x;
+                if (i < tot) {
+                    const int r = i / dpr, c = i - r * dpr;
+                    *(uint32_t*)(sl + r * str + 2 * c) = sv[e];
+                    *(uint32_t*)(bl + r * str + 2 * c) = bv[e];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
     struct Stage {
-        uint2 cw[U][RT];
+        uint4 cw[U / 2][RT];   // codes of groups g + 2p, g + 2p + 1 as loaded (see pair_codes)
         int32x4_t a[U][NB];
         float xs[NB];
-        uint2 sv[RT], bv[RT];                 // VSB: 4 scales, 4 biases per row
-        uint16_t su[U][RT], sj[RT], bj[RT];   // otherwise
+        uint16_t su[SBL ? 1 : U][RT], bj[RT];   // without SBL: the scales, and lane j's bias
     };
     const int gb = wave * per;
     const int ge = min(G, gb + per);
@@ -191,17 +288,24 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
     // nothing), so the compiler's count of loads in flight stays exact
     auto load = [&](Stage& t, int g) {
 #pragma unroll
+        for (int p = 0; p < U / 2; ++p) {
+            // lane (n, j): 16 bytes of row n at byte 16 j of the pair of
+            // groups g + 2p, g + 2p + 1, so the 4 lanes of a row read 64
+            // contiguous bytes
+            const bool ok = g + 2 * p < ge;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const uint32_t off = ok ? (uint32_t)(16 * rt + n) * rowb + (uint32_t)(g + 2 * p) * 32u + 16u * j : OOB;
+                t.cw[p][rt] = buf_load16(wr, off);
+            }
+        }
+#pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool ok = g + u < ge;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const uint32_t off = ok ? (uint32_t)(16 * rt + n) * rowb + (uint32_t)(g + u) * 32u + 8u * j : OOB;
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)off, 0, 0);
-                t.cw[u][rt] = make_uint2(v[0], v[1]);
-            }
-#pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const uint32_t qo = ok ? ((uint32_t)((g + u) * Mp + 16 * nb + n) * 64u + 16u * j) : OOB;
+                // the 16 inputs of block jb of the group, the block pair_codes gives lane j
+                const uint32_t qo = ok ? ((uint32_t)((g + u) * Mp + 16 * nb + n) * 64u + 16u * jb) : OOB;
                 const uint4 av = buf_load16(qr, qo);
                 t.a[u][nb] = int32x4_t{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
             }
@@ -212,22 +316,14 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
             const uint32_t xo = okj ? (uint32_t)((g + j) * Mp + 16 * nb + n) * 4u : OOB;
             t.xs[nb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, (int)xo, 0, 0));
         }
+        if constexpr (!SBL) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const uint32_t rg = (uint32_t)(16 * rt + n) * (uint32_t)G;
-            if constexpr (VSB) {
-                const uint32_t so = g < ge ? (rg + (uint32_t)g) * 2u : OOB;
-                const auto sv = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)so, 0, 0);
-                const auto bv = __builtin_amdgcn_raw_buffer_load_b64(br, (int)so, 0, 0);
-                t.sv[rt] = make_uint2(sv[0], sv[1]);
-                t.bv[rt] = make_uint2(bv[0], bv[1]);
-            } else {
+            for (int rt = 0; rt < RT; ++rt) {
+                const uint32_t rg = (uint32_t)(16 * rt + n) * (uint32_t)G;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     t.su[u][rt] = buf_load2(sr, g + u < ge ? (rg + (uint32_t)(g + u)) * 2u : OOB);
-                const uint32_t so = okj ? (rg + (uint32_t)(g + j)) * 2u : OOB;
-                t.sj[rt] = buf_load2(sr, so);
-                t.bj[rt] = buf_load2(br, so);
+                t.bj[rt] = buf_load2(br, okj ? (rg + (uint32_t)(g + j)) * 2u : OOB);
             }
         }
     };
@@ -244,32 +340,36 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
         const bool okj = g + j < ge;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float sc[U], sjv, bjv;
-            if constexpr (VSB) {
+            float sc[U], bjv;
+            if constexpr (SBL) {
+                // 4 scales and biases of row 16 rt + n from groups g .. g + 3 (8-byte aligned)
+                const int ro = (16 * rt + n) * str + g;
+                const uint2 sv = *(const uint2*)(sl + ro);
+                const uint2 bv = *(const uint2*)(bl + ro);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const uint32_t wd = u < 2 ? t.sv[rt].x : t.sv[rt].y;
+                    const uint32_t wd = u < 2 ? sv.x : sv.y;
                     sc[u] = g + u < ge ? h2f((uint16_t)(wd >> (16 * (u & 1)))) : 0.f;
                 }
-                sjv = h2f((uint16_t)(((j & 2) ? t.sv[rt].y : t.sv[rt].x) >> hs));
-                bjv = h2f((uint16_t)(((j & 2) ? t.bv[rt].y : t.bv[rt].x) >> hs));
+                bjv = h2f((uint16_t)(((j & 2) ? bv.y : bv.x) >> hs));
             } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) sc[u] = h2f(t.su[u][rt]);
-                sjv = h2f(t.sj[rt]);
                 bjv = h2f(t.bj[rt]);
             }
-            // w = s (q - 8) + (b + 8 s); a group past the run adds exactly zero
-            const float bi = okj ? fmaf(8.f, sjv, bjv) : 0.f;
+            // w = s q + b; a group past the run adds exactly zero
+            const float bi = okj ? bjv : 0.f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 acc[rt][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.xs[nb], bi, acc[rt][nb], 0, 0, 0);
+            int32x4_t bqs[U];
+#pragma unroll
+            for (int p = 0; p < U / 2; ++p) pair_codes(t.cw[p][rt], bqs[2 * p], bqs[2 * p + 1]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int32x4_t bq = vi_codes(t.cw[u][rt].x, t.cw[u][rt].y);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const int32x4_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(t.a[u][nb], bq, zero4, 0, 0, 0);
+                    const int32x4_t P = __builtin_amdgcn_mfma_i32_16x16x64_i8(t.a[u][nb], bqs[u], zero4, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[rt][nb][i] = fmaf(sc[u], (float)P[i], acc[rt][nb][i]);
                 }
@@ -286,13 +386,16 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
         if (g + U < ge) compute(B, g + U);
     }
 
-    // partial sums of the W waves, added in wave order
+    // partial sums of the W waves, added in wave order (the LDS held the
+    // scales until every wave is past its loop)
+    __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][(rt * NB + nb) * 4 + i][lane] = acc[rt][nb][i];
+            for (int i = 0; i < 4; ++i)
+                red[((wave * RT * NB + rt * NB + nb) * 4 + i) * 64 + lane] = acc[rt][nb][i];
     __syncthreads();
     for (int p = wave; p < RT * NB; p += W) {
         const int rt = p / NB, nb = p % NB;
@@ -301,20 +404,38 @@ __global__ __launch_bounds__(64 * W) void verify_i8_gemm_kernel(
         for (int i = 0; i < 4; ++i) {
             float v = 0.f;
 #pragma unroll
-            for (int wv = 0; wv < W; ++wv) v += red[wv][p * 4 + i][lane];
+            for (int wv = 0; wv < W; ++wv) v += red[((wv * RT * NB + p) * 4 + i) * 64 + lane];
             const int t = 16 * nb + 4 * j + i;
             if (t < M && row < N) y[(int64_t)t * N + row] = ws.sx[t] * v;
         }
     }
 }
 
-template <int NB, bool VSB>
+template <int RT, int NB, int W, bool SBL>
 static void vi_gemm(const uint32_t* wq, const uint16_t* s, const uint16_t* b, ViWs w, float* y, int M,
-                    int N, int K, int Mp, int per, hipStream_t st) {
-    constexpr int RT = VI_ROWS / 16 / NB;
+                    int N, int K, int Mp, hipStream_t st) {
+    const int G = K / 64;
+    // runs of whole stages; waves past the last group add nothing
+    const int per = ((G + W - 1) / W + VI_U - 1) / VI_U * VI_U;
     const dim3 grid((N + 16 * RT - 1) / (16 * RT));
-    hipLaunchKernelGGL((verify_i8_gemm_kernel<RT, NB, VI_W, VSB>), grid, dim3(64 * VI_W), 0, st, wq, s, b,
-                       w, y, M, N, K, Mp, per);
+    const size_t lds = vi_lds_bytes<RT, NB, W>(G, SBL);
+    hipLaunchKernelGGL((verify_i8_gemm_kernel<RT, NB, W, SBL>), grid, dim3(64 * W), lds, st, wq, s, b, w,
+                       y, M, N, K, Mp, per, vi_sb_stride(G));
+}
+
+template <int NB, int W>
+static void vi_gemm_rt(int rt, const uint32_t* wq, const uint16_t* s, const uint16_t* b, ViWs w, float* y,
+                       int M, int N, int K, int Mp, hipStream_t st) {
+    if constexpr (NB == 1) {
+        if (rt >= 4) {
+            vi_gemm<4, NB, W, true>(wq, s, b, w, y, M, N, K, Mp, st);
+            return;
+        }
+    }
+    if (rt >= 2)
+        vi_gemm<2, NB, W, true>(wq, s, b, w, y, M, N, K, Mp, st);
+    else
+        vi_gemm<1, NB, W, true>(wq, s, b, w, y, M, N, K, Mp, st);
 }
 
 hipError_t launch_verify_i8(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
@@ -325,18 +446,30 @@ hipError_t launch_verify_i8(const uint32_t* wq, const uint16_t* s, const uint16_
     const int Mp = (M + 15) / 16 * 16;
     const int G = K / 64;
     const ViWs w = vi_carve(ws, Mp, K);
-    hipLaunchKernelGGL(verify_i8_quant_kernel, dim3(Mp), dim3(256), 0, st, x, M, K, w, Mp);
+    hipLaunchKernelGGL(verify_i8_quant_kernel, dim3(Mp), dim3(VQ_T), 0, st, x, M, K, w, Mp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // runs of whole stages; waves past the last group add nothing
-    const int per = ((G + VI_W - 1) / VI_W + VI_U - 1) / VI_U * VI_U;
-    const bool vsb = G % 2 == 0;
-    if (Mp == 16)
-        vsb ? vi_gemm<1, true>(wq, s, b, w, y, M, N, K, Mp, per, st)
-            : vi_gemm<1, false>(wq, s, b, w, y, M, N, K, Mp, per, st);
-    else
-        vsb ? vi_gemm<2, true>(wq, s, b, w, y, M, N, K, Mp, per, st)
-            : vi_gemm<2, false>(wq, s, b, w, y, M, N, K, Mp, per, st);
+    // Tiles per workgroup: as many as the registers allow (4 at M <= 16, 2
+    // above), halved while the grid has fewer workgroups than the chip's 256
+    // CUs; 8 waves per workgroup on rows of 8192 inputs or more, 4 below
+    // (measured on the 7B FFN shapes).
+    int rt = Mp == 16 ? 4 : 2;
+    while (rt > 1 && (N + 16 * rt - 1) / (16 * rt) < 256) rt /= 2;
+    const bool wide = G >= 128;
+    const bool sbl = G % 2 == 0 && vi_lds_bytes<4, 1, 8>(G, true) <= VI_LDS_MAX;
+    if (!sbl) {
+        // odd G or very long rows: scales and biases from global memory
+        if (Mp == 16)
+            vi_gemm<1, 1, 8, false>(wq, s, b, w, y, M, N, K, Mp, st);
+        else
+            vi_gemm<1, 2, 8, false>(wq, s, b, w, y, M, N, K, Mp, st);
+    } else if (Mp == 16) {
+        wide ? vi_gemm_rt<1, 8>(rt, wq, s, b, w, y, M, N, K, Mp, st)
+             : vi_gemm_rt<1, 4>(rt, wq, s, b, w, y, M, N, K, Mp, st);
+    } else {
+        wide ? vi_gemm_rt<2, 8>(rt, wq, s, b, w, y, M, N, K, Mp, st)
+             : vi_gemm_rt<2, 4>(rt, wq, s, b, w, y, M, N, K, Mp, st);
+    }
     return hipGetLastError();
 }
 

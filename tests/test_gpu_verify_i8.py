@@ -210,3 +210,23 @@ def test_close_to_the_fp16_verification():
     _, wabs = oracle.gemv(w, np.ones((1, K)))     # A of an all-ones input = sum_k |w|
     bound = sc.astype(np.float64)[:, None] * 0.5 * wabs[0][None, :] * 1.001 + 1e-3 * np.abs(y16) + 1e-5
     assert np.all(np.abs(y8 - y16) <= bound)
+
+
+# Shapes that select each workgroup shape of the GEMM (tiles per workgroup
+# 4 / 2 / 1, 4 or 8 waves, scales staged in LDS or read per group), all with
+# a ragged last tile; checked on sampled rows that include the tail.
+TILE_SHAPES = [(16400, 4096, 16), (16400, 8192, 16), (8200, 4096, 32), (8200, 8192, 20),
+               (4100, 14336, 16), (4100, 4096, 5), (300, 32768, 16), (300, 32768, 32), (300, 32896, 3)]
+
+
+@pytest.mark.parametrize("N,K,M", TILE_SHAPES)
+def test_workgroup_shapes_on_sampled_rows(N, K, M):
+    print(f"verify_i8 tiles N={N} K={K} M={M}", flush=True)
+    w = synth.affine_weights(4, N, K, cfg=528, set_id=N + K + M)
+    xb = draw_x(M, K, N + M)
+    y = run(w, xb).cpu().numpy()
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.concatenate([np.arange(0, 40), rng.choice(N, 120, replace=False),
+                                     np.arange(N - 80, N)]))
+    yr, a = oracle.verify_i8(w, xb, rows)
+    assert_within(y[:, rows], yr, a, f"tiles N={N} K={K} M={M}")
