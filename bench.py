@@ -401,44 +401,55 @@ def bench_chunk(args, torch, qd):
 
 
 def bench_verify(args, torch, qd):
-    """Verification GEMM: M = 16 and 32 drafted tokens x K=4096 -> N=14336, int4
-    g64 weights, fp16 activations (the decode side's dtype; bf16 reported too),
-    fp32 output; 16 weight sets cycled (528 MB). Weight-stream bound at these M."""
+    """Verification GEMM over M = 16 and 32 drafted tokens, int4 g64 weights of
+    the 7B FFN: up projection K=4096 -> N=14336 and down projection K=14336 ->
+    N=4096, fp32 output; activations fp16 or bf16 (qgemm_affine4_verify) or
+    fp16 quantized per token to int8 on the fly (qgemm_affine4_verify_i8: the
+    quantization pass and the int8 GEMM both inside the timed step); 16 weight
+    sets cycled per shape (528 MB). Weight-stream bound at these M."""
     import synth
-    K, N = 4096, 14336
     nsets = args.sets or 16
-    sets = make_sets(torch, [(K, N)], nsets, 4)
     rows = []
-    for M in (16, 32):
-        for dt in ("f16", "bf16"):
-            xb = synth.x_f16(M, K, cfg=4, set_id=2000 + M) if dt == "f16" else \
-                synth.x_bf16(M, K, cfg=4, set_id=2000 + M)
-            x = to_dev_half(torch, xb) if dt == "f16" else to_dev_bf16(torch, xb)
-            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for K, N in ((4096, 14336), (14336, 4096)):
+        sets = make_sets(torch, [(K, N)], nsets, 4)
+        for M in (16, 32):
+            ws = torch.empty(max(qd.verify_i8_workspace_bytes(M, K), 16), dtype=torch.uint8, device="cuda")
+            for dt in ("f16", "bf16", "i8"):
+                xb = synth.x_bf16(M, K, cfg=4, set_id=2000 + M) if dt == "bf16" else \
+                    synth.x_f16(M, K, cfg=4, set_id=2000 + M)
+                x = to_dev_bf16(torch, xb) if dt == "bf16" else to_dev_half(torch, xb)
+                y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-            def step(s, x=x, y=y):
-                def f():
-                    wq, sc, bi = sets[s][0][:3]
-                    qd.qgemm_affine4_verify(wq, sc, bi, x, out=y)
-                return f
+                def step(s, x=x, y=y, dt=dt, ws=ws):
+                    def f():
+                        wq, sc, bi = sets[s][0][:3]
+                        if dt == "i8":
+                            qd.qgemm_affine4_verify_i8(wq, sc, bi, x, out=y, workspace=ws)
+                        else:
+                            qd.qgemm_affine4_verify(wq, sc, bi, x, out=y)
+                    return f
 
-            secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)
-            t = secs / args.steps
-            nbytes = matrix_bytes(N, K) + M * K * 2 + M * N * 4
-            rows.append(dict(M=M, dtype=dt, us=round(t * 1e6, 2), GBps=round(nbytes / t / 1e9, 1),
-                             TFLOPs=round(2.0 * M * N * K / t / 1e12, 1), bytes=nbytes))
-    main_row = [r for r in rows if r["M"] == 32 and r["dtype"] == "f16"][0]
+                secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)
+                t = secs / args.steps
+                nbytes = matrix_bytes(N, K) + M * K * 2 + M * N * 4
+                rows.append(dict(K=K, N=N, M=M, dtype=dt, us=round(t * 1e6, 2),
+                                 GBps=round(nbytes / t / 1e9, 1),
+                                 TFLOPs=round(2.0 * M * N * K / t / 1e12, 1), bytes=nbytes))
+        del sets
+    main_row = [r for r in rows if r["M"] == 32 and r["dtype"] == "f16" and r["K"] == 4096][0]
     gbs = main_row["GBps"]
     return {"metric": "verification GEMM achieved HBM GB/s (32 drafted tokens, int4 g64 weights)",
             "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(main_row["us"] / 1e3, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
             "data": "synthetic",
-            "config": {"workload": f"verify: M drafted tokens x K={K} -> N={N}, int4 g64, "
-                                   f"{nsets} weight sets cycled", "runs": rows},
+            "config": {"workload": "verify: M drafted tokens x 7B FFN up (K=4096 -> N=14336) and down "
+                                   f"(K=14336 -> N=4096) projections, int4 g64, {nsets} weight sets "
+                                   "cycled; dtype i8 = fp16 activations quantized per token to int8 "
+                                   "inside the step", "runs": rows},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": "qgemm_affine4_verify M=32, fp16 activations",
+                         "kernel": "qgemm_affine4_verify M=32, fp16 activations, K=4096 -> N=14336",
                          "bytes_per_launch": main_row["bytes"], "avg_launch_us": main_row["us"]},
             "cpu_baseline": None}
 
