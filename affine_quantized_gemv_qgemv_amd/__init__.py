@@ -31,7 +31,8 @@ QD_GELU_ERF, QD_GELU_TANH = 0, 1
 EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
            "qgemv_mirai_l_rht", "qmoe_route_topk",
            "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
-           "qgemm_affine4_verify", "qgemm_affine4_verify_i8_workspace_bytes", "qgemm_affine4_verify_i8",
+           "qgemm_affine4_verify_workspace_bytes", "qgemm_affine4_verify",
+           "qgemm_affine4_verify_i8_workspace_bytes", "qgemm_affine4_verify_i8",
            "qattn_decode_workspace_bytes", "qattn_decode",
            "qmoe_layer_decode", "qmoe_layer_decode_noalloc", "qd_stream_read",
            "qd_status_string", "qd_last_error")
@@ -82,7 +83,10 @@ def lib() -> ctypes.CDLL:
     L.qmoe_expert_gemv.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _I32, _I32, _P, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
-    L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemm_affine4_verify_workspace_bytes.argtypes = [_I32, _I32, _I32]
+    L.qgemm_affine4_verify_workspace_bytes.restype = ctypes.c_size_t
+    L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P,
+                                       ctypes.c_size_t, _P]
     L.qgemm_affine4_verify_i8_workspace_bytes.argtypes = [_I32, _I32]
     L.qgemm_affine4_verify_i8_workspace_bytes.restype = ctypes.c_size_t
     L.qgemm_affine4_verify_i8.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, ctypes.c_size_t,
@@ -419,9 +423,15 @@ def qgemm_affine4_chunk(wq, scales, biases, x, out=None):
     return out
 
 
-def qgemm_affine4_verify(wq, scales, biases, x, out=None):
+def verify_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().qgemm_affine4_verify_workspace_bytes(M, N, K))
+
+
+def qgemm_affine4_verify(wq, scales, biases, x, out=None, workspace=None):
     """Verification GEMM Y[m][n] = sum_k w[n][k] X[m][k] over drafted tokens, fp16 or bf16
-    X [M][K], M <= 128 (built for 9..64 tokens)."""
+    X [M][K], M <= 128 (built for 9..64 tokens). Shapes with few column tiles split K and
+    need `workspace` (uint8, device) of verify_workspace_bytes(M, N, K) bytes; by default a
+    fresh one is allocated when the shape needs it."""
     _need(wq, "wq", _CODES, 2)
     _need(scales, "scales", _HALF, 2)
     _need(biases, "biases", _HALF, 2)
@@ -437,8 +447,12 @@ def qgemm_affine4_verify(wq, scales, biases, x, out=None):
     _need(out, "out", (torch.float32,), 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out must be [M][N]")
+    if workspace is None:
+        need = verify_workspace_bytes(M, N, K)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qgemm_affine4_verify(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _x_dtype(x),
-                                      _ptr(out), M, N, K, 64, _stream()))
+                                      _ptr(out), M, N, K, 64, _ptr(workspace), wsb, _stream()))
     return out
 
 

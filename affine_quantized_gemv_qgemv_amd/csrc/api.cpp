@@ -417,13 +417,19 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
     CHECK_PTR(x);
     CHECK_PTR(y);
     return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, 1 /* bf16 */, y, M, N, K,
-                                          (hipStream_t)stream),
+                                          nullptr, 0, (hipStream_t)stream),
                     fn);
+}
+
+size_t qgemm_affine4_verify_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || M > 128 || N < 1 || K < 64 || K % 64 || K > (1 << 22)) return 0;
+    return qd::chunk_split_workspace_bytes(M, N, K);
 }
 
 qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                const uint16_t* x, qd_dtype x_dtype, float* y, int32_t M, int32_t N,
-                               int32_t K, int32_t group_size, qd_stream stream) {
+                               int32_t K, int32_t group_size, void* workspace, size_t ws_bytes,
+                               qd_stream stream) {
     const char* fn = "qgemm_affine4_verify";
     qd_status st = check_matrix(fn, N, K, group_size);
     if (st != QD_OK) return st;
@@ -436,9 +442,21 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
     CHECK_PTR(biases);
     CHECK_PTR(x);
     CHECK_PTR(y);
-    // the staged chunk kernel, whose row tiles follow M (x kinds: 0 fp16, 1 bf16)
+    const size_t need = qd::chunk_split_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace)
+            return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+        if (!aligned16(workspace))
+            return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+        if (ws_bytes < need)
+            return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes,
+                        need);
+    }
+    // the staged chunk kernel, whose row tiles follow M (x kinds: 0 fp16, 1 bf16);
+    // K split when the shape needs a workspace
     return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, x_dtype == QD_F16 ? 0 : 1, y, M,
-                                          N, K, (hipStream_t)stream),
+                                          N, K, need > 0 ? workspace : nullptr, ws_bytes,
+                                          (hipStream_t)stream),
                     fn);
 }
 

@@ -61,6 +61,7 @@ struct ChunkArgs {
     int ncol_tiles;      // ceil(N / 64)
     int64_t x_row_stride;   // elements between rows of x
     int64_t y_row_stride;   // elements between rows of y
+    int gsplit;          // K split: groups per split (blockIdx.y), 0 = whole K
 };
 
 // A workgroup owns MT = 32 MB WM rows (one row tile) and 64 columns. LDS
@@ -228,9 +229,16 @@ struct ChunkSb {
 //
 // SBL: scales and biases from an LDS copy (ChunkSb), placed after the
 // staging buffers in the dynamic LDS.
-template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false, bool SBL = false>
+//
+// KSPL: K split across workgroups. Split blockIdx.y takes the groups
+// [y gsplit, min((y + 1) gsplit, K / 64)) and writes its partial Y to slice y
+// of a [splits][M][N] array (a.y); chunk_ksum_kernel then adds the slices in
+// split order. The scale/bias LDS copy needs whole rows, so SBL is off.
+template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false, bool SBL = false,
+          bool KSPL = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
+    static_assert(!(KSPL && SBL), "the scale/bias copy needs whole rows");
     constexpr int SPR = D / SG;     // stages per round
     static_assert(XD == 1 || (XD == 2 && SPR % 2 == 0), "X prefetch depth");
     constexpr int JS = SG / NKS;    // groups per stage per wave
@@ -252,18 +260,26 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     const int wq = wave % WS;                 // wave within the K-set
     const int wm = wq % WM, wn = wq / WM, ks = wave / WS;   // ks < NKS
     const int h = lane >> 5, l32 = lane & 31;
-    const int G = a.K / 64;
+    const int GR = a.K / 64;   // groups per row of the matrix
+    int G = GR, g0 = 0;        // this workgroup's groups: [g0, g0 + G)
+    if constexpr (KSPL) {
+        g0 = (int)blockIdx.y * a.gsplit;
+        G = min(a.gsplit, GR - g0);
+        a.x += (int64_t)g0 * 64;
+        a.y += (int64_t)blockIdx.y * a.M * a.y_row_stride;
+    }
     const int NS = (G + SG - 1) / SG;
     // workgroups on one XCD are 8 apart in blockIdx.x: spread their starts
     const int rot = (int)((unsigned)(b >> 3) * (unsigned)SG % (unsigned)G);
     const int64_t wpr = a.K / 8;
     const int n = ct * CH_NT + wn * 32 + l32;                // this lane's column
     const int nc = min(n, a.N - 1);
-    const uint32_t* wrow = a.wq + (int64_t)nc * wpr + 4 * h;  // words 4h..4h+3 of group 0
+    // words 4h..4h+3 of group g0
+    const uint32_t* wrow = a.wq + (int64_t)nc * wpr + (int64_t)g0 * 8 + 4 * h;
     // SBL: the tile's copy in LDS ([64 G] scales, then [64 G] biases)
     uint16_t* sbl = (uint16_t*)(smem + L::bytes / 16);
-    const uint16_t* srow = SBL ? sbl + (nc - ct * CH_NT) * (G + 2) : a.s + (int64_t)nc * G;
-    const uint16_t* brow = SBL ? sbl + (64 + nc - ct * CH_NT) * (G + 2) : a.b + (int64_t)nc * G;
+    const uint16_t* srow = SBL ? sbl + (nc - ct * CH_NT) * (G + 2) : a.s + (int64_t)nc * GR + g0;
+    const uint16_t* brow = SBL ? sbl + (64 + nc - ct * CH_NT) * (G + 2) : a.b + (int64_t)nc * GR + g0;
 
     floatx16 acc[MB];
 #pragma unroll
@@ -471,17 +487,84 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
     }
 }
 
-template <int SG, int D, int MB, int WM, int NKS, bool F16, bool SBL = false>
-static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st) {
+// Y = sum of the split slices part[0..splits) ([splits][n] fp32), added in
+// split order, so results do not depend on timing. Four elements per thread.
+__global__ __launch_bounds__(256) void chunk_ksum_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ y, int splits,
+                                                         int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    if ((n & 3) == 0) {
+        float4 acc = *(const float4*)(part + i);
+        for (int sp = 1; sp < splits; ++sp) {
+            const float4 v = *(const float4*)(part + (int64_t)sp * n + i);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        *(float4*)(y + i) = acc;
+        return;
+    }
+    for (int64_t j = i; j < min(i + 4, n); ++j) {
+        float acc = part[j];
+        for (int sp = 1; sp < splits; ++sp) acc += part[(int64_t)sp * n + j];
+        y[j] = acc;
+    }
+}
+
+// K split of a call with fewer than CH_SPLIT_TILES tiles, which would leave
+// CUs idle (a short N, e.g. a down projection over a few dozen tokens):
+// enough splits that tiles x splits reaches CH_SPLIT_WG workgroups, each
+// split at least CH_SPLIT_MIN_G groups. Depends on the shape only, so a shape
+// always sums in the same order.
+constexpr int CH_SPLIT_TILES = 128;
+constexpr int CH_SPLIT_WG = 256;
+constexpr int CH_SPLIT_MIN_G = 16;
+
+static int chunk_row_tile(int M) { return M <= 32 ? 32 : M <= 64 ? 64 : 128; }
+
+ChunkSplit chunk_split(int M, int N, int K) {
+    const int G = K / 64;
+    if (M < 1 || N < 1 || G < 1 || M > CH_MMAX) return {1, G};
+    const int tiles = ((N + CH_NT - 1) / CH_NT) * ((M + chunk_row_tile(M) - 1) / chunk_row_tile(M));
+    const int sp = min((CH_SPLIT_WG + tiles - 1) / tiles, G / CH_SPLIT_MIN_G);
+    if (tiles >= CH_SPLIT_TILES || sp <= 1) return {1, G};
+    const int gs = (G + sp - 1) / sp;
+    return {(G + gs - 1) / gs, gs};
+}
+
+size_t chunk_split_workspace_bytes(int M, int N, int K) {
+    const ChunkSplit c = chunk_split(M, N, K);
+    return c.splits > 1 ? (size_t)c.splits * M * N * sizeof(float) : 0;
+}
+
+template <int SG, int D, int MB, int WM, int NKS, bool F16, bool SBL = false, bool KSPL = false>
+static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st, int splits = 1) {
     constexpr int MT = 32 * MB * WM;
     const int RT = (a.M + MT - 1) / MT;
     const int grid = ((a.ncol_tiles + 7) / 8) * 8 * RT;
     const size_t lds = ChunkLds<SG, MT, F16>::bytes + (SBL ? (size_t)256 * (a.K / 64 + 2) : 0);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     constexpr int threads = 128 * WM * NKS;
-    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16, SBL>;
+    auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16, SBL, KSPL>;
     (void)occupancy((const void*)kern, threads, lds);  // sets the dynamic-LDS limit once
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3(grid, splits), dim3(threads), lds, st, a);
+    return hipGetLastError();
+}
+
+// The K-split launch: the partial slices go to `part` ([splits][M][N]), then
+// one pass adds them into y.
+template <int SG, int D, int MB, int WM, int NKS, bool F16>
+static hipError_t launch_chunk_split(ChunkArgs a, const ChunkSplit& c, float* part, hipStream_t st) {
+    float* y = a.y;
+    a.y = part;
+    a.gsplit = c.gsplit;
+    hipError_t e = launch_chunk_cfg<SG, D, MB, WM, NKS, F16, false, true>(a, st, c.splits);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)a.M * a.N;
+    hipLaunchKernelGGL(chunk_ksum_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, st,
+                       (const float*)part, y, c.splits, n);
     return hipGetLastError();
 }
 
@@ -497,7 +580,7 @@ static hipError_t launch_chunk_sb(const ChunkArgs& a, hipStream_t st) {
 
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x, int xkind, float* y, int M, int N, int K,
-                             hipStream_t st) {
+                             void* ws, size_t ws_bytes, hipStream_t st) {
     if (bits != 4 || M > CH_MMAX || (xkind != X_F16 && xkind != X_BF16)) return hipErrorInvalidValue;
     ChunkArgs a{};
     a.wq = wq;
@@ -516,6 +599,21 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
 // and four K-sets; beyond, the whole chunk as four row blocks per wave, 2
 // column waves x 4 K-sets = 8 waves (2 per SIMD). All use 4 groups per stage
 // and a ring of 8 groups.
+    if (ws != nullptr) {
+        const ChunkSplit c = chunk_split(M, N, K);
+        if (c.splits > 1) {
+            if (ws_bytes < chunk_split_workspace_bytes(M, N, K)) return hipErrorInvalidValue;
+            float* part = (float*)ws;
+            if (xkind == X_F16) {
+                if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, true>(a, c, part, st);
+                if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, true>(a, c, part, st);
+                return launch_chunk_split<4, 8, 4, 1, 4, true>(a, c, part, st);
+            }
+            if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, false>(a, c, part, st);
+            if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, false>(a, c, part, st);
+            return launch_chunk_split<4, 8, 4, 1, 4, false>(a, c, part, st);
+        }
+    }
     if (xkind == X_F16) {
         if (M <= 32) return launch_chunk_sb<4, 8, 1, 1, 2, true>(a, st);
         if (M <= 64) return launch_chunk_sb<4, 8, 2, 1, 4, true>(a, st);

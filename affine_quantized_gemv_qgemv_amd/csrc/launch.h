@@ -100,9 +100,18 @@ hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* k_new, const ui
 // Read-only stream over bytes of device memory (the HBM read ceiling).
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st);
 
-// x: fp16 or bf16 bits (xkind X_F16 / X_BF16), [M][K].
+// x: fp16 or bf16 bits (xkind X_F16 / X_BF16), [M][K]. With a workspace of
+// chunk_split_workspace_bytes(M, N, K) bytes, shapes with few tiles split K
+// across workgroups (chunk_split) and add the slices in a second pass; with
+// ws == nullptr the call runs unsplit.
+struct ChunkSplit {
+    int splits;   // K splits (1 = none)
+    int gsplit;   // groups per split; the last one takes the rest
+};
+ChunkSplit chunk_split(int M, int N, int K);
+size_t chunk_split_workspace_bytes(int M, int N, int K);
 hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                              const uint16_t* x, int xkind, float* y, int M, int N, int K,
-                             hipStream_t st);
+                             void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace qd

@@ -414,19 +414,20 @@ def bench_verify(args, torch, qd):
         sets = make_sets(torch, [(K, N)], nsets, 4)
         for M in (16, 32):
             ws = torch.empty(max(qd.verify_i8_workspace_bytes(M, K), 16), dtype=torch.uint8, device="cuda")
+            vws = torch.empty(max(qd.verify_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
             for dt in ("f16", "bf16", "i8"):
                 xb = synth.x_bf16(M, K, cfg=4, set_id=2000 + M) if dt == "bf16" else \
                     synth.x_f16(M, K, cfg=4, set_id=2000 + M)
                 x = to_dev_bf16(torch, xb) if dt == "bf16" else to_dev_half(torch, xb)
                 y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-                def step(s, x=x, y=y, dt=dt, ws=ws):
+                def step(s, x=x, y=y, dt=dt, ws=ws, vws=vws):
                     def f():
                         wq, sc, bi = sets[s][0][:3]
                         if dt == "i8":
                             qd.qgemm_affine4_verify_i8(wq, sc, bi, x, out=y, workspace=ws)
                         else:
-                            qd.qgemm_affine4_verify(wq, sc, bi, x, out=y)
+                            qd.qgemm_affine4_verify(wq, sc, bi, x, out=y, workspace=vws)
                     return f
 
                 secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)

@@ -254,11 +254,21 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
  *   codes as the matrix operand and the scales and biases applied per group
  *   in fp32; built for the 9..64-token range between the GEMV kernels and a
  *   prefill chunk.
+ *   workspace: shapes with few 64-column tiles (a short N such as a down
+ *   projection) split K across workgroups; their fp32 partial results go to
+ *   the workspace, 16-byte aligned, of at least
+ *   qgemm_affine4_verify_workspace_bytes(M, N, K) bytes, and a second launch
+ *   adds them in a fixed order. That size is 0 for shapes that run unsplit
+ *   (and for arguments out of range); then workspace may be NULL. Otherwise
+ *   NULL or too small fails with QD_ERR_WORKSPACE before any launch. The
+ *   split depends on (M, N, K) only, so results do not depend on timing;
+ *   calls that share a workspace must be ordered on a stream.
  */
+size_t qgemm_affine4_verify_workspace_bytes(int32_t M, int32_t N, int32_t K);
 qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                                const uint16_t* x, qd_dtype x_dtype, float* y,
                                int32_t M, int32_t N, int32_t K, int32_t group_size,
-                               qd_stream stream);
+                               void* workspace, size_t ws_bytes, qd_stream stream);
 
 /*
  * Verification GEMM on int8 activations (uzu page on discuss.pytorch.kr,

@@ -91,8 +91,13 @@ int main() {
     // chunk and verification GEMMs
     EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 128, 14336, 4096, 64, nullptr), QD_OK);
     EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 129, 14336, 4096, 64, nullptr), QD_ERR_INVALID_ARGUMENT);
-    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 14336, 4096, 64, nullptr), QD_OK);
-    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, (qd_dtype)2, y, 32, 14336, 4096, 64, nullptr), QD_ERR_UNSUPPORTED);
+    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 14336, 4096, 64, nullptr, 0, nullptr), QD_OK);
+    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, (qd_dtype)2, y, 32, 14336, 4096, 64, nullptr, 0, nullptr), QD_ERR_UNSUPPORTED);
+    const size_t kws = qgemm_affine4_verify_workspace_bytes(32, 4096, 14336);
+    if (!(kws > 0) || qgemm_affine4_verify_workspace_bytes(129, 4096, 14336) != 0) ++fails;
+    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 4096, 14336, 64, A, kws, nullptr), QD_OK);
+    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 4096, 14336, 64, A, kws - 1, nullptr), QD_ERR_WORKSPACE);
+    EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 4096, 14336, 64, nullptr, kws, nullptr), QD_ERR_WORKSPACE);
     // decode attention
     const size_t vws = qgemm_affine4_verify_i8_workspace_bytes(32, 4096);
     if (!(vws > 0) || qgemm_affine4_verify_i8_workspace_bytes(33, 4096) != 0) ++fails;

@@ -63,8 +63,14 @@ hipError_t launch_attn_decode(const uint16_t*, const uint16_t*, const uint16_t*,
     ++g_launches;
     return hipSuccess;
 }
+// K split of shapes with fewer than 128 column x row tiles (N < 8192 at one row tile)
+size_t chunk_split_workspace_bytes(int M, int N, int K) {
+    const int mt = M <= 32 ? 32 : M <= 64 ? 64 : 128;
+    const int tiles = ((N + 63) / 64) * ((M + mt - 1) / mt);
+    return tiles < 128 && K >= 2048 ? (size_t)2 * M * N * 4 : 0;
+}
 hipError_t launch_chunk_gemm(int, const uint32_t*, const uint16_t*, const uint16_t*, const uint16_t*,
-                             int, float*, int, int, int, hipStream_t) {
+                             int, float*, int, int, int, void*, size_t, hipStream_t) {
     ++g_launches;
     return hipSuccess;
 }

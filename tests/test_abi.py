@@ -214,8 +214,8 @@ def test_verify_argument_errors():
     E = qd
     L = qd.lib()
 
-    def v(wq=A, s=A, b=A, x=A, dt=0, y=A, M=16, N=16, K=128, gs=64):
-        return L.qgemm_affine4_verify(wq, s, b, x, dt, y, M, N, K, gs, None)
+    def v(wq=A, s=A, b=A, x=A, dt=0, y=A, M=16, N=16, K=128, gs=64, w=None, wsb=0):
+        return L.qgemm_affine4_verify(wq, s, b, x, dt, y, M, N, K, gs, w, wsb, None)
 
     assert v(M=0) == E.QD_ERR_INVALID_ARGUMENT
     assert v(M=129) == E.QD_ERR_INVALID_ARGUMENT
@@ -224,6 +224,31 @@ def test_verify_argument_errors():
     assert v(dt=2) == E.QD_ERR_UNSUPPORTED
     assert v(b=None) == E.QD_ERR_INVALID_ARGUMENT
     assert v(x=MIS) == E.QD_ERR_MISALIGNED
+    # a down projection (N = 4096, 64 column tiles) splits K; a wide matrix does not
+    ws = qd.verify_workspace_bytes(32, 4096, 14336)
+    assert ws > 0 and ws % (32 * 4096 * 4) == 0
+    assert qd.verify_workspace_bytes(32, 28672, 4096) == 0
+    assert qd.verify_workspace_bytes(0, 4096, 14336) == 0 and qd.verify_workspace_bytes(129, 4096, 14336) == 0
+    assert qd.verify_workspace_bytes(16, 4096, 100) == 0
+    assert v(M=32, N=4096, K=14336) == E.QD_ERR_WORKSPACE
+    assert v(M=32, N=4096, K=14336, w=A, wsb=ws - 1) == E.QD_ERR_WORKSPACE
+    assert v(M=32, N=4096, K=14336, w=MIS, wsb=ws) == E.QD_ERR_MISALIGNED
+
+
+def test_verify_split_plan_covers_k_once():
+    # every split shape: the slices tile K exactly, each at least 16 groups, and the
+    # workspace holds splits x M x N fp32
+    for M in (1, 16, 32, 33, 64, 65, 128):
+        for N in (1, 64, 100, 4096, 8192):
+            for K in (64, 1024, 2048, 4096, 14336, 1 << 22):
+                ws = qd.verify_workspace_bytes(M, N, K)
+                if ws == 0:
+                    continue
+                splits = ws // (4 * M * N)
+                assert ws == splits * 4 * M * N and 2 <= splits
+                G = K // 64
+                gs = -(-G // splits)
+                assert -(-G // gs) == splits and gs >= 16 and G - (splits - 1) * gs >= 1
 
 
 def test_verify_i8_argument_errors():

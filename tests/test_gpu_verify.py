@@ -108,3 +108,82 @@ def test_full_size_7b_ffn(xdt, M):
     rows = np.unique(np.concatenate([np.random.default_rng(M).choice(N, 256, replace=False), [0, N - 1]]))
     yr, a = ref(w, xb, xdt, rows)
     assert_within(y[:, rows], yr, a, f"full {xdt} M={M}")
+
+
+# K split: shapes with fewer than 128 column x row tiles spread K over
+# workgroups and add the slices in a second pass (the workspace)
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [1, 16, 32, 33, 64, 65, 128])
+@pytest.mark.parametrize("N,K", [(130, 3200), (64, 2368), (4096, 2048)])
+def test_split_k_ragged(xdt, M, N, K):
+    ws = qd.verify_workspace_bytes(M, N, K)
+    splits = ws // (4 * M * N)
+    assert splits >= 2
+    seed = 7 * M + N + K
+    w = synth.affine_weights(4, N, K, cfg=516, set_id=seed)
+    xb = draw_x(M, K, xdt, seed)
+    print(f"verify split {xdt} M={M} N={N} K={K} splits={splits}", flush=True)
+    y = run(w, xb, xdt).cpu().numpy()
+    if N * M <= 64 * 1088 * 2:
+        yr, a = ref(w, xb, xdt)
+        assert_within(y, yr, a, f"split {xdt} M={M} N={N} K={K}")
+    else:
+        rows = np.unique(np.concatenate([np.random.default_rng(seed).choice(N, 200, replace=False), [0, N - 1]]))
+        yr, a = ref(w, xb, xdt, rows)
+        assert_within(y[:, rows], yr, a, f"split {xdt} M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_split_k_extreme_and_near_zero_codes(xdt):
+    N, K, M = 96, 4096, 20
+    for kind, c in (("zero", 0), ("const", 15), ("const", 8)):
+        w = synth.affine_weights(4, N, K, cfg=517, set_id=c, codes=kind, const_code=c)
+        xb = draw_x(M, K, xdt, c)
+        y = run(w, xb, xdt).cpu().numpy()
+        yr, a = ref(w, xb, xdt)
+        assert_within(y, yr, a, f"split {kind} {c} {xdt}")
+
+
+def test_split_k_deterministic_and_in_bounds():
+    # two calls bitwise equal; Y and the workspace written only inside their
+    # bounds; a workspace holding stale values from another shape changes nothing
+    for xdt in ("f16", "bf16"):
+        N, K, M = 4096, 14336, 32
+        ws = qd.verify_workspace_bytes(M, N, K)
+        assert ws > 0
+        w = synth.affine_weights(4, N, K, cfg=518, set_id=0)
+        xb = draw_x(M, K, xdt, 4)
+        wq, s, b = dev_weights(w)
+        x = dev_half(xb) if xdt == "f16" else dev_bf16(xb)
+        guard = 4096
+        ybuf = torch.full((guard + M * N + guard,), float("nan"), device="cuda")
+        wbuf = torch.full((guard + ws // 4 + guard,), float("nan"), device="cuda")
+        out = ybuf[guard:guard + M * N].view(M, N)
+        wsp = wbuf[guard:guard + ws // 4].view(torch.uint8)
+        y1 = qd.qgemm_affine4_verify(wq, s, b, x, out=out, workspace=wsp).clone()
+        torch.cuda.synchronize()
+        assert torch.isnan(ybuf[:guard]).all() and torch.isnan(ybuf[guard + M * N:]).all()
+        assert torch.isnan(wbuf[:guard]).all() and torch.isnan(wbuf[guard + ws // 4:]).all()
+        # stale contents from a smaller split shape, then the same call again
+        x2 = x[:7].contiguous()
+        qd.qgemm_affine4_verify(wq, s, b, x2, workspace=wsp)
+        y2 = qd.qgemm_affine4_verify(wq, s, b, x, workspace=wsp)
+        y3 = qd.qgemm_affine4_verify(wq, s, b, x)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(y1, y3)
+        with pytest.raises(qd.QDecodeError):
+            qd.qgemm_affine4_verify(wq, s, b, x, workspace=wsp[:ws - 16])
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [16, 32, 128])
+def test_full_size_7b_down_projection(xdt, M):
+    K, N = 14336, 4096
+    print(f"verify full down {xdt} M={M}", flush=True)
+    w = synth.affine_weights(4, N, K, cfg=519, set_id=0)
+    xb = draw_x(M, K, xdt, 6)
+    y = run(w, xb, xdt).cpu().numpy()
+    rows = np.unique(np.concatenate([np.random.default_rng(M + 1).choice(N, 128, replace=False), [0, N - 1]]))
+    yr, a = ref(w, xb, xdt, rows)
+    assert_within(y[:, rows], yr, a, f"full down {xdt} M={M}")
