@@ -177,14 +177,24 @@ template <int NTH>
 struct ChunkSb {
     static constexpr int KMAX = (16 * CH_SB_GMAX + NTH - 1) / NTH;   // uint4 per thread
     uint4 v[KMAX];
-    // all loads issued (indices clamp to the two runs, [8 G] uint4 each)
-    __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b, int G) {
-        const int n8 = 8 * G;
+    // all loads issued (indices clamp to the two runs, [8 G] uint4 each).
+    // STRIDED: the tile's rows are rs halfwords apart (a K split copies its
+    // G groups of rows of rs groups; 8 | rs and the split starts at a
+    // multiple of 8 groups, so every row run stays 16-byte aligned)
+    template <bool STRIDED = false>
+    __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b, int G, int rs = 0) {
+        const int n8 = 8 * G, upr = G / 8;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             const int i = min((int)threadIdx.x + NTH * k, 2 * n8 - 1);
-            const uint4* src = i < n8 ? (const uint4*)s + i : (const uint4*)b + (i - n8);
-            v[k] = *src;
+            if constexpr (STRIDED) {
+                const int arr = i >= n8, j = i - arr * n8;
+                const int r = j / upr, c = j - r * upr;
+                v[k] = *(const uint4*)((arr ? b : s) + (int64_t)r * rs + 8 * c);
+            } else {
+                const uint4* src = i < n8 ? (const uint4*)s + i : (const uint4*)b + (i - n8);
+                v[k] = *src;
+            }
         }
     }
     // dst: [64 rows][G + 2] scales, then the same for the biases
@@ -233,12 +243,12 @@ struct ChunkSb {
 // KSPL: K split across workgroups. Split blockIdx.y takes the groups
 // [y gsplit, min((y + 1) gsplit, K / 64)) and writes its partial Y to slice y
 // of a [splits][M][N] array (a.y); chunk_ksum_kernel then adds the slices in
-// split order. The scale/bias LDS copy needs whole rows, so SBL is off.
+// split order. With SBL the scale/bias copy takes the split's part of each
+// row (a strided copy).
 template <int SG, int D, int MB, int WM, int NKS, int XD = 1, bool F16 = false, bool SBL = false,
           bool KSPL = false>
 __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a) {
     static_assert(D % SG == 0 && SG % NKS == 0 && SG == 4, "stage shape");
-    static_assert(!(KSPL && SBL), "the scale/bias copy needs whole rows");
     constexpr int SPR = D / SG;     // stages per round
     static_assert(XD == 1 || (XD == 2 && SPR % 2 == 0), "X prefetch depth");
     constexpr int JS = SG / NKS;    // groups per stage per wave
@@ -302,7 +312,8 @@ __global__ __launch_bounds__(128 * WM * NKS) void chunk_gemm_kernel(ChunkArgs a)
         IO::load(a, m0, 0, G, rot, xr[0]);
         __builtin_amdgcn_sched_barrier(0);
         ChunkSb<128 * WM * NKS> sbc;
-        sbc.load(a.s + (int64_t)ct * CH_NT * G, a.b + (int64_t)ct * CH_NT * G, G);
+        sbc.template load<KSPL>(a.s + (int64_t)ct * CH_NT * GR + g0, a.b + (int64_t)ct * CH_NT * GR + g0,
+                                G, GR);
 #pragma unroll
         for (int e = 0; e < DW; ++e) bq[e] = *(const uint4*)(wrow + (int64_t)rot_group(NKS * e + ks, G, rot) * 8);
         __builtin_amdgcn_sched_barrier(0);
@@ -516,8 +527,9 @@ __global__ __launch_bounds__(256) void chunk_ksum_kernel(const float* __restrict
 // K split of a call with fewer than CH_SPLIT_TILES tiles, which would leave
 // CUs idle (a short N, e.g. a down projection over a few dozen tokens):
 // enough splits that tiles x splits reaches CH_SPLIT_WG workgroups, each
-// split at least CH_SPLIT_MIN_G groups. Depends on the shape only, so a shape
-// always sums in the same order.
+// split at least CH_SPLIT_MIN_G groups and, when 8 | G, a multiple of 8 (the
+// scale/bias LDS copy then still applies). Depends on the shape only, so a
+// shape always sums in the same order.
 constexpr int CH_SPLIT_TILES = 128;
 constexpr int CH_SPLIT_WG = 256;
 constexpr int CH_SPLIT_MIN_G = 16;
@@ -530,7 +542,8 @@ ChunkSplit chunk_split(int M, int N, int K) {
     const int tiles = ((N + CH_NT - 1) / CH_NT) * ((M + chunk_row_tile(M) - 1) / chunk_row_tile(M));
     const int sp = min((CH_SPLIT_WG + tiles - 1) / tiles, G / CH_SPLIT_MIN_G);
     if (tiles >= CH_SPLIT_TILES || sp <= 1) return {1, G};
-    const int gs = (G + sp - 1) / sp;
+    int gs = (G + sp - 1) / sp;
+    if (G % 8 == 0) gs = (gs + 7) / 8 * 8;   // splits start on 16-byte scale/bias runs
     return {(G + gs - 1) / gs, gs};
 }
 
@@ -544,7 +557,8 @@ static hipError_t launch_chunk_cfg(const ChunkArgs& a, hipStream_t st, int split
     constexpr int MT = 32 * MB * WM;
     const int RT = (a.M + MT - 1) / MT;
     const int grid = ((a.ncol_tiles + 7) / 8) * 8 * RT;
-    const size_t lds = ChunkLds<SG, MT, F16>::bytes + (SBL ? (size_t)256 * (a.K / 64 + 2) : 0);
+    const size_t lds = ChunkLds<SG, MT, F16>::bytes +
+                       (SBL ? (size_t)256 * ((KSPL ? a.gsplit : a.K / 64) + 2) : 0);
     if (lds > device_info().max_lds_per_block) return hipErrorInvalidValue;
     constexpr int threads = 128 * WM * NKS;
     auto kern = chunk_gemm_kernel<SG, D, MB, WM, NKS, 1, F16, SBL, KSPL>;
@@ -560,7 +574,15 @@ static hipError_t launch_chunk_split(ChunkArgs a, const ChunkSplit& c, float* pa
     float* y = a.y;
     a.y = part;
     a.gsplit = c.gsplit;
-    hipError_t e = launch_chunk_cfg<SG, D, MB, WM, NKS, F16, false, true>(a, st, c.splits);
+    // the scale/bias copy as unsplit: row tiles up to 64 (the 128-row tile's
+    // staging leaves no LDS for it), whole column tiles, 8 | split length
+    const int G = a.K / 64;
+    hipError_t e;
+    if (32 * MB * WM <= 64 && a.N % CH_NT == 0 && G % 8 == 0 && c.gsplit % 8 == 0 &&
+        c.gsplit <= CH_SB_GMAX)
+        e = launch_chunk_cfg<SG, D, MB, WM, NKS, F16, 32 * MB * WM <= 64, true>(a, st, c.splits);
+    else
+        e = launch_chunk_cfg<SG, D, MB, WM, NKS, F16, false, true>(a, st, c.splits);
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)a.M * a.N;
     hipLaunchKernelGGL(chunk_ksum_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, st,
