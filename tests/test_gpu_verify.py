@@ -187,3 +187,34 @@ def test_full_size_7b_down_projection(xdt, M):
     rows = np.unique(np.concatenate([np.random.default_rng(M + 1).choice(N, 128, replace=False), [0, N - 1]]))
     yr, a = ref(w, xb, xdt, rows)
     assert_within(y[:, rows], yr, a, f"full down {xdt} M={M}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_split_k_at_the_largest_k(xdt):
+    # K = 2^22 on 3 rows: 256 splits of 256 groups; M N = 6 is not a multiple
+    # of 4 (the adding pass's element-wise tail)
+    K, N, M = 1 << 22, 3, 2
+    ws = qd.verify_workspace_bytes(M, N, K)
+    assert ws // (4 * M * N) == 256
+    w = synth.affine_weights(4, N, K, cfg=520, set_id=0)
+    xb = draw_x(M, K, xdt, 8)
+    print(f"verify split K=2^22 {xdt}", flush=True)
+    y = run(w, xb, xdt).cpu().numpy()
+    yr, a = ref(w, xb, xdt)
+    assert_within(y, yr, a, f"split K=2^22 {xdt}")
+
+
+def test_split_k_ragged_elementwise_tail():
+    # M N odd on a split shape: every element, including the last, written once
+    for M, N, K in ((3, 7, 2048), (5, 65, 4096)):
+        ws = qd.verify_workspace_bytes(M, N, K)
+        assert ws > 0 and (M * N) % 4 != 0
+        w = synth.affine_weights(4, N, K, cfg=521, set_id=M)
+        xb = draw_x(M, K, "f16", M)
+        guard = 64
+        buf = torch.full((guard + M * N + guard,), float("nan"), device="cuda")
+        out = buf[guard:guard + M * N].view(M, N)
+        y = run(w, xb, "f16", out=out).cpu().numpy()
+        assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * N:]).all()
+        yr, a = ref(w, xb, "f16")
+        assert_within(y, yr, a, f"split tail M={M} N={N}")
