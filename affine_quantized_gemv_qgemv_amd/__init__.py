@@ -30,7 +30,8 @@ QD_GELU_ERF, QD_GELU_TANH = 0, 1
 
 EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "qgemv_mirai_m_rht",
            "qgemv_mirai_l_rht", "qmoe_route_topk",
-           "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk",
+           "qmoe_expert_workspace_bytes", "qmoe_expert_gemv", "qgemm_affine4_chunk_workspace_bytes",
+           "qgemm_affine4_chunk",
            "qgemm_affine4_verify_workspace_bytes", "qgemm_affine4_verify",
            "qgemm_affine4_verify_i8_workspace_bytes", "qgemm_affine4_verify_i8",
            "qattn_decode_workspace_bytes", "qattn_decode",
@@ -82,7 +83,9 @@ def lib() -> ctypes.CDLL:
     L.qmoe_expert_workspace_bytes.restype = ctypes.c_size_t
     L.qmoe_expert_gemv.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _I32, _I32, _P, ctypes.c_int,
                                    _P, _P, ctypes.c_size_t, _P]
-    L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P]
+    L.qgemm_affine4_chunk_workspace_bytes.argtypes = [_I32, _I32, _I32]
+    L.qgemm_affine4_chunk_workspace_bytes.restype = ctypes.c_size_t
+    L.qgemm_affine4_chunk.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, ctypes.c_size_t, _P]
     L.qgemm_affine4_verify_workspace_bytes.argtypes = [_I32, _I32, _I32]
     L.qgemm_affine4_verify_workspace_bytes.restype = ctypes.c_size_t
     L.qgemm_affine4_verify.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _P,
@@ -405,8 +408,15 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     _check(lib().qd_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream()))
 
 
-def qgemm_affine4_chunk(wq, scales, biases, x, out=None):
-    """Prefill chunk Y[m][n] = sum_k w[n][k] X[m][k] for bf16 X [M][K], M <= 128."""
+def chunk_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().qgemm_affine4_chunk_workspace_bytes(M, N, K))
+
+
+def qgemm_affine4_chunk(wq, scales, biases, x, out=None, workspace=None):
+    """Prefill chunk Y[m][n] = sum_k w[n][k] X[m][k] for bf16 X [M][K], M <= 128. Shapes
+    with few column tiles split K and need `workspace` (uint8, device) of
+    chunk_workspace_bytes(M, N, K) bytes; by default a fresh one is allocated when the
+    shape needs it."""
     _need(wq, "wq", _CODES, 2)
     _need(scales, "scales", _HALF, 2)
     _need(biases, "biases", _HALF, 2)
@@ -415,11 +425,19 @@ def qgemm_affine4_chunk(wq, scales, biases, x, out=None):
     M = x.shape[0]
     if x.shape[1] != K:
         raise ValueError("x must be [M][K]")
+    if tuple(scales.shape) != (N, K // 64) or tuple(biases.shape) != (N, K // 64):
+        raise ValueError("scales/biases must be [N][K/64]")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M][N]")
+    if workspace is None:
+        need = chunk_workspace_bytes(M, N, K)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qgemm_affine4_chunk(_ptr(wq), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), M, N,
-                                     K, 64, _stream()))
+                                     K, 64, _ptr(workspace), wsb, _stream()))
     return out
 
 

@@ -403,9 +403,30 @@ qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* rou
                     fn);
 }
 
+// Bytes of the K-split workspace of the chunk kernel (0: the shape runs unsplit).
+size_t chunk_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || M > 128 || N < 1 || K < 64 || K % 64 || K > (1 << 22)) return 0;
+    return qd::chunk_split_workspace_bytes(M, N, K);
+}
+
+// The workspace a K-split shape needs: present, aligned and large enough.
+qd_status check_split_workspace(const char* fn, size_t need, const void* workspace, size_t ws_bytes) {
+    if (need == 0) return QD_OK;
+    if (!workspace) return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned16(workspace)) return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (ws_bytes < need)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    return QD_OK;
+}
+
+size_t qgemm_affine4_chunk_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    return chunk_workspace_bytes(M, N, K);
+}
+
 qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y, int32_t M, int32_t N, int32_t K,
-                              int32_t group_size, qd_stream stream) {
+                              int32_t group_size, void* workspace, size_t ws_bytes,
+                              qd_stream stream) {
     const char* fn = "qgemm_affine4_chunk";
     qd_status st = check_matrix(fn, N, K, group_size);
     if (st != QD_OK) return st;
@@ -416,14 +437,17 @@ qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const 
     CHECK_PTR(biases);
     CHECK_PTR(x);
     CHECK_PTR(y);
+    const size_t need = chunk_workspace_bytes(M, N, K);
+    st = check_split_workspace(fn, need, workspace, ws_bytes);
+    if (st != QD_OK) return st;
     return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, 1 /* bf16 */, y, M, N, K,
-                                          nullptr, 0, (hipStream_t)stream),
+                                          need > 0 ? workspace : nullptr, ws_bytes,
+                                          (hipStream_t)stream),
                     fn);
 }
 
 size_t qgemm_affine4_verify_workspace_bytes(int32_t M, int32_t N, int32_t K) {
-    if (M < 1 || M > 128 || N < 1 || K < 64 || K % 64 || K > (1 << 22)) return 0;
-    return qd::chunk_split_workspace_bytes(M, N, K);
+    return chunk_workspace_bytes(M, N, K);
 }
 
 qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
@@ -442,16 +466,9 @@ qd_status qgemm_affine4_verify(const uint32_t* wq, const uint16_t* scales, const
     CHECK_PTR(biases);
     CHECK_PTR(x);
     CHECK_PTR(y);
-    const size_t need = qd::chunk_split_workspace_bytes(M, N, K);
-    if (need > 0) {
-        if (!workspace)
-            return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
-        if (!aligned16(workspace))
-            return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
-        if (ws_bytes < need)
-            return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes,
-                        need);
-    }
+    const size_t need = chunk_workspace_bytes(M, N, K);
+    st = check_split_workspace(fn, need, workspace, ws_bytes);
+    if (st != QD_OK) return st;
     // the staged chunk kernel, whose row tiles follow M (x kinds: 0 fp16, 1 bf16);
     // K split when the shape needs a workspace
     return from_hip(qd::launch_chunk_gemm(4, wq, scales, biases, x, x_dtype == QD_F16 ? 0 : 1, y, M,

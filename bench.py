@@ -366,23 +366,32 @@ def run_dense(args, torch, qd, shapes, batch, sets, cfg_id, fmt="affine", rht=Fa
 
 def bench_chunk(args, torch, qd):
     """Prefill chunk: M=128 x K=4096 x N=14336 int4 g64 weights, bf16 activations,
-    fp32 output; 16 weight sets cycled (528 MB)."""
+    fp32 output; 16 weight sets cycled (528 MB). Beside it the 7B down projection
+    over the same chunk (K=14336 -> N=4096, K split across workgroups)."""
     import synth
-    M, K, N = 128, 4096, 14336
+    M = 128
     nsets = args.sets or 16
-    sets = make_sets(torch, [(K, N)], nsets, 4)
-    xb = synth.x_bf16(M, K, cfg=4, set_id=1000)
-    x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
-    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
 
-    def step(s):
-        def f():
-            wq, sc, bi = sets[s][0][:3]
-            qd.qgemm_affine4_chunk(wq, sc, bi, x, out=y)
-        return f
+    def one(K, N):
+        sets = make_sets(torch, [(K, N)], nsets, 4)
+        xb = synth.x_bf16(M, K, cfg=4, set_id=1000)
+        x = torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(qd.chunk_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
 
-    secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)
-    t = secs / args.steps
+        def step(s):
+            def f():
+                wq, sc, bi = sets[s][0][:3]
+                qd.qgemm_affine4_chunk(wq, sc, bi, x, out=y, workspace=ws)
+            return f
+
+        secs, _ = Timer(torch).run([step(s) for s in range(nsets)], args.steps, args.warmup)
+        del sets
+        return secs / args.steps
+
+    K, N = 4096, 14336
+    t = one(K, N)
+    td = one(14336, 4096)
     flops = 2.0 * M * N * K
     nbytes = matrix_bytes(N, K) + M * K * 2 + M * N * 4
     tflops = flops / t / 1e12
@@ -392,7 +401,11 @@ def bench_chunk(args, torch, qd):
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"c4: prefill chunk M={M} x K={K} x N={N}, int4 g64, "
                                    f"{nsets} weight sets cycled", "us_per_call": round(t * 1e6, 2),
-                       "GBps": round(nbytes / t / 1e9, 1)},
+                       "GBps": round(nbytes / t / 1e9, 1),
+                       "down_projection": {"K": 14336, "N": 4096, "us_per_call": round(td * 1e6, 2),
+                                           "TFLOPs": round(flops / td / 1e12, 1),
+                                           "GBps": round((matrix_bytes(4096, 14336) + M * 14336 * 2
+                                                          + M * 4096 * 4) / td / 1e9, 1)}},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

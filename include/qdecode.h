@@ -238,11 +238,19 @@ qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* rou
  *   1 <= M <= 128; 4-bit codes as qgemv_affine4. Runs on bf16 MFMA with the
  *   exact integer codes as the matrix operand and the scales and biases
  *   applied per group in fp32.
+ *   workspace: as for qgemm_affine4_verify (same kernel, same split plan):
+ *   shapes with few 64-column tiles, such as a down projection, split K
+ *   across workgroups and need at least
+ *   qgemm_affine4_chunk_workspace_bytes(M, N, K) bytes (16-byte aligned) for
+ *   their fp32 partial results, which a second launch adds in split order;
+ *   0 bytes (workspace may be NULL) for shapes that run unsplit. NULL or too
+ *   small otherwise fails with QD_ERR_WORKSPACE before any launch.
  */
+size_t qgemm_affine4_chunk_workspace_bytes(int32_t M, int32_t N, int32_t K);
 qd_status qgemm_affine4_chunk(const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                               const uint16_t* x, float* y,
                               int32_t M, int32_t N, int32_t K, int32_t group_size,
-                              qd_stream stream);
+                              void* workspace, size_t ws_bytes, qd_stream stream);
 
 /*
  * Verification GEMM ([Mirai] speculative-decoding section: the target model

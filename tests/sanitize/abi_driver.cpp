@@ -89,8 +89,12 @@ int main() {
     bad = moe(257);
     EXPECT(qmoe_layer_decode_noalloc(&bad, U32 A, U16 A, U16 A, 8, A, QD_F16, y, (int32_t*)A, y, y, nullptr), QD_ERR_UNSUPPORTED);
     // chunk and verification GEMMs
-    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 128, 14336, 4096, 64, nullptr), QD_OK);
-    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 129, 14336, 4096, 64, nullptr), QD_ERR_INVALID_ARGUMENT);
+    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 128, 14336, 4096, 64, nullptr, 0, nullptr), QD_OK);
+    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 129, 14336, 4096, 64, nullptr, 0, nullptr), QD_ERR_INVALID_ARGUMENT);
+    const size_t cws = qgemm_affine4_chunk_workspace_bytes(128, 4096, 14336);
+    if (!(cws > 0) || qgemm_affine4_chunk_workspace_bytes(128, 14336, 4096) != 0) ++fails;
+    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 128, 4096, 14336, 64, A, cws, nullptr), QD_OK);
+    EXPECT(qgemm_affine4_chunk(U32 A, U16 A, U16 A, U16 A, y, 128, 4096, 14336, 64, nullptr, cws, nullptr), QD_ERR_WORKSPACE);
     EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, QD_F16, y, 32, 14336, 4096, 64, nullptr, 0, nullptr), QD_OK);
     EXPECT(qgemm_affine4_verify(U32 A, U16 A, U16 A, U16 A, (qd_dtype)2, y, 32, 14336, 4096, 64, nullptr, 0, nullptr), QD_ERR_UNSUPPORTED);
     const size_t kws = qgemm_affine4_verify_workspace_bytes(32, 4096, 14336);

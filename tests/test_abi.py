@@ -174,7 +174,8 @@ def test_moe_workspace_size_grows_with_tokens():
 def test_chunk_argument_errors():
     L = qd.lib()
     f = lambda **kw: L.qgemm_affine4_chunk(kw.get("wq", A), A, A, kw.get("x", A), A, kw.get("M", 128),
-                                           kw.get("N", 256), kw.get("K", 256), kw.get("g", 64), None)
+                                           kw.get("N", 256), kw.get("K", 256), kw.get("g", 64),
+                                           kw.get("w", None), kw.get("wsb", 0), None)
     assert f(M=0) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(M=129) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(K=96) == qd.QD_ERR_INVALID_ARGUMENT
@@ -182,6 +183,13 @@ def test_chunk_argument_errors():
     assert f(g=128) == qd.QD_ERR_UNSUPPORTED
     assert f(wq=None) == qd.QD_ERR_INVALID_ARGUMENT
     assert f(x=MIS) == qd.QD_ERR_MISALIGNED
+    # the prefill down projection (64 column tiles) splits K, with the verification GEMM's plan
+    ws = qd.chunk_workspace_bytes(128, 4096, 14336)
+    assert ws > 0 and ws == qd.verify_workspace_bytes(128, 4096, 14336)
+    assert qd.chunk_workspace_bytes(128, 14336, 4096) == 0 and qd.chunk_workspace_bytes(129, 4096, 14336) == 0
+    assert f(N=4096, K=14336) == qd.QD_ERR_WORKSPACE
+    assert f(N=4096, K=14336, w=A, wsb=ws - 1) == qd.QD_ERR_WORKSPACE
+    assert f(N=4096, K=14336, w=MIS, wsb=ws) == qd.QD_ERR_MISALIGNED
 
 
 def test_mirai_rht_argument_errors():

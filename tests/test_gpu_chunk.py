@@ -79,3 +79,24 @@ def test_full_size_dense_chunk():
     rows = np.unique(np.concatenate([np.random.default_rng(1).choice(N, 256, replace=False), [0, N - 1]]))
     yr, a = oracle.gemm_chunk(w, xb, rows=rows)
     assert_within(y[:, rows], yr, a, "c4 dense")
+
+
+def test_full_size_7b_down_projection_split_k():
+    # the prefill down projection K=14336 -> N=4096 over a 128-token chunk: 64 column
+    # tiles, so K is split across workgroups; sampled rows against the oracle, two
+    # calls bitwise equal, Y written only inside its bounds
+    K, N, M = 14336, 4096, 128
+    assert qd.chunk_workspace_bytes(M, N, K) > 0
+    w = synth.affine_weights(4, N, K, cfg=503, set_id=1)
+    xb = synth.x_bf16(M, K, cfg=503, set_id=1)
+    print("chunk down projection 128 x 14336 -> 4096", flush=True)
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), float("nan"), device="cuda")
+    out = buf[guard:guard + M * N].view(M, N)
+    y1 = run_chunk(w, xb, out=out).clone()
+    y2 = run_chunk(w, xb)
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * N:]).all()
+    assert torch.equal(y1, y2)
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(N, 96, replace=False), [0, N - 1]]))
+    yr, a = oracle.gemm_chunk(w, xb, rows)
+    assert_within(y1.cpu().numpy()[:, rows], yr, a, "chunk down projection")
