@@ -178,9 +178,10 @@ struct ChunkSb {
     static constexpr int KMAX = (16 * CH_SB_GMAX + NTH - 1) / NTH;   // uint4 per thread
     uint4 v[KMAX];
     // all loads issued (indices clamp to the two runs, [8 G] uint4 each).
-    // STRIDED: the tile's rows are rs halfwords apart (a K split copies its
-    // G groups of rows of rs groups; 8 | rs and the split starts at a
-    // multiple of 8 groups, so every row run stays 16-byte aligned)
+    // STRIDED (a K split): the tile's rows are rs values apart (the matrix's
+    // groups per row) and the copy takes G of them from each row; with
+    // 8 | rs and the split starting on a multiple of 8 groups, every row's
+    // run stays 16-byte aligned.
     template <bool STRIDED = false>
     __device__ __forceinline__ void load(const uint16_t* s, const uint16_t* b, int G, int rs = 0) {
         const int n8 = 8 * G, upr = G / 8;
@@ -620,21 +621,20 @@ hipError_t launch_chunk_gemm(int bits, const uint32_t* wq, const uint16_t* s, co
 // row block per wave and two K-sets (4 waves); up to 64 rows, two row blocks
 // and four K-sets; beyond, the whole chunk as four row blocks per wave, 2
 // column waves x 4 K-sets = 8 waves (2 per SIMD). All use 4 groups per stage
-// and a ring of 8 groups.
-    if (ws != nullptr) {
-        const ChunkSplit c = chunk_split(M, N, K);
-        if (c.splits > 1) {
-            if (ws_bytes < chunk_split_workspace_bytes(M, N, K)) return hipErrorInvalidValue;
-            float* part = (float*)ws;
-            if (xkind == X_F16) {
-                if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, true>(a, c, part, st);
-                if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, true>(a, c, part, st);
-                return launch_chunk_split<4, 8, 4, 1, 4, true>(a, c, part, st);
-            }
-            if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, false>(a, c, part, st);
-            if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, false>(a, c, part, st);
-            return launch_chunk_split<4, 8, 4, 1, 4, false>(a, c, part, st);
+// and a ring of 8 groups. With a workspace, shapes with few tiles split K
+// (chunk_split) on the same configurations.
+    const ChunkSplit c = chunk_split(M, N, K);
+    if (ws != nullptr && c.splits > 1) {
+        if (ws_bytes < chunk_split_workspace_bytes(M, N, K)) return hipErrorInvalidValue;
+        float* part = (float*)ws;
+        if (xkind == X_F16) {
+            if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, true>(a, c, part, st);
+            if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, true>(a, c, part, st);
+            return launch_chunk_split<4, 8, 4, 1, 4, true>(a, c, part, st);
         }
+        if (M <= 32) return launch_chunk_split<4, 8, 1, 1, 2, false>(a, c, part, st);
+        if (M <= 64) return launch_chunk_split<4, 8, 2, 1, 4, false>(a, c, part, st);
+        return launch_chunk_split<4, 8, 4, 1, 4, false>(a, c, part, st);
     }
     if (xkind == X_F16) {
         if (M <= 32) return launch_chunk_sb<4, 8, 1, 1, 2, true>(a, st);
