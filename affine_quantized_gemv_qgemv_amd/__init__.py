@@ -35,7 +35,8 @@ EXPORTS = ("qgemv_affine4", "qgemv_affine8", "qgemv_mirai_m", "qgemv_mirai_l", "
            "qgemm_affine4_verify_workspace_bytes", "qgemm_affine4_verify",
            "qgemm_affine4_verify_i8_workspace_bytes", "qgemm_affine4_verify_i8",
            "qattn_decode_workspace_bytes", "qattn_decode",
-           "qmoe_layer_decode", "qmoe_layer_decode_noalloc", "qd_stream_read",
+           "qmoe_layer_decode", "qmoe_layer_decode_noalloc", "qmoe_layer_prefill_workspace_bytes",
+           "qmoe_layer_prefill", "qd_stream_read",
            "qd_status_string", "qd_last_error")
 
 
@@ -96,6 +97,10 @@ def lib() -> ctypes.CDLL:
                                           _P]
     L.qmoe_layer_decode.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P, ctypes.c_int, _P,
                                     _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.qmoe_layer_prefill_workspace_bytes.argtypes = [ctypes.POINTER(MoeWeightsC), _I32, _I32]
+    L.qmoe_layer_prefill_workspace_bytes.restype = ctypes.c_size_t
+    L.qmoe_layer_prefill.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _I32, _P, ctypes.c_int,
+                                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.qmoe_layer_decode_noalloc.argtypes = [ctypes.POINTER(MoeWeightsC), _P, _P, _P, _I32, _P,
                                             ctypes.c_int, _P, _P, _P, _P, _P]
     L.qattn_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
@@ -321,8 +326,10 @@ class MoeWeights:
 
 
 def qmoe_workspace_bytes(w: MoeWeights, T: int, k: int) -> int:
+    """Workspace bytes of qmoe_layer (and of qmoe_expert_gemv) for T tokens."""
     st = w.cstruct()
-    return int(lib().qmoe_expert_workspace_bytes(ctypes.byref(st), T, k))
+    e = int(lib().qmoe_expert_workspace_bytes(ctypes.byref(st), T, k))
+    return max(e, int(lib().qmoe_layer_prefill_workspace_bytes(ctypes.byref(st), T, k)))
 
 
 def qmoe_expert_gemv(w: MoeWeights, idx, weights, x, out=None, workspace=None):
@@ -351,7 +358,8 @@ def qmoe_layer(w: MoeWeights, x, k: int = 8, workspace=None, logits=None, idx=No
     """One MoE FFN layer: int8 router GEMV -> top-k routing -> expert block.
 
     One token (decode) takes qmoe_layer_decode (the ranking inside the gate+up
-    kernel, identical results); several take the three separate calls."""
+    kernel, identical results); several take qmoe_layer_prefill (the router split
+    over the hidden size, its partial logits added by the routing)."""
     T = x.shape[0]
     if logits is None:
         logits = torch.empty((T, w.E), dtype=torch.float32, device=x.device)
@@ -372,9 +380,22 @@ def qmoe_layer(w: MoeWeights, x, k: int = 8, workspace=None, logits=None, idx=No
                                        _ptr(idx), _ptr(weights), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream()))
         return out
-    qgemv_affine8(w.router_q, w.router_s, w.router_b, x, out=logits)
-    idx, weights = qmoe_route_topk(logits, k, idx, weights)
-    return qmoe_expert_gemv(w, idx, weights, x, out=out, workspace=workspace)
+    _need(x, "x", (torch.float16, torch.bfloat16), 2)
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((T, w.H), dtype=torch.float32, device=x.device)
+    st = w.cstruct()
+    need = int(lib().qmoe_layer_prefill_workspace_bytes(ctypes.byref(st), T, k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().qmoe_layer_prefill(ctypes.byref(st), _ptr(w.router_q), _ptr(w.router_s),
+                                    _ptr(w.router_b), k, T, _ptr(x), _x_dtype(x), _ptr(logits),
+                                    _ptr(idx), _ptr(weights), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream()))
+    return out
 
 
 def qmoe_layer_decode_noalloc(w: MoeWeights, x, k: int = 8, logits=None, idx=None, weights=None,

@@ -403,6 +403,63 @@ qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* rou
                     fn);
 }
 
+// Prefill layer workspace: the expert block's, then the router's split slices.
+static size_t prefill_expert_part(const qd::MoeArgs& m, int T, int k) {
+    return (qd::moe_workspace_bytes(m, T, k) + 255) & ~(size_t)255;
+}
+
+size_t qmoe_layer_prefill_workspace_bytes(const qd_moe_weights* w, int32_t T, int32_t k) {
+    if (!w || T < 1 || T > 128 || k < 1 || w->I < 1 || w->I_shared < 1 || w->E < 1 || w->H < 64 ||
+        w->H % 64)
+        return 0;
+    const qd::G8Split c = qd::gemm8_split(w->E, w->H, T);
+    return prefill_expert_part(moe_args(w), T, k) + (size_t)c.splits * T * w->E * sizeof(float);
+}
+
+qd_status qmoe_layer_prefill(const qd_moe_weights* w, const uint32_t* router_q,
+                             const uint16_t* router_s, const uint16_t* router_b, int32_t k, int32_t T,
+                             const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                             float* weights, float* y, void* workspace, size_t ws_bytes,
+                             qd_stream stream) {
+    const char* fn = "qmoe_layer_prefill";
+    qd_status st = check_moe(fn, w);
+    if (st != QD_OK) return st;
+    if (T < 1 || T > 128)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: T = %d must be in [1, 128]", fn, T);
+    if (w->E > 1024) return fail(QD_ERR_UNSUPPORTED, "%s: E = %d (at most 1024)", fn, w->E);
+    if (k < 1 || k > w->E || k > 32)
+        return fail(QD_ERR_INVALID_ARGUMENT, "%s: k = %d must be in [1, min(E, 32)]", fn, k);
+    if (x_dtype != QD_F16 && x_dtype != QD_BF16)
+        return fail(QD_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, (int)x_dtype);
+    st = check_matrix(fn, w->E, w->H, 64);
+    if (st != QD_OK) return st;
+    CHECK_PTR(router_q);
+    CHECK_PTR(router_s);
+    CHECK_PTR(router_b);
+    CHECK_PTR(x);
+    CHECK_PTR(logits);
+    CHECK_PTR(idx);
+    CHECK_PTR(weights);
+    CHECK_PTR(y);
+    const size_t need = qmoe_layer_prefill_workspace_bytes(w, T, k);
+    if (!workspace) return fail(QD_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (!aligned16(workspace)) return fail(QD_ERR_MISALIGNED, "%s: workspace is not 16-byte aligned", fn);
+    if (ws_bytes < need)
+        return fail(QD_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    const qd::MoeArgs m = moe_args(w);
+    const size_t eb = prefill_expert_part(m, T, k);
+    float* part = (float*)((char*)workspace + eb);
+    const int xkind = x_dtype == QD_F16 ? 0 : 1;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = qd::launch_gemm8_tokens_split(router_q, router_s, router_b, (const uint16_t*)x, xkind,
+                                                 part, w->E, w->H, T, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    e = qd::launch_route_topk_slices(part, qd::gemm8_split(w->E, w->H, T).splits, T, w->E, k, logits,
+                                     idx, weights, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    return from_hip(qd::launch_moe_experts(m, idx, weights, T, k, x, xkind, y, workspace, eb, s), fn);
+}
+
 // Bytes of the K-split workspace of the chunk kernel (0: the shape runs unsplit).
 size_t chunk_workspace_bytes(int32_t M, int32_t N, int32_t K) {
     if (M < 1 || M > 128 || N < 1 || K < 64 || K % 64 || K > (1 << 22)) return 0;

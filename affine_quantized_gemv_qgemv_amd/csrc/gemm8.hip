@@ -38,8 +38,9 @@ struct G8Args {
     const uint16_t* s;    // [N][K/64] f16
     const uint16_t* b;    // [N][K/64] f16
     const uint16_t* x;    // [T][K] f16 or bf16
-    float* y;             // [T][N]
+    float* y;             // [T][N]; with a K split, the [splits][T][N] partial slices
     int T, N, K;
+    int gsplit;           // K split: groups per split (blockIdx.z), 0 = whole K
 };
 
 constexpr int G8_WAVES = 8;
@@ -52,7 +53,13 @@ __device__ __forceinline__ uint32_t byte_pair(uint32_t w, uint32_t m, uint32_t s
     return __builtin_amdgcn_perm(m, w, sel);
 }
 
-template <int XF>   // 0: f16 activations, 1: bf16 activations
+// KS: K split across workgroups: blockIdx.z takes groups [z gsplit,
+// min((z + 1) gsplit, K / 64)) and writes slice z of a.y; the slices are added
+// in split order by their reader (the routing of a prefill chunk). SLOTS:
+// groups a wave loads together; every slot is requested (clamped), so a split
+// runs with just enough slots for its groups: each 16-byte activation load
+// touches 32 rows' cache lines, and these requests bound the kernel.
+template <int XF, bool KS = false, int SLOTS = G8_SLOTS>   // XF 0: f16, 1: bf16 activations
 __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
     __shared__ float red[G8_WAVES - 1][16][64];
     const int lane = threadIdx.x & 63;
@@ -73,12 +80,18 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 
-    for (int g0 = wave; g0 < G; g0 += G8_WAVES * G8_SLOTS) {
-        uint4 xa[G8_SLOTS][4], wb[G8_SLOTS][2];
-        uint16_t sv[G8_SLOTS], bv[G8_SLOTS];
+    int gb = 0, ge = G;   // this workgroup's groups
+    if constexpr (KS) {
+        gb = (int)blockIdx.z * a.gsplit;
+        ge = min(G, gb + a.gsplit);
+        a.y += (int64_t)blockIdx.z * a.T * a.N;
+    }
+    for (int g0 = gb + wave; g0 < ge; g0 += G8_WAVES * SLOTS) {
+        uint4 xa[SLOTS][4], wb[SLOTS][2];
+        uint16_t sv[SLOTS], bv[SLOTS];
 #pragma unroll
-        for (int j = 0; j < G8_SLOTS; ++j) {   // clamped loads, used only if g < G
-            const int g = min(g0 + G8_WAVES * j, G - 1);
+        for (int j = 0; j < SLOTS; ++j) {   // clamped loads, used only if g < ge
+            const int g = min(g0 + G8_WAVES * j, ge - 1);
             const uint4* xp = (const uint4*)(xrow + (int64_t)g * 64);
 #pragma unroll
             for (int st = 0; st < 4; ++st) xa[j][st] = xp[st];
@@ -94,8 +107,8 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
         // each slot's loads into it, one memory round trip per group)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < G8_SLOTS; ++j) {
-            const bool valid = g0 + G8_WAVES * j < G;   // uniform
+        for (int j = 0; j < SLOTS; ++j) {
+            const bool valid = g0 + G8_WAVES * j < ge;   // uniform
             const uint32_t wv[8] = {wb[j][0].x, wb[j][0].y, wb[j][0].z, wb[j][0].w,
                                     wb[j][1].x, wb[j][1].y, wb[j][1].z, wb[j][1].w};
             floatx16 P, X1;
@@ -156,11 +169,44 @@ __global__ __launch_bounds__(64 * G8_WAVES) void gemm8_tokens_kernel(G8Args a) {
     }
 }
 
+// K split of the chunk router: 128 tokens x 128 experts are 16 tiles of 32 x 32,
+// each pulling its 32 tokens' activations through one CU. Up to G8_SPLIT
+// splits of at least 8 groups each (a 2816-input router: 5 splits of 9
+// groups, 80 workgroups), each wave of a split loading G8_SPLIT_SLOTS groups
+// at once (measured per c4 MoE layer: 4 splits with 2 slots 187.4 µs, this
+// 186.2, unsplit 192.4).
+constexpr int G8_SPLIT = 8;
+constexpr int G8_SPLIT_SLOTS = 1;
+
+G8Split gemm8_split(int N, int K, int T) {
+    const int G = K / 64;
+    const int sp = min(G8_SPLIT, G / 8);
+    if (N < 1 || T < 1 || G < 1 || sp <= 1) return {1, G};
+    const int gs = (G + sp - 1) / sp;
+    return {(G + gs - 1) / gs, gs};
+}
+
+hipError_t launch_gemm8_tokens_split(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                     const uint16_t* x, int xkind, float* part, int N, int K, int T,
+                                     hipStream_t st) {
+    if (K % 64 != 0 || (xkind != X_F16 && xkind != X_BF16)) return hipErrorInvalidValue;
+    const G8Split c = gemm8_split(N, K, T);
+    G8Args a{wq, s, b, x, part, T, N, K, c.gsplit};
+    const dim3 grid((N + 31) / 32, (T + 31) / 32, c.splits);
+    if (xkind == X_F16)
+        hipLaunchKernelGGL((gemm8_tokens_kernel<0, true, G8_SPLIT_SLOTS>), grid, dim3(64 * G8_WAVES), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((gemm8_tokens_kernel<1, true, G8_SPLIT_SLOTS>), grid, dim3(64 * G8_WAVES), 0,
+                           st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,
                                hipStream_t st) {
     if (K % 64 != 0 || (xkind != X_F16 && xkind != X_BF16)) return hipErrorInvalidValue;
-    G8Args a{wq, s, b, x, y, T, N, K};
+    G8Args a{wq, s, b, x, y, T, N, K, 0};
     const dim3 grid((N + 31) / 32, (T + 31) / 32);
     if (xkind == X_F16)
         hipLaunchKernelGGL(gemm8_tokens_kernel<0>, grid, dim3(64 * G8_WAVES), 0, st, a);

@@ -40,6 +40,10 @@ hipError_t launch_gemv(int bits, int fmt, const uint32_t* wq, const uint16_t* s,
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                              hipStream_t st);
+// Routing from the router's split slices part [splits][T][E]: the logits are
+// their sum in split order (also written to `logits`).
+hipError_t launch_route_topk_slices(const float* part, int splits, int T, int E, int k,
+                                    float* logits, int32_t* idx, float* w, hipStream_t st);
 
 struct MoeArgs {
     int E, H, I, Is, act;
@@ -89,6 +93,16 @@ hipError_t launch_verify_i8(const uint32_t* wq, const uint16_t* s, const uint16_
 hipError_t launch_gemm8_tokens(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                const uint16_t* x, int xkind, float* y, int N, int K, int T,
                                hipStream_t st);
+// The same with K split across workgroups: slices part [splits][T][N], added
+// by their reader (launch_route_topk_slices). The split depends on the shape only.
+struct G8Split {
+    int splits;   // 1 = none
+    int gsplit;   // groups per split; the last one takes the rest
+};
+G8Split gemm8_split(int N, int K, int T);
+hipError_t launch_gemm8_tokens_split(const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                     const uint16_t* x, int xkind, float* part, int N, int K, int T,
+                                     hipStream_t st);
 
 // Decode attention of one token over fp16 KV caches (circular when window > 0).
 size_t attn_workspace_bytes(int Hq, int Hkv, int D, int cap);

@@ -232,6 +232,31 @@ qd_status qmoe_layer_decode_noalloc(const qd_moe_weights* w, const uint32_t* rou
                                     float* weights, float* y, qd_stream stream);
 
 /*
+ * One MoE layer over a prefill chunk of T tokens ([TF] internals: a chunk of
+ * up to 128 tokens goes through the router at once, and each token's top-8
+ * experts and the shared expert are combined): the 8-bit router over the
+ * chunk (as qgemv_affine8, router [E][H], E <= 1024), top-k routing (as
+ * qmoe_route_topk), then the expert block (as qmoe_expert_gemv). The router
+ * splits H across workgroups (128 tokens x 128 experts are only 16 tiles of
+ * 32 x 32); its partial logits go to the workspace and the routing adds them
+ * in a fixed order, so results do not depend on timing (the logits may differ
+ * from a separate qgemv_affine8 call by that summation order).
+ *   x [T][H] fp16 or bf16 bits; logits [T][E], idx [T][k], weights [T][k]
+ *   and y [T][H] are outputs; 1 <= T <= 128, 1 <= k <= min(E, 32).
+ *   workspace: 16-byte aligned device memory of at least
+ *   qmoe_layer_prefill_workspace_bytes(w, T, k) bytes (0 for arguments out
+ *   of range), overwritten by every call; NULL or too small fails with
+ *   QD_ERR_WORKSPACE before any launch.
+ * Launches on `stream`: the router, the routing, then the expert block's.
+ */
+size_t qmoe_layer_prefill_workspace_bytes(const qd_moe_weights* w, int32_t T, int32_t k);
+qd_status qmoe_layer_prefill(const qd_moe_weights* w, const uint32_t* router_q,
+                             const uint16_t* router_s, const uint16_t* router_b, int32_t k, int32_t T,
+                             const void* x, qd_dtype x_dtype, float* logits, int32_t* idx,
+                             float* weights, float* y, void* workspace, size_t ws_bytes,
+                             qd_stream stream);
+
+/*
  * Prefill chunk ([TF] internals: prompts run in chunks of at most 128 tokens
  * so one fetch of a weight serves many rows):
  *   Y[m][n] = sum_k w[n][k] * X[m][k],  X [M][K] bf16 bits, Y [M][N] fp32.

@@ -84,6 +84,12 @@ int main() {
     EXPECT(qmoe_layer_decode(&w, U32 A, U16 A, U16 A, 8, A, QD_F16, y, (int32_t*)A, y, y, A, ws1, nullptr), QD_OK);
     EXPECT(qmoe_layer_decode(&w, U32 A, U16 A, U16 A, 8, A, QD_F16, y, (int32_t*)A, y, y, nullptr, ws1, nullptr), QD_ERR_WORKSPACE);
     EXPECT(qmoe_layer_decode_noalloc(&w, U32 A, U16 A, U16 A, 8, A, QD_F16, y, (int32_t*)A, y, y, nullptr), QD_OK);
+    const size_t pws = qmoe_layer_prefill_workspace_bytes(&w, 128, 8);
+    if (!(pws > qmoe_expert_workspace_bytes(&w, 128, 8)) || qmoe_layer_prefill_workspace_bytes(&w, 129, 8) != 0) ++fails;
+    EXPECT(qmoe_layer_prefill(&w, U32 A, U16 A, U16 A, 8, 128, A, QD_BF16, y, (int32_t*)A, y, y, A, pws, nullptr), QD_OK);
+    EXPECT(qmoe_layer_prefill(&w, U32 A, U16 A, U16 A, 8, 128, A, QD_BF16, y, (int32_t*)A, y, y, A, pws - 1, nullptr), QD_ERR_WORKSPACE);
+    EXPECT(qmoe_layer_prefill(&w, U32 A, U16 A, U16 A, 8, 129, A, QD_BF16, y, (int32_t*)A, y, y, A, pws, nullptr), QD_ERR_INVALID_ARGUMENT);
+    EXPECT(qmoe_layer_prefill(&w, nullptr, U16 A, U16 A, 8, 128, A, QD_BF16, y, (int32_t*)A, y, y, A, pws, nullptr), QD_ERR_INVALID_ARGUMENT);
     bad = moe(64, 2816, 32768, 1024);
     EXPECT(qmoe_layer_decode_noalloc(&bad, U32 A, U16 A, U16 A, 32, A, QD_F16, y, (int32_t*)A, y, y, nullptr), QD_ERR_WORKSPACE);
     bad = moe(257);

@@ -34,6 +34,17 @@ hipError_t launch_gemv(int, int, const uint32_t*, const uint16_t*, const uint16_
     ++g_launches;
     return hipSuccess;
 }
+G8Split gemm8_split(int, int K, int) { return {K >= 4096 ? 4 : 1, K / 64}; }
+hipError_t launch_gemm8_tokens_split(const uint32_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                                     int, float*, int, int, int, hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_route_topk_slices(const float*, int, int, int, int, float*, int32_t*, float*,
+                                    hipStream_t) {
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_route_topk(const float*, int, int, int, int32_t*, float*, hipStream_t) {
     ++g_launches;
     return hipSuccess;
