@@ -209,3 +209,39 @@ def test_full_prefill_chunk(full_layer):
     for xdt in ("bf16", "f16"):
         xb = (synth.x_bf16 if xdt == "bf16" else synth.x_f16)(128, full_layer.H, cfg=4, set_id=7)
         check_layer(full_layer, xb, 8, xdt=xdt, tokens=[0, 1, 31, 64, 127], what=f"c4 moe {xdt}")
+
+
+# ------------------------------------------------- prefill layer (one call)
+
+@pytest.mark.parametrize("E,H,T,k", [(300, 1088, 37, 5), (128, 2816, 9, 8), (40, 512, 2, 32),
+                                     (600, 704, 1, 8)])
+def test_prefill_layer_split_router(E, H, T, k):
+    """qmoe_layer_prefill: the router split over H (1088 = 17 groups: two splits
+    of 9 and 8; 2816: five of 9; 512: one), its slices added by the routing; ids
+    and weights equal qmoe_route_topk on the logits it wrote, y equals
+    qmoe_expert_gemv, logits and y within the bar of the oracle. E > 256 takes
+    the prefill call for a single token too."""
+    mw = synth.moe_weights(E=E, H=H, I=64, Is=128, cfg=410, layer=E)
+    xb = synth.x_bf16(T, H, cfg=410, set_id=T)
+    print(f"prefill layer E={E} H={H} T={T} k={k}", flush=True)
+    check_layer(mw, xb, k, xdt="bf16", what=f"prefill E={E} H={H} T={T}")
+
+
+def test_prefill_layer_deterministic_and_in_bounds():
+    mw = synth.moe_weights(E=128, H=2816, I=64, Is=128, cfg=411, layer=0)
+    w = dev_moe(mw)
+    T, k = 50, 8
+    xb = synth.x_f16(T, 2816, cfg=411, set_id=0)
+    x = dev_half(xb)
+    need = qd.qmoe_workspace_bytes(w, T, k)
+    guard = 4096
+    wbuf = torch.full((guard + need + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ybuf = torch.full((guard + T * 2816 + guard,), float("nan"), device="cuda")
+    ws = wbuf[guard:guard + need]
+    out = ybuf[guard:guard + T * 2816].view(T, 2816)
+    y1 = qd.qmoe_layer(w, x, k=k, workspace=ws, out=out).clone()
+    y2 = qd.qmoe_layer(w, x, k=k, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert (wbuf[:guard] == 0x5A).all() and (wbuf[guard + need:] == 0x5A).all()
+    assert torch.isnan(ybuf[:guard]).all() and torch.isnan(ybuf[guard + T * 2816:]).all()
+    assert torch.equal(y1, y2)
