@@ -122,6 +122,35 @@ def moe_call(st, T=1, k=8, ws=A, ws_bytes=1 << 30, x=A, dt=0):
     return qd.lib().qmoe_expert_gemv(ctypes.byref(st), A, A, T, k, x, dt, A, ws, ws_bytes, None)
 
 
+def test_prefill_layer_argument_errors():
+    L = qd.lib()
+    st = moe_struct()
+    need = L.qmoe_layer_prefill_workspace_bytes(ctypes.byref(st), 128, 8)
+    # the expert block's workspace plus the router's split slices (at least one T x E slice)
+    assert need >= L.qmoe_expert_workspace_bytes(ctypes.byref(st), 128, 8) + 128 * 128 * 4
+    assert L.qmoe_layer_prefill_workspace_bytes(ctypes.byref(st), 0, 8) == 0
+    assert L.qmoe_layer_prefill_workspace_bytes(ctypes.byref(st), 129, 8) == 0
+    assert L.qmoe_layer_prefill_workspace_bytes(None, 16, 8) == 0
+
+    def f(w=st, rq=A, k=8, T=128, x=A, dt=1, lg=A, ws=A, wsb=need):
+        return L.qmoe_layer_prefill(ctypes.byref(w) if w is not None else None, rq, A, A, k, T, x, dt, lg,
+                                    A, A, A, ws, wsb, None)
+
+    assert f(w=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(T=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(T=129) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(k=0) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(k=33) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(w=moe_struct(E=1025)) == qd.QD_ERR_UNSUPPORTED
+    assert f(dt=2) == qd.QD_ERR_UNSUPPORTED
+    assert f(rq=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(lg=None) == qd.QD_ERR_INVALID_ARGUMENT
+    assert f(x=MIS) == qd.QD_ERR_MISALIGNED
+    assert f(ws=None) == qd.QD_ERR_WORKSPACE
+    assert f(wsb=need - 1) == qd.QD_ERR_WORKSPACE
+    assert f(ws=MIS) == qd.QD_ERR_MISALIGNED
+
+
 def test_moe_argument_errors():
     L = qd.lib()
     assert L.qmoe_expert_gemv(None, A, A, 1, 8, A, 0, A, A, 1 << 30, None) == qd.QD_ERR_INVALID_ARGUMENT
